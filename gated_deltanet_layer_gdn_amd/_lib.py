@@ -1,0 +1,98 @@
+"""ctypes declarations for libgdn.so (the C ABI in include/gdn.h).
+
+The library must have been built (``python -m gated_deltanet_layer_gdn_amd.build``
+or ``__graft_entry__.build()``); loading fails loudly otherwise.  There is no
+fallback implementation of any step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SO_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_OK = 0
+STATUS = {
+    0: "GDN_OK", -1: "GDN_ERR_INVALID_ARG", -2: "GDN_ERR_UNSUPPORTED", -3: "GDN_ERR_ALIGNMENT",
+    -4: "GDN_ERR_ALIAS", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_BLOB_MAGIC",
+    -7: "GDN_ERR_BLOB_VERSION", -8: "GDN_ERR_BLOB_SHAPE", -9: "GDN_ERR_BLOB_SIZE",
+    -10: "GDN_ERR_BLOB_CHECKSUM", -11: "GDN_ERR_HIP",
+}
+F32, BF16 = 0, 1
+ABI_VERSION = 1
+
+EXPORTS = (
+    "gdn_abi_version", "gdn_status_str", "gdn_last_hip_error", "gdn_rec_state_bytes",
+    "gdn_conv_state_bytes", "gdn_state_blob_bytes", "gdn_prefill_workspace_bytes",
+    "gdn_decode_workspace_bytes", "gdn_conv1d", "gdn_prefill_chunked", "gdn_decode_step",
+    "gdn_state_save", "gdn_state_restore", "gdn_state_check",
+)
+
+
+class GdnDims(ctypes.Structure):
+    _fields_ = [
+        ("abi", ctypes.c_int32), ("B", ctypes.c_int32), ("H_k", ctypes.c_int32),
+        ("H_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("W", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("l2_eps", ctypes.c_float), ("q_scale", ctypes.c_float),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        name = STATUS.get(status, str(status))
+        super().__init__(f"{where}: {name}" + (f" ({detail})" if detail else ""))
+
+
+_LIB = None
+
+
+def load():
+    """Load libgdn.so once and declare its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(SO_PATH):
+        raise RuntimeError(
+            f"{SO_PATH} is missing: build it with `python -m gated_deltanet_layer_gdn_amd.build`")
+    L = ctypes.CDLL(SO_PATH)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    dp = ctypes.POINTER(GdnDims)
+    L.gdn_abi_version.restype = ctypes.c_int
+    L.gdn_abi_version.argtypes = []
+    L.gdn_status_str.restype = ctypes.c_char_p
+    L.gdn_status_str.argtypes = [ctypes.c_int]
+    L.gdn_last_hip_error.restype = ctypes.c_char_p
+    L.gdn_last_hip_error.argtypes = []
+    for f in ("gdn_rec_state_bytes", "gdn_conv_state_bytes", "gdn_state_blob_bytes",
+              "gdn_decode_workspace_bytes"):
+        getattr(L, f).restype = sz
+        getattr(L, f).argtypes = [dp]
+    L.gdn_prefill_workspace_bytes.restype = sz
+    L.gdn_prefill_workspace_bytes.argtypes = [dp, i64, i32]
+    L.gdn_conv1d.restype = ctypes.c_int
+    L.gdn_conv1d.argtypes = [dp, i64, vp, vp, vp, vp, vp]
+    L.gdn_prefill_chunked.restype = ctypes.c_int
+    L.gdn_prefill_chunked.argtypes = [dp, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gdn_decode_step.restype = ctypes.c_int
+    L.gdn_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gdn_state_save.restype = ctypes.c_int
+    L.gdn_state_save.argtypes = [dp, vp, vp, vp, sz, vp]
+    L.gdn_state_restore.restype = ctypes.c_int
+    L.gdn_state_restore.argtypes = [dp, vp, sz, vp, vp, vp]
+    L.gdn_state_check.restype = ctypes.c_int
+    L.gdn_state_check.argtypes = [dp, vp, sz]
+    if L.gdn_abi_version() != ABI_VERSION:
+        raise RuntimeError("libgdn.so ABI version mismatch")
+    _LIB = L
+    return L
+
+
+def check(status: int, where: str) -> None:
+    if status != GDN_OK:
+        detail = ""
+        if status == -11:
+            detail = load().gdn_last_hip_error().decode()
+        raise GdnError(status, where, detail)

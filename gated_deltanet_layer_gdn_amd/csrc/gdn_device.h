@@ -1,0 +1,142 @@
+// gdn_device.h -- device-side helpers shared by the GDN kernels (gfx950).
+//
+// MFMA operand layout of v_mfma_f32_16x16x32_bf16 on a 64-lane wave, with
+// lane l, group g = l / 16 and column c = l % 16:
+//   A (16 x 32, M x K): the lane supplies A[c][8g + i], i = 0..7
+//   B (32 x 16, K x N): the lane supplies B[8g + i][c]
+//   D (16 x 16):        the lane holds    D[4g + r][c], r = 0..3
+// A 32-wide K step that spans two consecutive 16-row D tiles can therefore be
+// fed straight from D registers if the K index is permuted: K slot 8g + i
+// stands for index 4g + i (i < 4, first tile) or 16 + 4g + (i - 4) (second
+// tile).  Every operand that is loaded from memory is stored in that permuted
+// order, so no data ever moves between lanes to turn a result into the next
+// product's operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- numbers
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Split x into hi + lo, both bf16: hi = bf16(x), lo = bf16(x - hi).  hi + lo
+// carries 16 significant bits of x.
+__device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
+  hi = f32_to_bf16_bits(x);
+  lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+template <int DT>  // 0 = fp32, 1 = bf16
+__device__ __forceinline__ float load_elem(const void *p, size_t i) {
+  if constexpr (DT == 0)
+    return static_cast<const float *>(p)[i];
+  else
+    return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(void *p, size_t i, float v) {
+  if constexpr (DT == 0)
+    static_cast<float *>(p)[i] = v;
+  else
+    static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(v);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + __expf(-x)); }
+
+// Causal width-4 conv of one channel: taps w0..w3 meet x[t-3]..x[t].  The
+// accumulation order is fixed so that every kernel gets the same bits.
+__device__ __forceinline__ float conv4(float w0, float w1, float w2, float w3, float x0,
+                                       float x1, float x2, float x3) {
+  float acc = w0 * x0;
+  acc = __builtin_fmaf(w1, x1, acc);
+  acc = __builtin_fmaf(w2, x2, acc);
+  acc = __builtin_fmaf(w3, x3, acc);
+  return acc;
+}
+
+// ---------------------------------------------------------------- wave ops
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele; fixed order).
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    float o = __shfl_up(v, d, kWave);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u16x8 &a, const u16x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Split-precision product: (a_hi + a_lo)(b_hi + b_lo) without the lo*lo term.
+__device__ __forceinline__ f32x4 mfma_split3(const u16x8 &ah, const u16x8 &al,
+                                             const u16x8 &bh, const u16x8 &bl, f32x4 c) {
+  c = mfma16x16x32(al, bh, c);
+  c = mfma16x16x32(ah, bl, c);
+  c = mfma16x16x32(ah, bh, c);
+  return c;
+}
+
+// a plain bf16, b split.
+__device__ __forceinline__ f32x4 mfma_split2(const u16x8 &a, const u16x8 &bh,
+                                             const u16x8 &bl, f32x4 c) {
+  c = mfma16x16x32(a, bl, c);
+  c = mfma16x16x32(a, bh, c);
+  return c;
+}
+
+// Pack the D registers of two stacked 16-row tiles (t0: K indices 0..15, t1:
+// 16..31) into a split B (or A) operand with the permuted K order.
+__device__ __forceinline__ void pack_split(const f32x4 &t0, const f32x4 &t1, u16x8 &hi,
+                                           u16x8 &lo) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint16_t h, l;
+    split_bf16(t0[r], h, l);
+    hi[r] = h;
+    lo[r] = l;
+    split_bf16(t1[r], h, l);
+    hi[4 + r] = h;
+    lo[4 + r] = l;
+  }
+}
+
+// Position of index j (0..31) of a K step in the permuted slot order.
+__host__ __device__ __forceinline__ int kslot(int j) {
+  const int tile = j >> 4, within = j & 15;
+  return 8 * (within >> 2) + 4 * tile + (within & 3);
+}
+
+}  // namespace gdn

@@ -1,0 +1,55 @@
+// gdn_internal.h -- host-side plumbing between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+// Everything a kernel needs to know about the geometry, as plain values.
+struct Geom {
+  int B, H_k, H_v, D, W, G;  // D = d_k = d_v, G = H_v / H_k
+  int C_ch;                  // 2*H_k*D + H_v*D
+  int in_dt, out_dt;         // 0 = fp32, 1 = bf16
+  float eps, q_scale;
+};
+
+// Prefill workspace carve-up (byte offsets from the workspace base, each
+// 256-byte aligned).  Dp = max(D, 32); Cp = max(C, 32); T_pad = T rounded up
+// to a multiple of Cp; NC = T_pad / C chunks.
+//   q/k token-major   [B][H_k][T_pad][Dp]     bf16 hi and lo, head-dim in
+//                                               permuted K order per 32
+//   k dim-major       [B][H_k][T_pad/32][D][32] bf16 hi and lo, tokens in
+//                                               permuted K order
+//   v dim-major       [B][H_v][T_pad/16][D][16] fp32
+//   T = (I + A)^{-1}  [B][H_v][NC][C][Cp]      bf16, columns permuted
+//   P = tril(D) * QK^T [B][H_v][NC][C][Cp]     bf16 hi and lo, columns permuted
+struct PrefillWs {
+  int64_t T, T_pad;
+  int C, Cp, Dp, NC;
+  size_t q_hi, q_lo, k_hi, k_lo, kT_hi, kT_lo, vT, Tm, P_hi, P_lo;
+  size_t total;
+};
+
+bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *ws);
+size_t decode_ws_bytes(const Geom &g);
+
+// Kernel launchers (enqueue only; return the launch status).
+hipError_t launch_conv_plain(const Geom &g, int64_t T, const void *x, const void *w,
+                             void *hist, float *out, hipStream_t s);
+hipError_t launch_conv_prefill(const Geom &g, const PrefillWs &L, const void *x,
+                               const void *w, const void *hist, char *ws, hipStream_t s);
+hipError_t launch_conv_roll(const Geom &g, int64_t T, const void *x, void *hist,
+                            hipStream_t s);
+hipError_t launch_decode(const Geom &g, const float *qkv, const void *z, const float *gl,
+                         const float *beta, float *S, void *y, hipStream_t s);
+hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
+                               const float *beta, char *ws, hipStream_t s);
+hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z,
+                                const float *gl, const float *beta, float *S, void *y,
+                                const char *ws, hipStream_t s);
+
+}  // namespace gdn
