@@ -124,9 +124,10 @@ def conv1d(d: Dims, x, conv_w, conv_state, out=None):
 
 
 def prefill_chunked(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, chunk: int = 64,
-                    y=None, ws=None):
+                    y=None, ws=None, kernel_ms=None):
     """Whole layer over T tokens; updates conv_state and rec_state in place and
-    returns y [B,T,H_v,d_v]."""
+    returns y [B,T,H_v,d_v].  With ``kernel_ms`` (a list), calls the timed
+    entry point and appends the 4 per-kernel durations in ms."""
     torch = _torch()
     L = _lib.load()
     T = x.shape[1]
@@ -147,16 +148,22 @@ def prefill_chunked(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, chunk
     if need == 0:
         raise GdnError(-2, "gdn_prefill_chunked", f"no workspace size for T={T} chunk={chunk}")
     ws = _workspace(need, x, ws)
-    rc = L.gdn_prefill_chunked(ctypes.byref(d.c()), T, chunk, *args,
-                               ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
-                               _stream())
+    tail = [ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream()]
+    if kernel_ms is None:
+        rc = L.gdn_prefill_chunked(ctypes.byref(d.c()), T, chunk, *args, *tail)
+    else:
+        ms = (ctypes.c_float * 4)()
+        rc = L.gdn_prefill_chunked_timed(ctypes.byref(d.c()), T, chunk, *args, *tail, ms)
+        kernel_ms.extend(float(v) for v in ms)
     _lib.check(rc, "gdn_prefill_chunked")
     return y
 
 
-def decode_step(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, y=None, ws=None):
+def decode_step(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, y=None, ws=None,
+                kernel_ms=None):
     """One token per sequence: x [B,1,C_ch] (or [B,C_ch]), z [B,1,H_v,d_v] (or
-    [B,H_v,d_v]), g/beta [B,1,H_v] (or [B,H_v]); returns y shaped like z."""
+    [B,H_v,d_v]), g/beta [B,1,H_v] (or [B,H_v]); returns y shaped like z.
+    With ``kernel_ms`` (a list), appends the 2 per-kernel durations in ms."""
     torch = _torch()
     L = _lib.load()
     dt = _dt(d.in_dtype)
@@ -175,8 +182,13 @@ def decode_step(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, y=None, w
     args.append(_need(y.reshape(d.B, d.H_v, d.d_v), "y", (d.B, d.H_v, d.d_v), _dt(d.out_dtype)))
     need = L.gdn_decode_workspace_bytes(ctypes.byref(d.c()))
     ws = _workspace(need, x, ws)
-    rc = L.gdn_decode_step(ctypes.byref(d.c()), *args, ctypes.c_void_p(ws.data_ptr()),
-                           ws.numel() * ws.element_size(), _stream())
+    tail = [ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream()]
+    if kernel_ms is None:
+        rc = L.gdn_decode_step(ctypes.byref(d.c()), *args, *tail)
+    else:
+        ms = (ctypes.c_float * 2)()
+        rc = L.gdn_decode_step_timed(ctypes.byref(d.c()), *args, *tail, ms)
+        kernel_ms.extend(float(v) for v in ms)
     _lib.check(rc, "gdn_decode_step")
     return y
 

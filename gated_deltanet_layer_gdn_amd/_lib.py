@@ -26,7 +26,8 @@ EXPORTS = (
     "gdn_abi_version", "gdn_status_str", "gdn_last_hip_error", "gdn_rec_state_bytes",
     "gdn_conv_state_bytes", "gdn_state_blob_bytes", "gdn_prefill_workspace_bytes",
     "gdn_decode_workspace_bytes", "gdn_conv1d", "gdn_prefill_chunked", "gdn_decode_step",
-    "gdn_state_save", "gdn_state_restore", "gdn_state_check",
+    "gdn_state_save", "gdn_state_restore", "gdn_state_check", "gdn_prefill_chunked_timed",
+    "gdn_decode_step_timed",
 )
 
 
@@ -78,6 +79,10 @@ def load():
     L.gdn_prefill_chunked.argtypes = [dp, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gdn_prefill_chunked_timed.restype = ctypes.c_int
+    L.gdn_prefill_chunked_timed.argtypes = L.gdn_prefill_chunked.argtypes + [vp]
+    L.gdn_decode_step_timed.restype = ctypes.c_int
+    L.gdn_decode_step_timed.argtypes = L.gdn_decode_step.argtypes + [vp]
     L.gdn_state_save.restype = ctypes.c_int
     L.gdn_state_save.argtypes = [dp, vp, vp, vp, sz, vp]
     L.gdn_state_restore.restype = ctypes.c_int

@@ -133,6 +133,30 @@ size_t rec_state_bytes(const Geom &g) {
   return static_cast<size_t>(g.B) * g.H_v * g.D * g.D * 4;
 }
 
+// Optional HIP events around each launch of one call, for the timed entry
+// points.  Records on the caller's stream; elapsed() waits for the last one.
+struct LaunchTimer {
+  float *out;
+  int n = 0;
+  hipEvent_t ev[8] = {};
+  explicit LaunchTimer(float *o) : out(o) {}
+  ~LaunchTimer() {
+    for (int i = 0; i < n; ++i) (void)hipEventDestroy(ev[i]);
+  }
+  hipError_t mark(hipStream_t s) {
+    if (!out) return hipSuccess;
+    hipError_t e = hipEventCreate(&ev[n]);
+    if (e != hipSuccess) return e;
+    return hipEventRecord(ev[n++], s);
+  }
+  hipError_t elapsed() {
+    if (!out) return hipSuccess;
+    hipError_t e = hipEventSynchronize(ev[n - 1]);
+    for (int i = 0; e == hipSuccess && i + 1 < n; ++i) e = hipEventElapsedTime(&out[i], ev[i], ev[i + 1]);
+    return e;
+  }
+};
+
 }  // namespace
 
 bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *w) {
@@ -246,10 +270,10 @@ int gdn_conv1d(const gdn_dims *dims, int64_t T, const void *x, const void *conv_
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_conv1d");
 }
 
-int gdn_prefill_chunked(const gdn_dims *dims, int64_t T, int32_t chunk, const void *x,
+static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const void *x,
                         const void *z, const float *gl, const float *beta,
                         const void *conv_w, void *conv_state, float *rec_state, void *y,
-                        void *ws, size_t ws_bytes, void *stream) {
+                        void *ws, size_t ws_bytes, void *stream, float *kernel_ms) {
   Geom g;
   int rc = check_dims(dims, &g);
   if (rc) return rc;
@@ -272,16 +296,41 @@ int gdn_prefill_chunked(const gdn_dims *dims, int64_t T, int32_t chunk, const vo
   if (injected_launch_failure()) return GDN_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *w = static_cast<char *>(ws);
-  hipError_t e = launch_conv_prefill(g, L, x, conv_w, conv_state, w, s);
+  LaunchTimer tm(kernel_ms);
+  hipError_t e = tm.mark(s);
+  if (e == hipSuccess) e = launch_conv_prefill(g, L, x, conv_w, conv_state, w, s);
+  if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = launch_prefill_prep(g, L, gl, beta, w, s);
+  if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = launch_conv_roll(g, T, x, conv_state, s);
+  if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = launch_prefill_state(g, L, z, gl, beta, rec_state, y, w, s);
+  if (e == hipSuccess) e = tm.mark(s);
+  if (e == hipSuccess) e = tm.elapsed();
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_prefill_chunked");
 }
 
-int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, const float *gl,
+int gdn_prefill_chunked(const gdn_dims *dims, int64_t T, int32_t chunk, const void *x,
+                        const void *z, const float *gl, const float *beta,
+                        const void *conv_w, void *conv_state, float *rec_state, void *y,
+                        void *ws, size_t ws_bytes, void *stream) {
+  return prefill_impl(dims, T, chunk, x, z, gl, beta, conv_w, conv_state, rec_state, y, ws,
+                      ws_bytes, stream, nullptr);
+}
+
+int gdn_prefill_chunked_timed(const gdn_dims *dims, int64_t T, int32_t chunk, const void *x,
+                              const void *z, const float *gl, const float *beta,
+                              const void *conv_w, void *conv_state, float *rec_state, void *y,
+                              void *ws, size_t ws_bytes, void *stream, float *kernel_ms) {
+  if (!kernel_ms) return GDN_ERR_INVALID_ARG;
+  return prefill_impl(dims, T, chunk, x, z, gl, beta, conv_w, conv_state, rec_state, y, ws,
+                      ws_bytes, stream, kernel_ms);
+}
+
+static int decode_impl(const gdn_dims *dims, const void *x, const void *z, const float *gl,
                     const float *beta, const void *conv_w, void *conv_state,
-                    float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream) {
+                    float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream,
+                    float *kernel_ms) {
   Geom g;
   int rc = check_dims(dims, &g);
   if (rc) return rc;
@@ -302,9 +351,30 @@ int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, const fl
   if (injected_launch_failure()) return GDN_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float *qkv = static_cast<float *>(ws);
-  hipError_t e = launch_conv_plain(g, 1, x, conv_w, conv_state, qkv, s);
+  LaunchTimer tm(kernel_ms);
+  hipError_t e = tm.mark(s);
+  if (e == hipSuccess) e = launch_conv_plain(g, 1, x, conv_w, conv_state, qkv, s);
+  if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = launch_decode(g, qkv, z, gl, beta, rec_state, y, s);
+  if (e == hipSuccess) e = tm.mark(s);
+  if (e == hipSuccess) e = tm.elapsed();
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_decode_step");
+}
+
+int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, const float *gl,
+                    const float *beta, const void *conv_w, void *conv_state,
+                    float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream) {
+  return decode_impl(dims, x, z, gl, beta, conv_w, conv_state, rec_state, y, ws, ws_bytes,
+                     stream, nullptr);
+}
+
+int gdn_decode_step_timed(const gdn_dims *dims, const void *x, const void *z, const float *gl,
+                          const float *beta, const void *conv_w, void *conv_state,
+                          float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream,
+                          float *kernel_ms) {
+  if (!kernel_ms) return GDN_ERR_INVALID_ARG;
+  return decode_impl(dims, x, z, gl, beta, conv_w, conv_state, rec_state, y, ws, ws_bytes,
+                     stream, kernel_ms);
 }
 
 int gdn_state_check(const gdn_dims *dims, const void *blob, size_t blob_bytes) {

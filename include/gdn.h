@@ -152,6 +152,28 @@ GDN_API int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, 
                     const float *beta, const void *conv_w, void *conv_state,
                     float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream);
 
+/* Measurement variants ("Add a performance-parity Qwen3.8-27B Q4 and Q8 text
+ * backend on Metal", section Measurements and gates, asks for the conv, the
+ * prefill, the decode and the recurrent-state update to be measured in
+ * isolation).  Same arguments and effects as the plain calls, plus
+ * `kernel_ms`, which receives the duration of each kernel launch of the call,
+ * taken from HIP events that the library records on `stream` between its
+ * launches:
+ *   prefill: [0] conv + L2 norm, [1] chunk-local prep (Gram, (I+A)^{-1}, P),
+ *            [2] conv history roll, [3] state pass + gate          (4 floats)
+ *   decode:  [0] conv step + L2 norm, [1] state stream + gate      (2 floats)
+ * These variants create HIP events and wait for the last one before they
+ * return. */
+GDN_API int gdn_prefill_chunked_timed(const gdn_dims *dims, int64_t T, int32_t chunk,
+                                      const void *x, const void *z, const float *g,
+                                      const float *beta, const void *conv_w, void *conv_state,
+                                      float *rec_state, void *y, void *ws, size_t ws_bytes,
+                                      void *stream, float *kernel_ms);
+GDN_API int gdn_decode_step_timed(const gdn_dims *dims, const void *x, const void *z,
+                                  const float *g, const float *beta, const void *conv_w,
+                                  void *conv_state, float *rec_state, void *y, void *ws,
+                                  size_t ws_bytes, void *stream, float *kernel_ms);
+
 /* Session checkpoint of every GDN conv and recurrent component with
  * versioned validation (issue #95, section Implementation).
  * Blob layout (little-endian): a 128-byte header
