@@ -19,8 +19,11 @@
 namespace gdn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -37,11 +40,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Split x into hi + lo, both bf16: hi = bf16(x), lo = bf16(x - hi).  hi + lo
-// carries 16 significant bits of x.
+// Split a pair into hi + lo, both bf16 (round to nearest even, on gfx950's
+// packed convert): hi = bf16(x), lo = bf16(x - hi), so hi + lo carries 16
+// significant bits of x.  Returns each pair packed low element first.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  const f32x2 v = {a, b};
+  const bf16x2 h = __builtin_convertvector(v, bf16x2);
+  const f32x2 hf = __builtin_convertvector(h, f32x2);
+  const bf16x2 l = __builtin_convertvector(v - hf, bf16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
-  hi = f32_to_bf16_bits(x);
-  lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+  uint32_t h, l;
+  split2(x, 0.f, h, l);
+  hi = static_cast<uint16_t>(h);
+  lo = static_cast<uint16_t>(l);
 }
 
 template <int DT>  // 0 = fp32, 1 = bf16
@@ -60,8 +75,9 @@ __device__ __forceinline__ void store_elem(void *p, size_t i, float v) {
     static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(v);
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + __expf(-x)); }
+// Hardware reciprocal (1 ulp) instead of an IEEE division sequence.
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+__device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Causal width-4 conv of one channel: taps w0..w3 meet x[t-3]..x[t].  The
 // accumulation order is fixed so that every kernel gets the same bits.
@@ -121,16 +137,14 @@ __device__ __forceinline__ f32x4 mfma_split2(const u16x8 &a, const u16x8 &bh,
 // 16..31) into a split B (or A) operand with the permuted K order.
 __device__ __forceinline__ void pack_split(const f32x4 &t0, const f32x4 &t1, u16x8 &hi,
                                            u16x8 &lo) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    uint16_t h, l;
-    split_bf16(t0[r], h, l);
-    hi[r] = h;
-    lo[r] = l;
-    split_bf16(t1[r], h, l);
-    hi[4 + r] = h;
-    lo[4 + r] = l;
-  }
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split2(t0[0], t0[1], h0, l0);
+  split2(t0[2], t0[3], h1, l1);
+  split2(t1[0], t1[1], h2, l2);
+  split2(t1[2], t1[3], h3, l3);
+  const u32x4 h = {h0, h1, h2, h3}, l = {l0, l1, l2, l3};
+  hi = __builtin_bit_cast(u16x8, h);
+  lo = __builtin_bit_cast(u16x8, l);
 }
 
 // Position of index j (0..31) of a K step in the permuted slot order.

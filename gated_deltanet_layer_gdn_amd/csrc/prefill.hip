@@ -71,6 +71,8 @@ __device__ __forceinline__ u16x8 load8(const uint16_t *p) {
 
 __device__ __forceinline__ int tri_index(int mt, int nt) { return mt * (mt + 1) / 2 + nt; }
 
+
+
 // ---------------------------------------------------------------- prep kernel
 
 template <int D, int C>
@@ -222,10 +224,14 @@ __global__ __launch_bounds__(256) void prep_kernel(Geom g, PrefillWs L,
 
 // ---------------------------------------------------------------- state kernel
 
-template <int D>
+template <int D, int C>
 struct StateShape {
   static constexpr int NWV = D >= 128 ? 4 : 1;   // waves; each owns a slice of d_k
   static constexpr int NDT = D >= 32 ? 2 : 1;    // 16-wide d_k tiles per wave
+  // 16-row state tiles per block: two share every K / Q / K^T operand load
+  // (the partial sums of a 128-token chunk would not fit the LDS twice).
+  static constexpr int NB = (D >= 128 && C <= 64) ? 2 : 1;
+  static constexpr int ROWS = 16 * NB;           // state rows per block
   static constexpr int Dp = D < 32 ? 32 : D;
 };
 
@@ -238,195 +244,447 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return (bid % 8) * per + bid / 8;
 }
 
+// Load through a block-uniform base and a 32-bit byte offset (lets the
+// compiler use the scalar-base + vector-offset addressing form).
+template <typename V>
+__device__ __forceinline__ V ldb(const void *base, uint32_t byte_off) {
+  return *reinterpret_cast<const V *>(static_cast<const char *>(base) + byte_off);
+}
+
+// Per-chunk operands of one wave.  None of them depends on the state, so
+// each is fetched for the next chunk as soon as this chunk has consumed it
+// (into the same registers): every load has about one chunk of compute to
+// arrive.  Wave w owns the output tokens of tiles w, w + NWV, ...
+template <int NT, int MW, int KSC, int NDT, int NB>
+struct ChunkOps {
+  u16x8 kh[NT], kl[NT], qh[NT], ql[NT];  // A operands of K S^T / Q S^T (all tiles, own d_k slice)
+  float g0, g1, b0, b1;                  // lane t: g/beta of token t (and 64 + t)
+  float4 v[MW][NB];                      // V of the owned tiles (D-register order)
+  u16x8 tm[MW][KSC], ph[MW][KSC], pl[MW][KSC];  // (I+A)^{-1} and P rows of owned tiles
+  float z[MW][NB][4];                    // gate inputs of the owned outputs
+  u16x8 th[NDT][KSC], tl[NDT][KSC];      // A operands of the state update (own d_k slice)
+};
+
+// Four bf16 values of one D-register tile, hi and lo halves.
+struct Split4 {
+  uint2 hi, lo;
+};
+
 template <int D, int C, int DTZ, int DTY>
-__global__ __launch_bounds__(StateShape<D>::NWV * 64) void state_kernel(
+struct StateKernel {
+  using SS = StateShape<D, C>;
+  static constexpr int NWV = SS::NWV, NDT = SS::NDT, Dp = SS::Dp, NB = SS::NB;
+  static constexpr int NT = C / 16, Cp = C < 32 ? 32 : C, KSC = Cp / 32;
+  static constexpr int MW = (NT + NWV - 1) / NWV;  // output tiles per wave
+  using Ops = ChunkOps<NT, MW, KSC, NDT, NB>;
+
+  // Shared memory of one block.  Every tile is stored in D-register order
+  // (one entry per lane), so writes and reads are lane-contiguous.
+  struct Smem {
+    f32x4 part[NWV][2][NT][NB][64];  // K S^T / Q S^T partial sums of each wave's d_k slice
+    Split4 R[NT][NB][64];            // R tiles, split
+    Split4 U[NT][NB][64];            // U tiles, split (operand of P U)
+    Split4 DU[NT][NB][64];           // exp(G_last - G_t) U tiles, split (operand of the update)
+    float gate[NWV][3][C];           // per wave: gamma_t, exp(G_last - G_t), beta_t
+  };
+
+  // Block-uniform base pointers (advanced per chunk by uniform strides) and
+  // per-lane byte offsets, so that every load is base + 32-bit offset.
+  struct Ctx {
+    const uint16_t *khi, *klo, *qhi, *qlo;  // token-major rows of this key head
+    const uint16_t *kThi, *kTlo;            // dim-major blocks of this key head
+    const float *vT;                        // dim-major v of this value head
+    const uint16_t *Tm, *Ph, *Pl;           // chunk matrices of this value head
+    const float *gl, *beta;                 // [.][T][H_v] at (b, 0, h)
+    const void *z;                          // [.][T][H_v][D] at (b, 0, h, first row)
+    void *y;
+    int64_t T;
+    int H_v, NC, wave, lane, gq;
+    uint32_t o_tok, o_kT, o_v, o_mat, o_zy, o_g;  // byte offsets (o_zy: elements)
+  };
+
+  static __device__ __forceinline__ int valid_of(const Ctx &x, int chunk) {
+    const int64_t r = x.T - static_cast<int64_t>(chunk) * C;
+    return static_cast<int>(r < C ? r : C);
+  }
+
+  static __device__ __forceinline__ Split4 split4(const f32x4 &v) {
+    uint32_t h0, h1, l0, l1;
+    split2(v[0], v[1], h0, l0);
+    split2(v[2], v[3], h1, l1);
+    return Split4{make_uint2(h0, h1), make_uint2(l0, l1)};
+  }
+
+  // B operand of one 32-wide K step from two split tiles (second may be absent).
+  static __device__ __forceinline__ void operand(const Split4 &a, const Split4 &b, u16x8 &hi,
+                                                 u16x8 &lo) {
+    const u32x4 h = {a.hi.x, a.hi.y, b.hi.x, b.hi.y}, l = {a.lo.x, a.lo.y, b.lo.x, b.lo.y};
+    hi = __builtin_bit_cast(u16x8, h);
+    lo = __builtin_bit_cast(u16x8, l);
+  }
+
+  static __device__ __forceinline__ void load_head(const Ctx &x, int chunk, Ops &o) {
+    const size_t row = static_cast<size_t>(chunk) * C * Dp * 2;
+    const int n_valid = valid_of(x, chunk);
+    const char *kh = reinterpret_cast<const char *>(x.khi) + row;
+    const char *kl = reinterpret_cast<const char *>(x.klo) + row;
+    const char *qh = reinterpret_cast<const char *>(x.qhi) + row;
+    const char *ql = reinterpret_cast<const char *>(x.qlo) + row;
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const uint32_t ao = x.o_tok + 16 * m * Dp * 2;
+      o.kh[m] = ldb<u16x8>(kh, ao);
+      o.kl[m] = ldb<u16x8>(kl, ao);
+      o.qh[m] = ldb<u16x8>(qh, ao);
+      o.ql[m] = ldb<u16x8>(ql, ao);
+    }
+    const float *gb = x.gl + static_cast<size_t>(chunk) * C * x.H_v;
+    const float *bb = x.beta + static_cast<size_t>(chunk) * C * x.H_v;
+    const int t0 = x.lane, t1 = 64 + x.lane;
+    o.g0 = (t0 < C && t0 < n_valid) ? ldb<float>(gb, x.o_g) : 0.f;
+    o.b0 = (t0 < C && t0 < n_valid) ? ldb<float>(bb, x.o_g) : 0.f;
+    o.g1 = (C > 64 && t1 < n_valid) ? ldb<float>(gb, x.o_g + 64 * 4 * x.H_v) : 0.f;
+    o.b1 = (C > 64 && t1 < n_valid) ? ldb<float>(bb, x.o_g + 64 * 4 * x.H_v) : 0.f;
+  }
+
+  static __device__ __forceinline__ void load_v(const Ctx &x, int chunk, Ops &o) {
+    const float *base = x.vT + static_cast<size_t>(chunk) * C * D;
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int m = x.wave + i * NWV;
+      if (m < NT) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) o.v[i][n] = ldb<float4>(base, x.o_v + (m * 16 * D + n * 16 * 16) * 4);
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void load_tm(const Ctx &x, int chunk, Ops &o) {
+    const uint16_t *base = x.Tm + static_cast<size_t>(chunk) * C * Cp;
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int m = x.wave + i * NWV;
+      if (m < NT) {
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks)
+          if (ks <= m / 2) o.tm[i][ks] = ldb<u16x8>(base, x.o_mat + (16 * m * Cp + 32 * ks) * 2);
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void load_pz(const Ctx &x, int chunk, Ops &o) {
+    const size_t mo = static_cast<size_t>(chunk) * C * Cp;
+    const uint16_t *ph = x.Ph + mo;
+    const uint16_t *pl = x.Pl + mo;
+    const int n_valid = valid_of(x, chunk);
+    constexpr int ez = DTZ == 0 ? 4 : 2;
+    const char *zb = static_cast<const char *>(x.z) + static_cast<size_t>(chunk) * C * x.H_v * D * ez;
+    const uint32_t tstride = x.H_v * D * ez;
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int m = x.wave + i * NWV;
+      if (m < NT) {
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks)
+          if (ks <= m / 2) {
+            const uint32_t ao = x.o_mat + (16 * m * Cp + 32 * ks) * 2;
+            o.ph[i][ks] = ldb<u16x8>(ph, ao);
+            o.pl[i][ks] = ldb<u16x8>(pl, ao);
+          }
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * m + 4 * x.gq + r;
+            float v = 0.f;
+            if (t < n_valid) {
+              const uint32_t zo = (x.o_zy + 16 * n) * ez + (16 * m + r) * tstride;
+              if constexpr (DTZ == 0)
+                v = ldb<float>(zb, zo);
+              else
+                v = bf16_bits_to_f32(ldb<uint16_t>(zb, zo));
+            }
+            o.z[i][n][r] = v;
+          }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void load_kT(const Ctx &x, int chunk, Ops &o) {
+    // The 32-token key block that holds the chunk (a 16-token chunk with an
+    // odd index sits in the second half of its block).
+    const size_t base = static_cast<size_t>((static_cast<int64_t>(chunk) * C) & ~int64_t(31)) * D;
+    const uint16_t *th = x.kThi + base;
+    const uint16_t *tl = x.kTlo + base;
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t ao = x.o_kT + (ks * D + 16 * dt) * 32 * 2;
+        o.th[dt][ks] = ldb<u16x8>(th, ao);
+        o.tl[dt][ks] = ldb<u16x8>(tl, ao);
+      }
+  }
+
+  static __device__ __forceinline__ void load_all(const Ctx &x, int chunk, Ops &o) {
+    load_head(x, chunk, o);
+    load_v(x, chunk, o);
+    load_tm(x, chunk, o);
+    load_pz(x, chunk, o);
+    load_kT(x, chunk, o);
+  }
+
+  // One chunk.  On entry `o` holds this chunk's operands (loads possibly in
+  // flight); on exit it holds the next chunk's.  Three barriers: after the
+  // K S^T / Q S^T partials, after the R tiles, after the U tiles.  The gated
+  // outputs are stored last, after every load for the next chunk is issued,
+  // so that no later wait on those loads also waits for these stores.
+  static __device__ __forceinline__ void chunk_step(const Ctx &x, int chunk, Ops &o,
+                                                    f32x4 (&st)[NB][NDT], Smem &sm) {
+    const int lane = x.lane, wave = x.wave, gq = x.gq;
+    const int n_valid = valid_of(x, chunk);
+    const bool more = chunk + 1 < x.NC;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const Split4 none = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+
+    // Gates, once per lane (lane t = token t), into this wave's table.
+    {
+      const float G0 = wave_incl_scan(o.g0);
+      float G1 = 0.f;
+      if constexpr (C > 64) G1 = wave_incl_scan(o.g1) + __shfl(G0, 63, kWave);
+      const float Glast = C > 64 ? __shfl(G1, (C - 1) & 63, kWave) : __shfl(G0, C - 1, kWave);
+      if (lane < C) {
+        sm.gate[wave][0][lane] = __expf(G0);
+        sm.gate[wave][1][lane] = __expf(Glast - G0);
+        sm.gate[wave][2][lane] = o.b0;
+      }
+      if constexpr (C > 64) {
+        sm.gate[wave][0][64 + lane] = __expf(G1);
+        sm.gate[wave][1][64 + lane] = __expf(Glast - G1);
+        sm.gate[wave][2][64 + lane] = o.b1;
+      }
+    }
+    const float *gt = sm.gate[wave][0];
+    const float *dl = sm.gate[wave][1];
+    const float *bt = sm.gate[wave][2];
+
+    // 1. Partial K S^T and Q S^T over this wave's d_k slice, all token tiles.
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      u16x8 bh, bl;
+      pack_split(st[n][0], NDT > 1 ? st[n][NDT - 1] : zero, bh, bl);
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        sm.part[wave][0][m][n][lane] = mfma_split3(o.kh[m], o.kl[m], bh, bl, zero);
+        sm.part[wave][1][m][n][lane] = mfma_split3(o.qh[m], o.ql[m], bh, bl, zero);
+      }
+    }
+    if (more) load_head(x, chunk + 1, o);
+    __syncthreads();
+
+    // 2. Owned tiles: R = beta (V - gamma K S^T), published split; Q S^T kept.
+    f32x4 qs[MW][NB];
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int m = wave + i * NWV;
+      if (m < NT) {
+        const float4 g4 = *reinterpret_cast<const float4 *>(gt + 16 * m + 4 * gq);
+        const float4 b4 = *reinterpret_cast<const float4 *>(bt + 16 * m + 4 * gq);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          f32x4 ks = sm.part[0][0][m][n][lane];
+          qs[i][n] = sm.part[0][1][m][n][lane];
+#pragma unroll
+          for (int w = 1; w < NWV; ++w) {
+            ks += sm.part[w][0][m][n][lane];
+            qs[i][n] += sm.part[w][1][m][n][lane];
+          }
+          const float4 vv = o.v[i][n];
+          const f32x4 r = {b4.x * (vv.x - g4.x * ks[0]), b4.y * (vv.y - g4.y * ks[1]),
+                           b4.z * (vv.z - g4.z * ks[2]), b4.w * (vv.w - g4.w * ks[3])};
+          sm.R[m][n][lane] = split4(r);
+        }
+      }
+    }
+    if (more) load_v(x, chunk + 1, o);
+    __syncthreads();
+
+    // 3. Owned tiles: U = Tm R, published split, also scaled by exp(G_last - G_t).
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int m = wave + i * NWV;
+      if (m < NT) {
+        const float4 d4 = *reinterpret_cast<const float4 *>(dl + 16 * m + 4 * gq);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          f32x4 acc = zero;
+#pragma unroll
+          for (int ks = 0; ks < KSC; ++ks)
+            if (ks <= m / 2) {
+              u16x8 bh, bl;
+              operand(sm.R[2 * ks][n][lane],
+                      (2 * ks + 1 < NT) ? sm.R[(2 * ks + 1) % NT][n][lane] : none, bh, bl);
+              acc = mfma_split2(o.tm[i][ks], bh, bl, acc);
+            }
+          sm.U[m][n][lane] = split4(acc);
+          const f32x4 du = {d4.x * acc[0], d4.y * acc[1], d4.z * acc[2], d4.w * acc[3]};
+          sm.DU[m][n][lane] = split4(du);
+        }
+      }
+    }
+    if (more) load_tm(x, chunk + 1, o);
+    __syncthreads();
+
+    // 4. Owned tiles: O = gamma Q S^T + P U, gated (stored at the end).
+    f32x4 out[MW][NB];
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int m = wave + i * NWV;
+      if (m < NT) {
+        const float4 g4 = *reinterpret_cast<const float4 *>(gt + 16 * m + 4 * gq);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          f32x4 acc = {g4.x * qs[i][n][0], g4.y * qs[i][n][1], g4.z * qs[i][n][2], g4.w * qs[i][n][3]};
+#pragma unroll
+          for (int ks = 0; ks < KSC; ++ks)
+            if (ks <= m / 2) {
+              u16x8 bh, bl;
+              operand(sm.U[2 * ks][n][lane],
+                      (2 * ks + 1 < NT) ? sm.U[(2 * ks + 1) % NT][n][lane] : none, bh, bl);
+              acc = mfma_split3(o.ph[i][ks], o.pl[i][ks], bh, bl, acc);
+            }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) out[i][n][r] = acc[r] * sigmoidf_(o.z[i][n][r]);
+        }
+      }
+    }
+    if (more) load_pz(x, chunk + 1, o);
+
+    // 5. S^T <- gamma_last S^T + K^T (D_last * U) over this wave's d_k slice.
+    {
+      const float gl_last = gt[C - 1];
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) st[n][dt] *= gl_last;
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+          Split4 a = sm.DU[2 * ks < NT ? 2 * ks : 0][n][lane];
+          Split4 b = (2 * ks + 1 < NT) ? sm.DU[(2 * ks + 1) % NT][n][lane] : none;
+          // A 16-token chunk fills one half of a 32-token key block.
+          if (C == 16 && (chunk & 1)) {
+            b = a;
+            a = none;
+          }
+          u16x8 bh, bl;
+          operand(a, b, bh, bl);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            st[n][dt] = mfma_split3(o.th[dt][ks], o.tl[dt][ks], bh, bl, st[n][dt]);
+        }
+      }
+    }
+    if (more) load_kT(x, chunk + 1, o);
+
+    // 6. Gated outputs of the owned tiles.
+    constexpr int ey = DTY == 0 ? 4 : 2;
+    char *yb = static_cast<char *>(x.y) + static_cast<size_t>(chunk) * C * x.H_v * D * ey;
+    const uint32_t tstride = x.H_v * D * ey;
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int m = wave + i * NWV;
+      if (m < NT) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * m + 4 * gq + r;
+            if (t < n_valid) {
+              char *dst = yb + (x.o_zy + 16 * n) * ey + (16 * m + r) * tstride;
+              if constexpr (DTY == 0)
+                *reinterpret_cast<float *>(dst) = out[i][n][r];
+              else
+                *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16_bits(out[i][n][r]);
+            }
+          }
+      }
+    }
+  }
+};
+
+template <int D, int C, int DTZ, int DTY>
+__global__ __launch_bounds__((StateShape<D, C>::NWV * 64)) void state_kernel(
     Geom g, PrefillWs L, const void *__restrict__ z, const float *__restrict__ gl,
     const float *__restrict__ beta, float *__restrict__ S, void *__restrict__ y,
     const char *__restrict__ ws) {
-  using SS = StateShape<D>;
-  constexpr int NWV = SS::NWV, NDT = SS::NDT, Dp = SS::Dp;
-  constexpr int NT = C / 16, Cp = C < 32 ? 32 : C, KSC = Cp / 32;
-  __shared__ float part[NWV][2][NT][4][64];  // K S^T / Q S^T partial sums
-  __shared__ float Ush[NT][4][64];           // U tiles in D-register order
+  using K = StateKernel<D, C, DTZ, DTY>;
+  constexpr int NDT = K::NDT, NB = K::NB, Dp = K::Dp, Cp = K::Cp, ROWS = StateShape<D, C>::ROWS;
+  __shared__ typename K::Smem sm;
 
-  const int RB = D / 16;
-  const int nblk = g.B * g.H_v * RB;
-  const int lid = xcd_remap(blockIdx.x, nblk);
+  const int RB = D / ROWS;
+  const int lid = xcd_remap(blockIdx.x, g.B * g.H_v * RB);
   const int rb = lid % RB;
   const int h = (lid / RB) % g.H_v;
   const int b = lid / (RB * g.H_v);
   const int kh = h / g.G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, gq = lane >> 4;
 
-  // S^T tiles of this wave: rows d_k = 32*wave + 16*dt + 4*gq + r, column = state row 16*rb + c.
-  float *Sh = S + ((static_cast<size_t>(b) * g.H_v + h) * D + 16 * rb + c) * D;
-  f32x4 st[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    const float4 v = *reinterpret_cast<const float4 *>(Sh + 32 * wave + 16 * dt + 4 * gq);
-    st[dt] = f32x4{v.x, v.y, v.z, v.w};
-  }
-
-  const uint16_t *khi = reinterpret_cast<const uint16_t *>(ws + L.k_hi);
-  const uint16_t *klo = reinterpret_cast<const uint16_t *>(ws + L.k_lo);
-  const uint16_t *qhi = reinterpret_cast<const uint16_t *>(ws + L.q_hi);
-  const uint16_t *qlo = reinterpret_cast<const uint16_t *>(ws + L.q_lo);
-  const uint16_t *kThi = reinterpret_cast<const uint16_t *>(ws + L.kT_hi);
-  const uint16_t *kTlo = reinterpret_cast<const uint16_t *>(ws + L.kT_lo);
-  const float *vT = reinterpret_cast<const float *>(ws + L.vT);
+  typename K::Ctx x;
   const size_t kbase = (static_cast<size_t>(b) * g.H_k + kh) * L.T_pad;
-  const size_t kTbase = (static_cast<size_t>(b) * g.H_k + kh) * (L.T_pad / 32);
-  const size_t vbase = (static_cast<size_t>(b) * g.H_v + h) * (L.T_pad / 16);
+  x.khi = reinterpret_cast<const uint16_t *>(ws + L.k_hi) + kbase * Dp;
+  x.klo = reinterpret_cast<const uint16_t *>(ws + L.k_lo) + kbase * Dp;
+  x.qhi = reinterpret_cast<const uint16_t *>(ws + L.q_hi) + kbase * Dp;
+  x.qlo = reinterpret_cast<const uint16_t *>(ws + L.q_lo) + kbase * Dp;
+  x.kThi = reinterpret_cast<const uint16_t *>(ws + L.kT_hi) + kbase * D;
+  x.kTlo = reinterpret_cast<const uint16_t *>(ws + L.kT_lo) + kbase * D;
+  x.vT = reinterpret_cast<const float *>(ws + L.vT) +
+         (static_cast<size_t>(b) * g.H_v + h) * L.T_pad * D;
+  const size_t mat = (static_cast<size_t>(b) * g.H_v + h) * L.NC * C * Cp;
+  x.Tm = reinterpret_cast<const uint16_t *>(ws + L.Tm) + mat;
+  x.Ph = reinterpret_cast<const uint16_t *>(ws + L.P_hi) + mat;
+  x.Pl = reinterpret_cast<const uint16_t *>(ws + L.P_lo) + mat;
+  x.gl = gl + static_cast<size_t>(b) * L.T * g.H_v + h;
+  x.beta = beta + static_cast<size_t>(b) * L.T * g.H_v + h;
+  const size_t zy = (static_cast<size_t>(b) * L.T * g.H_v + h) * D + ROWS * rb;
+  x.z = static_cast<const char *>(z) + zy * (DTZ == 0 ? 4 : 2);
+  x.y = static_cast<char *>(y) + zy * (DTY == 0 ? 4 : 2);
+  x.T = L.T;
+  x.H_v = g.H_v;
+  x.NC = L.NC;
+  x.wave = wave;
+  x.lane = lane;
+  x.gq = gq;
+  x.o_tok = (c * Dp + 32 * wave + 8 * gq) * 2;
+  x.o_kT = ((32 * wave + c) * 32 + 8 * gq) * 2;
+  x.o_v = ((ROWS * rb + c) * 16 + 4 * gq) * 4;
+  x.o_mat = (c * Cp + 8 * gq) * 2;
+  x.o_zy = 4 * gq * g.H_v * D + c;
+  x.o_g = lane * g.H_v * 4;
 
-  for (int chunk = 0; chunk < L.NC; ++chunk) {
-    const int64_t tau0 = static_cast<int64_t>(chunk) * C;
-    const int n_valid = static_cast<int>((L.T - tau0) < C ? (L.T - tau0) : C);
-    const size_t gbase = (static_cast<size_t>(b) * L.T + tau0) * g.H_v + h;
-
-    // Gates for this chunk (every wave computes the same values).
-    float g0, g1;
-    chunk_prefix<C>(gl, gbase, g.H_v, n_valid, g0, g1);
-    const float Glast = prefix_at<C>(g0, g1, C - 1);
-
-    // 1. Partial K S^T and Q S^T over this wave's d_k slice.
-    {
-      u16x8 bh, bl;
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      pack_split(st[0], NDT > 1 ? st[NDT - 1] : zero, bh, bl);
+  // S^T tiles: for state-row tile n, rows d_k = 32*wave + 16*dt + 4*gq + r,
+  // column = state row ROWS*rb + 16*n + c.
+  float *Sh = S + ((static_cast<size_t>(b) * g.H_v + h) * D + ROWS * rb + c) * D;
+  f32x4 st[NB][NDT];
 #pragma unroll
-      for (int m = 0; m < NT; ++m) {
-        const size_t ao = (kbase + tau0 + 16 * m + c) * Dp + 32 * wave + 8 * gq;
-        f32x4 ak = mfma_split3(load8(khi + ao), load8(klo + ao), bh, bl, zero);
-        f32x4 aq = mfma_split3(load8(qhi + ao), load8(qlo + ao), bh, bl, zero);
+  for (int n = 0; n < NB; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          part[wave][0][m][r][lane] = ak[r];
-          part[wave][1][m][r][lane] = aq[r];
-        }
-      }
-    }
-    __syncthreads();
-
-    // 2. R tiles (needed up to this wave's last output tile), then U = Tm R.
-    int max_m = -1;
-    for (int m = wave; m < NT; m += NWV) max_m = m;
-    const size_t mat = ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C * Cp;
-    const uint16_t *Tm = reinterpret_cast<const uint16_t *>(ws + L.Tm) + mat;
-    const uint16_t *Ph = reinterpret_cast<const uint16_t *>(ws + L.P_hi) + mat;
-    const uint16_t *Pl = reinterpret_cast<const uint16_t *>(ws + L.P_lo) + mat;
-    f32x4 Rt[NT];
-#pragma unroll
-    for (int m = 0; m < NT; ++m) {
-      Rt[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (m <= max_m) {
-        const float4 vv = *reinterpret_cast<const float4 *>(
-            vT + ((vbase + (tau0 + 16 * m) / 16) * D + 16 * rb + c) * 16 + 4 * gq);
-        const float va[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * m + 4 * gq + r;
-          float ks = 0.f;
-#pragma unroll
-          for (int w = 0; w < NWV; ++w) ks += part[w][0][m][r][lane];
-          const float Gt = prefix_at<C>(g0, g1, t);
-          const float bt = (t < n_valid) ? beta[gbase + static_cast<size_t>(t) * g.H_v] : 0.f;
-          Rt[m][r] = bt * (va[r] - __expf(Gt) * ks);
-        }
-      }
-    }
-    for (int m = wave; m < NT; m += NWV) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks <= m / 2; ++ks) {
-        u16x8 bh, bl;
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        pack_split(Rt[2 * ks], (2 * ks + 1 < NT) ? Rt[2 * ks + 1] : zero, bh, bl);
-        acc = mfma_split2(load8(Tm + static_cast<size_t>(16 * m + c) * Cp + 32 * ks + 8 * gq), bh, bl,
-                          acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ush[m][r][lane] = acc[r];
-    }
-    __syncthreads();
-
-    // 3. O = gamma * QS + P U, gated store.
-    for (int m = wave; m < NT; m += NWV) {
-      f32x4 acc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * m + 4 * gq + r;
-        float qs = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWV; ++w) qs += part[w][1][m][r][lane];
-        acc[r] = __expf(prefix_at<C>(g0, g1, t)) * qs;
-      }
-      for (int ks = 0; ks <= m / 2; ++ks) {
-        f32x4 u0, u1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) u0[r] = Ush[2 * ks][r][lane];
-        if (2 * ks + 1 < NT) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) u1[r] = Ush[2 * ks + 1][r][lane];
-        }
-        u16x8 bh, bl;
-        pack_split(u0, u1, bh, bl);
-        const size_t ao = static_cast<size_t>(16 * m + c) * Cp + 32 * ks + 8 * gq;
-        acc = mfma_split3(load8(Ph + ao), load8(Pl + ao), bh, bl, acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * m + 4 * gq + r;
-        if (t < n_valid) {
-          const size_t yi = ((static_cast<size_t>(b) * L.T + tau0 + t) * g.H_v + h) * D + 16 * rb + c;
-          store_elem<DTY>(y, yi, acc[r] * sigmoidf_(load_elem<DTZ>(z, yi)));
-        }
-      }
+    for (int dt = 0; dt < NDT; ++dt) {
+      const float4 v = *reinterpret_cast<const float4 *>(Sh + 16 * n * D + 32 * wave + 16 * dt + 4 * gq);
+      st[n][dt] = f32x4{v.x, v.y, v.z, v.w};
     }
 
-    // 4. S^T <- gamma_last S^T + K^T (D_last * U) for this wave's d_k slice.
-    {
-      const float gl_last = __expf(Glast);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[dt][r] *= gl_last;
-#pragma unroll
-      for (int ks = 0; ks < KSC; ++ks) {
-        f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int m = 2 * ks + half;
-          if (m < NT) {
-            f32x4 &u = half ? u1 : u0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = 16 * m + 4 * gq + r;
-              u[r] = __expf(Glast - prefix_at<C>(g0, g1, t)) * Ush[m][r][lane];
-            }
-          }
-        }
-        // A 16-token chunk fills one half of a 32-token key block.
-        if (C == 16 && (tau0 & 16)) {
-          u1 = u0;
-          u0 = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        u16x8 bh, bl;
-        pack_split(u0, u1, bh, bl);
-        const size_t blk = kTbase + (tau0 + 32 * ks) / 32;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const size_t ao = (blk * D + 32 * wave + 16 * dt + c) * 32 + 8 * gq;
-          st[dt] = mfma_split3(load8(kThi + ao), load8(kTlo + ao), bh, bl, st[dt]);
-        }
-      }
-    }
-    __syncthreads();
-  }
+  typename K::Ops ops;
+  K::load_all(x, 0, ops);
+  for (int chunk = 0; chunk < L.NC; ++chunk) K::chunk_step(x, chunk, ops, st, sm);
 
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-    *reinterpret_cast<float4 *>(Sh + 32 * wave + 16 * dt + 4 * gq) =
-        make_float4(st[dt][0], st[dt][1], st[dt][2], st[dt][3]);
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<float4 *>(Sh + 16 * n * D + 32 * wave + 16 * dt + 4 * gq) =
+          make_float4(st[n][dt][0], st[n][dt][1], st[n][dt][2], st[n][dt][3]);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -459,8 +717,8 @@ hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *g
 template <int D, int C>
 static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, const float *gl,
                            const float *beta, float *S, void *y, const char *ws, hipStream_t s) {
-  dim3 grid(g.B * g.H_v * (D / 16));
-  dim3 block(StateShape<D>::NWV * 64);
+  dim3 grid(g.B * g.H_v * (D / StateShape<D, C>::ROWS));
+  dim3 block(StateShape<D, C>::NWV * 64);
   const int key = (g.in_dt << 1) | g.out_dt;
   switch (key) {
     case 0: hipLaunchKernelGGL((state_kernel<D, C, 0, 0>), grid, block, 0, s, g, L, z, gl, beta, S, y, ws); break;
