@@ -77,6 +77,9 @@ def main():
                     help="graph replays per decode timing (each replays R rotated steps)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run --steps plain device copies of MIB MiB (for scaling the HBM "
+                         "byte counters of rocprofv3 against a kernel of known traffic)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -95,6 +98,17 @@ def main():
         from gated_deltanet_layer_gdn_amd import build as _b
         _b.build()
     torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "copies": args.steps}), flush=True)
+        return
 
     def dev(a):
         if a.dtype == np.uint16:
