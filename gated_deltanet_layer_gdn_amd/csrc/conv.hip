@@ -135,8 +135,9 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
     const int j = ch % D;
     if (is_q || is_k) {
       const int kh = (is_q ? ch : ch - nq) / D;
-      const size_t row0 = (static_cast<size_t>(b) * g.H_k + kh) * L.T_pad + t0;
-      const int pos = (j & ~31) + kslot(j & 31);
+      // slice-major: [b][kh][j / 32][t][32]
+      const size_t row0 = ((static_cast<size_t>(b) * g.H_k + kh) * (L.Dp / 32) + (j >> 5)) * L.T_pad + t0;
+      const int pos = kslot(j & 31);
       uint16_t *phi = reinterpret_cast<uint16_t *>(a.ws + (is_q ? L.q_hi : L.k_hi));
       uint16_t *plo = reinterpret_cast<uint16_t *>(a.ws + (is_q ? L.q_lo : L.k_lo));
       uint16_t hi[TT], lo[TT];
@@ -151,11 +152,11 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
       }
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-        phi[(row0 + t) * L.Dp + pos] = hi[t];
-        plo[(row0 + t) * L.Dp + pos] = lo[t];
+        phi[(row0 + t) * 32 + pos] = hi[t];
+        plo[(row0 + t) * 32 + pos] = lo[t];
         if constexpr (D < 32) {  // zero the unused half of the 32-wide K step
-          phi[(row0 + t) * L.Dp + kslot(j + 16)] = 0;
-          plo[(row0 + t) * L.Dp + kslot(j + 16)] = 0;
+          phi[(row0 + t) * 32 + kslot(j + 16)] = 0;
+          plo[(row0 + t) * 32 + kslot(j + 16)] = 0;
         }
       }
       if (is_k) {

@@ -188,6 +188,7 @@ bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *w) {
   w->Tm = take(mat);
   w->P_hi = take(mat);
   w->P_lo = take(mat);
+  w->gates = take(static_cast<size_t>(g.B) * g.H_v * w->NC * 3 * C * 4);
   w->total = off;
   return true;
 }
@@ -283,7 +284,7 @@ static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const vo
   const size_t es = esize(g.in_dt), eo = esize(g.out_dt);
   const size_t bt = static_cast<size_t>(g.B) * T;
   const Buf in[] = {{x, bt * g.C_ch * es, es},
-                    {z, bt * g.H_v * g.D * es, es},
+                    {z, bt * g.H_v * g.D * es, 16},
                     {gl, bt * g.H_v * 4, 4},
                     {beta, bt * g.H_v * 4, 4},
                     {conv_w, static_cast<size_t>(g.C_ch) * g.W * es, es}};
@@ -304,7 +305,7 @@ static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const vo
   if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = launch_conv_roll(g, T, x, conv_state, s);
   if (e == hipSuccess) e = tm.mark(s);
-  if (e == hipSuccess) e = launch_prefill_state(g, L, z, gl, beta, rec_state, y, w, s);
+  if (e == hipSuccess) e = launch_prefill_state(g, L, z, rec_state, y, w, s);
   if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = tm.elapsed();
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_prefill_chunked");

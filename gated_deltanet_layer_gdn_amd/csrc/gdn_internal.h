@@ -19,18 +19,21 @@ struct Geom {
 
 // Prefill workspace carve-up (byte offsets from the workspace base, each
 // 256-byte aligned).  Dp = max(D, 32); Cp = max(C, 32); T_pad = T rounded up
-// to a multiple of Cp; NC = T_pad / C chunks.
-//   q/k token-major   [B][H_k][T_pad][Dp]     bf16 hi and lo, head-dim in
-//                                               permuted K order per 32
+// to a multiple of Cp; NC = ceil(T / C) chunks.
+//   q/k token-major   [B][H_k][Dp/32][T_pad][32] bf16 hi and lo: each 32-wide
+//                                               slice of the head dimension in
+//                                               permuted K order, slice-major
 //   k dim-major       [B][H_k][T_pad/32][D][32] bf16 hi and lo, tokens in
 //                                               permuted K order
 //   v dim-major       [B][H_v][T_pad/16][D][16] fp32
 //   T = (I + A)^{-1}  [B][H_v][NC][C][Cp]      bf16, columns permuted
 //   P = tril(D) * QK^T [B][H_v][NC][C][Cp]     bf16 hi and lo, columns permuted
+//   gates             [B][H_v][NC][3][C]       fp32: gamma_t = exp(G_t),
+//                                               exp(G_last - G_t), beta_t
 struct PrefillWs {
   int64_t T, T_pad;
   int C, Cp, Dp, NC;
-  size_t q_hi, q_lo, k_hi, k_lo, kT_hi, kT_lo, vT, Tm, P_hi, P_lo;
+  size_t q_hi, q_lo, k_hi, k_lo, kT_hi, kT_lo, vT, Tm, P_hi, P_lo, gates;
   size_t total;
 };
 
@@ -48,8 +51,7 @@ hipError_t launch_decode(const Geom &g, const float *qkv, const void *z, const f
                          const float *beta, float *S, void *y, hipStream_t s);
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
                                const float *beta, char *ws, hipStream_t s);
-hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z,
-                                const float *gl, const float *beta, float *S, void *y,
-                                const char *ws, hipStream_t s);
+hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z, float *S,
+                                void *y, const char *ws, hipStream_t s);
 
 }  // namespace gdn

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Geom g, PrefillWs L,
 
   // 1. K K^T and Q K^T, lower tiles only, split operands.
   {
-    const size_t row0 = (static_cast<size_t>(b) * g.H_k + kh) * L.T_pad + tau0;
+    const size_t head0 = (static_cast<size_t>(b) * g.H_k + kh) * (Dp / 32);  // first 32-slice
     const uint16_t *khi = reinterpret_cast<const uint16_t *>(ws + L.k_hi);
     const uint16_t *klo = reinterpret_cast<const uint16_t *>(ws + L.k_lo);
     const uint16_t *qhi = reinterpret_cast<const uint16_t *>(ws + L.q_hi);
@@ -121,8 +121,9 @@ __global__ __launch_bounds__(256) void prep_kernel(Geom g, PrefillWs L,
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < Sh::KS_D; ++ks) {
-        const size_t ao = (row0 + 16 * mt + c) * Dp + 32 * ks + 8 * gq;
-        const size_t bo = (row0 + 16 * nt + c) * Dp + 32 * ks + 8 * gq;
+        const size_t slice = (head0 + ks) * L.T_pad + tau0;
+        const size_t ao = (slice + 16 * mt + c) * 32 + 8 * gq;
+        const size_t bo = (slice + 16 * nt + c) * 32 + 8 * gq;
         acc = mfma_split3(load8(ah + ao), load8(al + ao), load8(khi + bo), load8(klo + bo), acc);
       }
       float *dst = is_q ? QK[tri] : KK[tri];
@@ -149,6 +150,17 @@ __global__ __launch_bounds__(256) void prep_kernel(Geom g, PrefillWs L,
       }
     }
     __syncthreads();
+
+    // Gate factors of this chunk for the state pass.
+    {
+      float *gt = reinterpret_cast<float *>(ws + L.gates) +
+                  ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * 3 * C;
+      for (int t = threadIdx.x; t < C; t += blockDim.x) {
+        gt[t] = __expf(Gs[t]);
+        gt[C + t] = __expf(Gs[C - 1] - Gs[t]);
+        gt[2 * C + t] = Bs[t];
+      }
+    }
 
     // A[t][s] = beta_t exp(G_t - G_s) KK[t][s] for s < t.
     auto Aval = [&](int t, int s) -> float {
@@ -255,13 +267,14 @@ __device__ __forceinline__ V ldb(const void *base, uint32_t byte_off) {
 // each is fetched for the next chunk as soon as this chunk has consumed it
 // (into the same registers): every load has about one chunk of compute to
 // arrive.  Wave w owns the output tokens of tiles w, w + NWV, ...
-template <int NT, int MW, int KSC, int NDT, int NB>
+template <int NT, int MW, int KSC, int NDT, int NB, int ZK>
 struct ChunkOps {
   u16x8 kh[NT], kl[NT], qh[NT], ql[NT];  // A operands of K S^T / Q S^T (all tiles, own d_k slice)
-  float g0, g1, b0, b1;                  // lane t: g/beta of token t (and 64 + t)
+  float4 gam[MW], dl[MW], bt[MW];        // gate factors of the owned tiles (D-register order)
+  float glast;                           // gamma of the chunk's last token
   float4 v[MW][NB];                      // V of the owned tiles (D-register order)
   u16x8 tm[MW][KSC], ph[MW][KSC], pl[MW][KSC];  // (I+A)^{-1} and P rows of owned tiles
-  float z[MW][NB][4];                    // gate inputs of the owned outputs
+  uint4 z[MW][ZK];                       // gate inputs of the owned tiles, token-major 16-byte pieces
   u16x8 th[NDT][KSC], tl[NDT][KSC];      // A operands of the state update (own d_k slice)
 };
 
@@ -273,10 +286,13 @@ struct Split4 {
 template <int D, int C, int DTZ, int DTY>
 struct StateKernel {
   using SS = StateShape<D, C>;
-  static constexpr int NWV = SS::NWV, NDT = SS::NDT, Dp = SS::Dp, NB = SS::NB;
+  static constexpr int NWV = SS::NWV, NDT = SS::NDT, Dp = SS::Dp, NB = SS::NB, ROWS = SS::ROWS;
   static constexpr int NT = C / 16, Cp = C < 32 ? 32 : C, KSC = Cp / 32;
   static constexpr int MW = (NT + NWV - 1) / NWV;  // output tiles per wave
-  using Ops = ChunkOps<NT, MW, KSC, NDT, NB>;
+  static constexpr int EZ = DTZ == 0 ? 4 : 2;      // bytes per z element
+  static constexpr int ZL = ROWS * EZ / 16;        // 16-byte pieces per token row of z
+  static constexpr int ZK = (16 * ZL + 63) / 64;   // pieces per lane per tile
+  using Ops = ChunkOps<NT, MW, KSC, NDT, NB, ZK>;
 
   // Shared memory of one block.  Every tile is stored in D-register order
   // (one entry per lane), so writes and reads are lane-contiguous.
@@ -285,22 +301,22 @@ struct StateKernel {
     Split4 R[NT][NB][64];            // R tiles, split
     Split4 U[NT][NB][64];            // U tiles, split (operand of P U)
     Split4 DU[NT][NB][64];           // exp(G_last - G_t) U tiles, split (operand of the update)
-    float gate[NWV][3][C];           // per wave: gamma_t, exp(G_last - G_t), beta_t
+    uint4 z[NWV][16 * ZL];           // per wave: one token tile of z, token-major
   };
 
-  // Block-uniform base pointers (advanced per chunk by uniform strides) and
+  // Wave-uniform base pointers (advanced per chunk by uniform strides) and
   // per-lane byte offsets, so that every load is base + 32-bit offset.
   struct Ctx {
-    const uint16_t *khi, *klo, *qhi, *qlo;  // token-major rows of this key head
+    const uint16_t *khi, *klo, *qhi, *qlo;  // this wave's 32-slice of the token-major rows
     const uint16_t *kThi, *kTlo;            // dim-major blocks of this key head
     const float *vT;                        // dim-major v of this value head
     const uint16_t *Tm, *Ph, *Pl;           // chunk matrices of this value head
-    const float *gl, *beta;                 // [.][T][H_v] at (b, 0, h)
+    const float *gates;                     // gate table of this value head
     const void *z;                          // [.][T][H_v][D] at (b, 0, h, first row)
     void *y;
     int64_t T;
     int H_v, NC, wave, lane, gq;
-    uint32_t o_tok, o_kT, o_v, o_mat, o_zy, o_g;  // byte offsets (o_zy: elements)
+    uint32_t o_tok, o_kT, o_v, o_mat, o_zy, o_gate;  // byte offsets (o_zy: elements)
   };
 
   static __device__ __forceinline__ int valid_of(const Ctx &x, int chunk) {
@@ -323,39 +339,51 @@ struct StateKernel {
     lo = __builtin_bit_cast(u16x8, l);
   }
 
+  // The loads below are branch-free (indices are clamped instead, so a load
+  // that is not needed re-reads a valid address): the compiler then knows
+  // exactly which loads are outstanding and waits only for the ones a
+  // product needs, keeping the next chunk's loads in flight.
+  static __device__ __forceinline__ int own_tile(const Ctx &x, int i) {
+    const int m = x.wave + i * NWV;
+    return m < NT ? m : NT - 1;
+  }
+
   static __device__ __forceinline__ void load_head(const Ctx &x, int chunk, Ops &o) {
-    const size_t row = static_cast<size_t>(chunk) * C * Dp * 2;
-    const int n_valid = valid_of(x, chunk);
+    const size_t row = static_cast<size_t>(chunk) * C * 32 * 2;
     const char *kh = reinterpret_cast<const char *>(x.khi) + row;
     const char *kl = reinterpret_cast<const char *>(x.klo) + row;
     const char *qh = reinterpret_cast<const char *>(x.qhi) + row;
     const char *ql = reinterpret_cast<const char *>(x.qlo) + row;
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
-      const uint32_t ao = x.o_tok + 16 * m * Dp * 2;
+      const uint32_t ao = x.o_tok + 16 * m * 32 * 2;
       o.kh[m] = ldb<u16x8>(kh, ao);
       o.kl[m] = ldb<u16x8>(kl, ao);
       o.qh[m] = ldb<u16x8>(qh, ao);
       o.ql[m] = ldb<u16x8>(ql, ao);
     }
-    const float *gb = x.gl + static_cast<size_t>(chunk) * C * x.H_v;
-    const float *bb = x.beta + static_cast<size_t>(chunk) * C * x.H_v;
-    const int t0 = x.lane, t1 = 64 + x.lane;
-    o.g0 = (t0 < C && t0 < n_valid) ? ldb<float>(gb, x.o_g) : 0.f;
-    o.b0 = (t0 < C && t0 < n_valid) ? ldb<float>(bb, x.o_g) : 0.f;
-    o.g1 = (C > 64 && t1 < n_valid) ? ldb<float>(gb, x.o_g + 64 * 4 * x.H_v) : 0.f;
-    o.b1 = (C > 64 && t1 < n_valid) ? ldb<float>(bb, x.o_g + 64 * 4 * x.H_v) : 0.f;
+  }
+
+  // Gate factors are used in steps 2-5, so they are fetched after step 5.
+  static __device__ __forceinline__ void load_gates(const Ctx &x, int chunk, Ops &o) {
+    const float *gb = x.gates + static_cast<size_t>(chunk) * 3 * C;
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int m = own_tile(x, i);
+      o.gam[i] = ldb<float4>(gb, x.o_gate + m * 64);
+      o.dl[i] = ldb<float4>(gb, x.o_gate + m * 64 + C * 4);
+      o.bt[i] = ldb<float4>(gb, x.o_gate + m * 64 + 2 * C * 4);
+    }
+    o.glast = ldb<float>(gb, (C - 1) * 4);
   }
 
   static __device__ __forceinline__ void load_v(const Ctx &x, int chunk, Ops &o) {
     const float *base = x.vT + static_cast<size_t>(chunk) * C * D;
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
-      const int m = x.wave + i * NWV;
-      if (m < NT) {
+      const int m = own_tile(x, i);
 #pragma unroll
-        for (int n = 0; n < NB; ++n) o.v[i][n] = ldb<float4>(base, x.o_v + (m * 16 * D + n * 16 * 16) * 4);
-      }
+      for (int n = 0; n < NB; ++n) o.v[i][n] = ldb<float4>(base, x.o_v + (m * 16 * D + n * 16 * 16) * 4);
     }
   }
 
@@ -363,11 +391,11 @@ struct StateKernel {
     const uint16_t *base = x.Tm + static_cast<size_t>(chunk) * C * Cp;
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
-      const int m = x.wave + i * NWV;
-      if (m < NT) {
+      const int m = own_tile(x, i);
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks)
-          if (ks <= m / 2) o.tm[i][ks] = ldb<u16x8>(base, x.o_mat + (16 * m * Cp + 32 * ks) * 2);
+      for (int ks = 0; ks < KSC; ++ks) {
+        const int kk = ks <= m / 2 ? ks : m / 2;
+        o.tm[i][ks] = ldb<u16x8>(base, x.o_mat + (16 * m * Cp + 32 * kk) * 2);
       }
     }
   }
@@ -376,36 +404,29 @@ struct StateKernel {
     const size_t mo = static_cast<size_t>(chunk) * C * Cp;
     const uint16_t *ph = x.Ph + mo;
     const uint16_t *pl = x.Pl + mo;
-    const int n_valid = valid_of(x, chunk);
-    constexpr int ez = DTZ == 0 ? 4 : 2;
-    const char *zb = static_cast<const char *>(x.z) + static_cast<size_t>(chunk) * C * x.H_v * D * ez;
-    const uint32_t tstride = x.H_v * D * ez;
+    const int n_valid = valid_of(x, chunk);  // >= 1 for every chunk of the sequence
+    const char *zb = static_cast<const char *>(x.z) + static_cast<size_t>(chunk) * C * x.H_v * D * EZ;
+    const uint32_t tstride = x.H_v * D * EZ;
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
-      const int m = x.wave + i * NWV;
-      if (m < NT) {
+      const int m = own_tile(x, i);
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks)
-          if (ks <= m / 2) {
-            const uint32_t ao = x.o_mat + (16 * m * Cp + 32 * ks) * 2;
-            o.ph[i][ks] = ldb<u16x8>(ph, ao);
-            o.pl[i][ks] = ldb<u16x8>(pl, ao);
-          }
+      for (int ks = 0; ks < KSC; ++ks) {
+        const int kk = ks <= m / 2 ? ks : m / 2;
+        const uint32_t ao = x.o_mat + (16 * m * Cp + 32 * kk) * 2;
+        o.ph[i][ks] = ldb<u16x8>(ph, ao);
+        o.pl[i][ks] = ldb<u16x8>(pl, ao);
+      }
+      // z of this tile: 16 token rows of ROWS elements, one 16-byte piece per
+      // lane; rows past the sequence end re-read its last row (their outputs
+      // are not stored).
 #pragma unroll
-        for (int n = 0; n < NB; ++n)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * m + 4 * x.gq + r;
-            float v = 0.f;
-            if (t < n_valid) {
-              const uint32_t zo = (x.o_zy + 16 * n) * ez + (16 * m + r) * tstride;
-              if constexpr (DTZ == 0)
-                v = ldb<float>(zb, zo);
-              else
-                v = bf16_bits_to_f32(ldb<uint16_t>(zb, zo));
-            }
-            o.z[i][n][r] = v;
-          }
+      for (int k = 0; k < ZK; ++k) {
+        int idx = x.lane + 64 * k;
+        idx = idx < 16 * ZL ? idx : 16 * ZL - 1;
+        int t = 16 * m + idx / ZL;
+        t = t < n_valid ? t : n_valid - 1;
+        o.z[i][k] = ldb<uint4>(zb, t * tstride + (idx % ZL) * 16);
       }
     }
   }
@@ -426,12 +447,21 @@ struct StateKernel {
       }
   }
 
+  // First chunk's operands, issued in the order the loop issues them (the
+  // compiler barriers keep that order), so that the wait counts at the top of
+  // the loop are the same on entry as on every later iteration.
   static __device__ __forceinline__ void load_all(const Ctx &x, int chunk, Ops &o) {
     load_head(x, chunk, o);
+    asm volatile("" ::: "memory");
     load_v(x, chunk, o);
+    asm volatile("" ::: "memory");
     load_tm(x, chunk, o);
+    asm volatile("" ::: "memory");
     load_pz(x, chunk, o);
+    asm volatile("" ::: "memory");
     load_kT(x, chunk, o);
+    load_gates(x, chunk, o);
+    asm volatile("" ::: "memory");
   }
 
   // One chunk.  On entry `o` holds this chunk's operands (loads possibly in
@@ -441,32 +471,12 @@ struct StateKernel {
   // so that no later wait on those loads also waits for these stores.
   static __device__ __forceinline__ void chunk_step(const Ctx &x, int chunk, Ops &o,
                                                     f32x4 (&st)[NB][NDT], Smem &sm) {
-    const int lane = x.lane, wave = x.wave, gq = x.gq;
+    const int lane = x.lane, wave = x.wave, gq = x.gq, c = lane & 15;
     const int n_valid = valid_of(x, chunk);
-    const bool more = chunk + 1 < x.NC;
+    // The last chunk re-reads its own operands instead of branching.
+    const int next = chunk + 1 < x.NC ? chunk + 1 : chunk;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const Split4 none = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
-
-    // Gates, once per lane (lane t = token t), into this wave's table.
-    {
-      const float G0 = wave_incl_scan(o.g0);
-      float G1 = 0.f;
-      if constexpr (C > 64) G1 = wave_incl_scan(o.g1) + __shfl(G0, 63, kWave);
-      const float Glast = C > 64 ? __shfl(G1, (C - 1) & 63, kWave) : __shfl(G0, C - 1, kWave);
-      if (lane < C) {
-        sm.gate[wave][0][lane] = __expf(G0);
-        sm.gate[wave][1][lane] = __expf(Glast - G0);
-        sm.gate[wave][2][lane] = o.b0;
-      }
-      if constexpr (C > 64) {
-        sm.gate[wave][0][64 + lane] = __expf(G1);
-        sm.gate[wave][1][64 + lane] = __expf(Glast - G1);
-        sm.gate[wave][2][64 + lane] = o.b1;
-      }
-    }
-    const float *gt = sm.gate[wave][0];
-    const float *dl = sm.gate[wave][1];
-    const float *bt = sm.gate[wave][2];
 
     // 1. Partial K S^T and Q S^T over this wave's d_k slice, all token tiles.
 #pragma unroll
@@ -479,7 +489,7 @@ struct StateKernel {
         sm.part[wave][1][m][n][lane] = mfma_split3(o.qh[m], o.ql[m], bh, bl, zero);
       }
     }
-    if (more) load_head(x, chunk + 1, o);
+    load_head(x, next, o);
     __syncthreads();
 
     // 2. Owned tiles: R = beta (V - gamma K S^T), published split; Q S^T kept.
@@ -488,8 +498,7 @@ struct StateKernel {
     for (int i = 0; i < MW; ++i) {
       const int m = wave + i * NWV;
       if (m < NT) {
-        const float4 g4 = *reinterpret_cast<const float4 *>(gt + 16 * m + 4 * gq);
-        const float4 b4 = *reinterpret_cast<const float4 *>(bt + 16 * m + 4 * gq);
+        const float4 g4 = o.gam[i], b4 = o.bt[i];
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
           f32x4 ks = sm.part[0][0][m][n][lane];
@@ -506,7 +515,7 @@ struct StateKernel {
         }
       }
     }
-    if (more) load_v(x, chunk + 1, o);
+    load_v(x, next, o);
     __syncthreads();
 
     // 3. Owned tiles: U = Tm R, published split, also scaled by exp(G_last - G_t).
@@ -514,7 +523,7 @@ struct StateKernel {
     for (int i = 0; i < MW; ++i) {
       const int m = wave + i * NWV;
       if (m < NT) {
-        const float4 d4 = *reinterpret_cast<const float4 *>(dl + 16 * m + 4 * gq);
+        const float4 d4 = o.dl[i];
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
           f32x4 acc = zero;
@@ -532,16 +541,25 @@ struct StateKernel {
         }
       }
     }
-    if (more) load_tm(x, chunk + 1, o);
+    load_tm(x, next, o);
     __syncthreads();
 
-    // 4. Owned tiles: O = gamma Q S^T + P U, gated (stored at the end).
+    // 4. Owned tiles: O = gamma Q S^T + P U, gated (stored at the end).  z
+    //    arrives token-major; this wave's LDS slot turns it into D-register order.
     f32x4 out[MW][NB];
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
       const int m = wave + i * NWV;
       if (m < NT) {
-        const float4 g4 = *reinterpret_cast<const float4 *>(gt + 16 * m + 4 * gq);
+#pragma unroll
+        for (int k = 0; k < ZK; ++k)
+          if (lane + 64 * k < 16 * ZL) sm.z[wave][lane + 64 * k] = o.z[i][k];
+        // Other lanes of this wave read what was just written: keep the
+        // compiler from moving those reads above the stores (LDS operations of
+        // one wave execute in order).
+        asm volatile("" ::: "memory");
+        const char *zt = reinterpret_cast<const char *>(sm.z[wave]);
+        const float4 g4 = o.gam[i];
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
           f32x4 acc = {g4.x * qs[i][n][0], g4.y * qs[i][n][1], g4.z * qs[i][n][2], g4.w * qs[i][n][3]};
@@ -554,19 +572,27 @@ struct StateKernel {
               acc = mfma_split3(o.ph[i][ks], o.pl[i][ks], bh, bl, acc);
             }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) out[i][n][r] = acc[r] * sigmoidf_(o.z[i][n][r]);
+          for (int r = 0; r < 4; ++r) {
+            const int off = ((4 * gq + r) * ROWS + 16 * n + c) * EZ;
+            float zz;
+            if constexpr (DTZ == 0)
+              zz = *reinterpret_cast<const float *>(zt + off);
+            else
+              zz = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(zt + off));
+            out[i][n][r] = acc[r] * sigmoidf_(zz);
+          }
         }
+        asm volatile("" ::: "memory");
       }
     }
-    if (more) load_pz(x, chunk + 1, o);
+    load_pz(x, next, o);
 
     // 5. S^T <- gamma_last S^T + K^T (D_last * U) over this wave's d_k slice.
     {
-      const float gl_last = gt[C - 1];
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) st[n][dt] *= gl_last;
+        for (int dt = 0; dt < NDT; ++dt) st[n][dt] *= o.glast;
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
           Split4 a = sm.DU[2 * ks < NT ? 2 * ks : 0][n][lane];
@@ -584,7 +610,8 @@ struct StateKernel {
         }
       }
     }
-    if (more) load_kT(x, chunk + 1, o);
+    load_kT(x, next, o);
+    load_gates(x, next, o);
 
     // 6. Gated outputs of the owned tiles.
     constexpr int ey = DTY == 0 ? 4 : 2;
@@ -614,11 +641,10 @@ struct StateKernel {
 
 template <int D, int C, int DTZ, int DTY>
 __global__ __launch_bounds__((StateShape<D, C>::NWV * 64)) void state_kernel(
-    Geom g, PrefillWs L, const void *__restrict__ z, const float *__restrict__ gl,
-    const float *__restrict__ beta, float *__restrict__ S, void *__restrict__ y,
+    Geom g, PrefillWs L, const void *__restrict__ z, float *__restrict__ S, void *__restrict__ y,
     const char *__restrict__ ws) {
   using K = StateKernel<D, C, DTZ, DTY>;
-  constexpr int NDT = K::NDT, NB = K::NB, Dp = K::Dp, Cp = K::Cp, ROWS = StateShape<D, C>::ROWS;
+  constexpr int NDT = K::NDT, NB = K::NB, Dp = K::Dp, Cp = K::Cp, ROWS = K::ROWS;
   __shared__ typename K::Smem sm;
 
   const int RB = D / ROWS;
@@ -632,11 +658,13 @@ __global__ __launch_bounds__((StateShape<D, C>::NWV * 64)) void state_kernel(
   const int c = lane & 15, gq = lane >> 4;
 
   typename K::Ctx x;
+  // token-major slices: [b][kh][slice][T_pad][32]; this wave reads slice `wave`
+  const size_t slice0 = ((static_cast<size_t>(b) * g.H_k + kh) * (Dp / 32) + wave) * L.T_pad * 32;
+  x.khi = reinterpret_cast<const uint16_t *>(ws + L.k_hi) + slice0;
+  x.klo = reinterpret_cast<const uint16_t *>(ws + L.k_lo) + slice0;
+  x.qhi = reinterpret_cast<const uint16_t *>(ws + L.q_hi) + slice0;
+  x.qlo = reinterpret_cast<const uint16_t *>(ws + L.q_lo) + slice0;
   const size_t kbase = (static_cast<size_t>(b) * g.H_k + kh) * L.T_pad;
-  x.khi = reinterpret_cast<const uint16_t *>(ws + L.k_hi) + kbase * Dp;
-  x.klo = reinterpret_cast<const uint16_t *>(ws + L.k_lo) + kbase * Dp;
-  x.qhi = reinterpret_cast<const uint16_t *>(ws + L.q_hi) + kbase * Dp;
-  x.qlo = reinterpret_cast<const uint16_t *>(ws + L.q_lo) + kbase * Dp;
   x.kThi = reinterpret_cast<const uint16_t *>(ws + L.kT_hi) + kbase * D;
   x.kTlo = reinterpret_cast<const uint16_t *>(ws + L.kT_lo) + kbase * D;
   x.vT = reinterpret_cast<const float *>(ws + L.vT) +
@@ -645,10 +673,10 @@ __global__ __launch_bounds__((StateShape<D, C>::NWV * 64)) void state_kernel(
   x.Tm = reinterpret_cast<const uint16_t *>(ws + L.Tm) + mat;
   x.Ph = reinterpret_cast<const uint16_t *>(ws + L.P_hi) + mat;
   x.Pl = reinterpret_cast<const uint16_t *>(ws + L.P_lo) + mat;
-  x.gl = gl + static_cast<size_t>(b) * L.T * g.H_v + h;
-  x.beta = beta + static_cast<size_t>(b) * L.T * g.H_v + h;
+  x.gates = reinterpret_cast<const float *>(ws + L.gates) +
+            (static_cast<size_t>(b) * g.H_v + h) * L.NC * 3 * C;
   const size_t zy = (static_cast<size_t>(b) * L.T * g.H_v + h) * D + ROWS * rb;
-  x.z = static_cast<const char *>(z) + zy * (DTZ == 0 ? 4 : 2);
+  x.z = static_cast<const char *>(z) + zy * K::EZ;
   x.y = static_cast<char *>(y) + zy * (DTY == 0 ? 4 : 2);
   x.T = L.T;
   x.H_v = g.H_v;
@@ -656,12 +684,12 @@ __global__ __launch_bounds__((StateShape<D, C>::NWV * 64)) void state_kernel(
   x.wave = wave;
   x.lane = lane;
   x.gq = gq;
-  x.o_tok = (c * Dp + 32 * wave + 8 * gq) * 2;
+  x.o_tok = (c * 32 + 8 * gq) * 2;
   x.o_kT = ((32 * wave + c) * 32 + 8 * gq) * 2;
   x.o_v = ((ROWS * rb + c) * 16 + 4 * gq) * 4;
   x.o_mat = (c * Cp + 8 * gq) * 2;
   x.o_zy = 4 * gq * g.H_v * D + c;
-  x.o_g = lane * g.H_v * 4;
+  x.o_gate = 4 * gq * 4;
 
   // S^T tiles: for state-row tile n, rows d_k = 32*wave + 16*dt + 4*gq + r,
   // column = state row ROWS*rb + 16*n + c.
@@ -715,28 +743,27 @@ hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *g
 }
 
 template <int D, int C>
-static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, const float *gl,
-                           const float *beta, float *S, void *y, const char *ws, hipStream_t s) {
+static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, float *S, void *y,
+                           const char *ws, hipStream_t s) {
   dim3 grid(g.B * g.H_v * (D / StateShape<D, C>::ROWS));
   dim3 block(StateShape<D, C>::NWV * 64);
   const int key = (g.in_dt << 1) | g.out_dt;
   switch (key) {
-    case 0: hipLaunchKernelGGL((state_kernel<D, C, 0, 0>), grid, block, 0, s, g, L, z, gl, beta, S, y, ws); break;
-    case 1: hipLaunchKernelGGL((state_kernel<D, C, 0, 1>), grid, block, 0, s, g, L, z, gl, beta, S, y, ws); break;
-    case 2: hipLaunchKernelGGL((state_kernel<D, C, 1, 0>), grid, block, 0, s, g, L, z, gl, beta, S, y, ws); break;
-    default: hipLaunchKernelGGL((state_kernel<D, C, 1, 1>), grid, block, 0, s, g, L, z, gl, beta, S, y, ws); break;
+    case 0: hipLaunchKernelGGL((state_kernel<D, C, 0, 0>), grid, block, 0, s, g, L, z, S, y, ws); break;
+    case 1: hipLaunchKernelGGL((state_kernel<D, C, 0, 1>), grid, block, 0, s, g, L, z, S, y, ws); break;
+    case 2: hipLaunchKernelGGL((state_kernel<D, C, 1, 0>), grid, block, 0, s, g, L, z, S, y, ws); break;
+    default: hipLaunchKernelGGL((state_kernel<D, C, 1, 1>), grid, block, 0, s, g, L, z, S, y, ws); break;
   }
 }
 
-hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z,
-                                const float *gl, const float *beta, float *S, void *y,
-                                const char *ws, hipStream_t s) {
-#define GDN_STATE(Dv)                                                         \
-  switch (L.C) {                                                              \
-    case 16: launch_state_t<Dv, 16>(g, L, z, gl, beta, S, y, ws, s); break;   \
-    case 32: launch_state_t<Dv, 32>(g, L, z, gl, beta, S, y, ws, s); break;   \
-    case 64: launch_state_t<Dv, 64>(g, L, z, gl, beta, S, y, ws, s); break;   \
-    default: launch_state_t<Dv, 128>(g, L, z, gl, beta, S, y, ws, s); break;  \
+hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z, float *S,
+                                void *y, const char *ws, hipStream_t s) {
+#define GDN_STATE(Dv)                                                 \
+  switch (L.C) {                                                      \
+    case 16: launch_state_t<Dv, 16>(g, L, z, S, y, ws, s); break;     \
+    case 32: launch_state_t<Dv, 32>(g, L, z, S, y, ws, s); break;     \
+    case 64: launch_state_t<Dv, 64>(g, L, z, S, y, ws, s); break;     \
+    default: launch_state_t<Dv, 128>(g, L, z, S, y, ws, s); break;    \
   }
   if (g.D == 128) {
     GDN_STATE(128)
