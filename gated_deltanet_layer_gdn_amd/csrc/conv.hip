@@ -57,6 +57,72 @@ __device__ __forceinline__ void head_sums(float (&ss)[TT], float (*red)[kConvTT]
   }
 }
 
+// DPP lane exchange within a row of 16 lanes (gfx9 control codes):
+// row_mirror (0x140) pairs lanes l and 15 - l, row_half_mirror (0x141) pairs
+// l and 7 - l in each group of 8, quad_perm (2,3,0,1) (0x4E) pairs l and l ^ 2,
+// quad_perm (1,0,3,2) (0xB1) pairs l and l ^ 1.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// One exchange of the transpose-reduce: N per-token values become N / 2.  The
+// lane whose BIT is set keeps the upper half of the tokens, its partner (which
+// has BIT clear and the same bits above) the lower half; each adds what the
+// other sends for the half it keeps.
+template <int N, int CTRL, int BIT>
+__device__ __forceinline__ void tr_step(float *v, int lane) {
+  const bool up = (lane & BIT) != 0;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = up ? v[i + N / 2] : v[i];
+    const float send = up ? v[i] : v[i + N / 2];
+    v[i] = keep + dpp_f<CTRL>(send);
+  }
+}
+
+// Per-token factor sc / sqrt(sum of squares + eps) of one 128-channel head
+// held by the block's two waves, for 32 tokens.  On entry ss[t] is this
+// lane's square for token t, on exit the factor for token t.  The 32 sums over
+// 64 lanes are a transpose-reduce: every exchange hands half of the remaining
+// tokens to a partner lane and keeps the other half, so the lane-swap
+// instructions of gfx950 (distance 32, then 16) and DPP (the rest) need
+// 16 + 8 + 4 + 2 + 1 + 1 exchanges, after which lane l holds token l / 2.  The
+// two waves' partial sums meet in LDS, one reciprocal square root per lane
+// follows, and a wave-local LDS broadcast hands every lane all 32 factors.
+__device__ __forceinline__ void head_scale_128x32(float (&ss)[32], float eps, float sc,
+                                                  float (*red)[kConvTT],
+                                                  float (*bc)[kConvTT]) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss[i]),
+                                                    __float_as_uint(ss[i + 16]), false, false);
+    ss[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss[i]),
+                                                    __float_as_uint(ss[i + 8]), false, false);
+    ss[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  tr_step<8, 0x140, 8>(ss, lane);
+  tr_step<4, 0x141, 4>(ss, lane);
+  tr_step<2, 0x4E, 2>(ss, lane);
+  const float s = ss[0] + dpp_f<0xB1>(ss[0]);
+  const int t = lane >> 1;
+  if ((lane & 1) == 0) red[w][t] = s;
+  __syncthreads();
+  const float f = __builtin_amdgcn_rsqf(red[0][t] + red[1][t] + eps) * sc;
+  if ((lane & 1) == 0) bc[w][t] = f;
+  // Only this wave reads bc[w], after its own writes (LDS keeps a wave's
+  // accesses in order).
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < kConvTT; ++i) ss[i] = bc[w][i];
+}
+
 // One thread per channel and kConvTT tokens: the tile's inputs (plus the three
 // previous rows) are loaded up front, so every x element is read once and all
 // loads are in flight together; the per-channel outputs stay in registers,
@@ -64,34 +130,56 @@ __device__ __forceinline__ void head_sums(float (&ss)[TT], float (*red)[kConvTT]
 template <int DT, int D, int MODE, int TT>
 __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) {
   __shared__ float red[2][kConvTT];
+  __shared__ float bc[2][kConvTT];
   const int ch = blockIdx.y * kConvThreads + threadIdx.x;
   const int b = blockIdx.z;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TT;
   const bool active = ch < g.C_ch;
+  // Lanes past the last channel load a valid channel and drop their results,
+  // so every load below is unconditional per lane.
+  const int chc = active ? ch : g.C_ch - 1;
   const int nq = g.H_k * D;
   const int nqk = 2 * nq;
-  const bool is_q = ch < nq;
-  const bool is_k = !is_q && ch < nqk;
-  // For D = 128 a block is exactly one head, so this is uniform per block.
-  const bool qk_block = (D == 128) ? (blockIdx.y * kConvThreads < nqk) : true;
+  // For D = 128 a block is exactly one head: the kind is uniform per block.
+  const int head0 = (D == 128) ? static_cast<int>(blockIdx.y) * kConvThreads : ch;
+  const bool is_q = head0 < nq;
+  const bool is_k = !is_q && head0 < nqk;
+  const bool qk_block = (D == 128) ? (is_q || is_k) : true;
+  constexpr int ES = DT == 0 ? 4 : 2;
+  const size_t rowb = static_cast<size_t>(g.C_ch) * ES;
+  const uint32_t lane_off = static_cast<uint32_t>(chc) * ES;
 
-  float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+  auto ld = [&](const void *row_base) -> float {
+    if constexpr (DT == 0)
+      return *reinterpret_cast<const float *>(static_cast<const char *>(row_base) + lane_off);
+    else
+      return bf16_bits_to_f32(
+          *reinterpret_cast<const uint16_t *>(static_cast<const char *>(row_base) + lane_off));
+  };
+  const char *wrow = static_cast<const char *>(a.w);
+  const float w0 = load_elem<DT>(wrow, static_cast<size_t>(chc) * 4 + 0);
+  const float w1 = load_elem<DT>(wrow, static_cast<size_t>(chc) * 4 + 1);
+  const float w2 = load_elem<DT>(wrow, static_cast<size_t>(chc) * 4 + 2);
+  const float w3 = load_elem<DT>(wrow, static_cast<size_t>(chc) * 4 + 3);
   float xv[TT + 3];
-  if (active) {
-    w0 = load_elem<DT>(a.w, static_cast<size_t>(ch) * 4 + 0);
-    w1 = load_elem<DT>(a.w, static_cast<size_t>(ch) * 4 + 1);
-    w2 = load_elem<DT>(a.w, static_cast<size_t>(ch) * 4 + 2);
-    w3 = load_elem<DT>(a.w, static_cast<size_t>(ch) * 4 + 3);
-  }
+  const char *xb = static_cast<const char *>(a.x) + static_cast<size_t>(b) * a.T * rowb;
+  if (t0 >= 3 && t0 + TT <= a.T) {
+    // Interior tile: rows t0 - 3 .. t0 + TT - 1 all come from x.
+    const char *r0 = xb + static_cast<size_t>(t0 - 3) * rowb;
 #pragma unroll
-  for (int i = 0; i < TT + 3; ++i) {
-    const int64_t tau = t0 - 3 + i;
-    float v = 0.f;
-    if (active && tau < a.T) {
-      v = tau >= 0 ? load_elem<DT>(a.x, (static_cast<size_t>(b) * a.T + tau) * g.C_ch + ch)
-                   : load_elem<DT>(a.hist, (static_cast<size_t>(b) * 3 + 3 + tau) * g.C_ch + ch);
+    for (int i = 0; i < TT + 3; ++i) xv[i] = ld(r0 + i * rowb);
+  } else {
+    const char *hb = static_cast<const char *>(a.hist) + static_cast<size_t>(b) * 3 * rowb;
+#pragma unroll
+    for (int i = 0; i < TT + 3; ++i) {
+      const int64_t tau = t0 - 3 + i;  // uniform per block
+      float v = 0.f;
+      if (tau < 0)
+        v = ld(hb + static_cast<size_t>(3 + tau) * rowb);
+      else if (tau < a.T)
+        v = ld(xb + static_cast<size_t>(tau) * rowb);
+      xv[i] = v;
     }
-    xv[i] = v;
   }
   float val[TT], ss[TT];
 #pragma unroll
@@ -100,16 +188,24 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
     ss[t] = val[t] * val[t];
   }
   if (qk_block) {
-    head_sums<D, TT>(ss, red);
-    if (is_q || is_k) {
-      const float sc = is_q ? g.q_scale : 1.0f;
+    if constexpr (D == 128 && TT == kConvTT) {
+      head_scale_128x32(ss, g.eps, is_q ? g.q_scale : 1.0f, red, bc);
 #pragma unroll
-      for (int t = 0; t < TT; ++t) val[t] = val[t] * (1.0f / __builtin_sqrtf(ss[t] + g.eps)) * sc;
+      for (int t = 0; t < TT; ++t) val[t] *= ss[t];
+    } else {
+      head_sums<D, TT>(ss, red);
+      if (is_q || is_k) {
+        const float sc = is_q ? g.q_scale : 1.0f;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) val[t] *= __builtin_amdgcn_rsqf(ss[t] + g.eps) * sc;
+      }
     }
   }
+  if (t0 + TT > a.T) {
 #pragma unroll
-  for (int t = 0; t < TT; ++t)
-    if (t0 + t >= a.T) val[t] = 0.f;  // padding tokens of the prefill layout
+    for (int t = 0; t < TT; ++t)
+      if (t0 + t >= a.T) val[t] = 0.f;  // padding tokens of the prefill layout
+  }
   if (!active) return;
 
   if constexpr (MODE == kOutPlain) {

@@ -75,9 +75,17 @@ __device__ __forceinline__ void store_elem(void *p, size_t i, float v) {
     static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(v);
 }
 
+// e^{-x} as the hardware base-2 exponential of -x log2(e): one v_exp_f32
+// without the library's denormal range handling.  A result that underflows
+// becomes 0 and one that overflows +inf, and both ends give the right limit
+// below (1 / (1 + inf) = 0, 1 / (1 + 0) = 1).
+__device__ __forceinline__ float exp_neg(float x) {
+  return __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+}
+
 // Hardware reciprocal (1 ulp) instead of an IEEE division sequence.
-__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
-__device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + exp_neg(z)); }
+__device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + exp_neg(x)); }
 
 // Causal width-4 conv of one channel: taps w0..w3 meet x[t-3]..x[t].  The
 // accumulation order is fixed so that every kernel gets the same bits.
