@@ -31,6 +31,8 @@
 // Precision: every product that carries the value path uses split bf16
 // operands (hi + lo, 16 significant bits) with fp32 accumulation; only Tm
 // (unit diagonal, small off-diagonal) is rounded to plain bf16.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -715,6 +717,473 @@ __global__ __launch_bounds__((StateShape<D, C>::NWV * 64)) void state_kernel(
           make_float4(st[n][dt][0], st[n][dt][1], st[n][dt][2], st[n][dt][3]);
 }
 
+// ---------------------------------------------------------------- state pass, split roles
+//
+// The state recurrence of a chunk is a chain (K S^T -> R -> U -> S update),
+// while the outputs (Q S^T, P U, the gate and the stores) hang off it.  With
+// d = 128 and 64-token chunks the block therefore runs eight waves, two per
+// SIMD: chain waves 0-3 own token tile w for K S^T, R and U and d_k slice w
+// of the state, output waves 4-7 own token tile w - 4 for Q S^T, P U and y.
+// Both kinds of wave go through the same three barriers per chunk, so a
+// SIMD always has the other wave's independent products to issue while one
+// waits on a barrier, an LDS round trip or a dependent MFMA.  The state is
+// shared as ready-made split B operands (one 32-wide d_k step per chain
+// wave), so each wave forms its full-depth products itself and no partial
+// sums cross waves.
+//   phase 1: chain  KS = K_t S^T (full d_k), R = beta (V - gamma KS) -> LDS
+//            output QS = Q_t S^T (kept in registers)
+//   phase 2: chain  U = Tm R, DU = exp(G_last - G) U -> LDS
+//            output z tile -> sigmoid, through the wave's LDS slot
+//   phase 3: chain  S^T <- gamma_last S^T + K^T DU, new state operands -> LDS
+//            output O = gamma QS + P U, y = O sigmoid(z) -> HBM
+template <int DTZ, int DTY>
+struct StateKernelWS {
+  static constexpr int D = 128, C = 64, NT = 4, NB = 2, ROWS = 32, NDT = 2, KSC = 2, Cp = 64;
+  static constexpr int NS = D / 32;              // 32-wide d_k steps
+  static constexpr int EZ = DTZ == 0 ? 4 : 2;    // bytes per z element
+  static constexpr int ZL = ROWS * EZ / 16;      // 16-byte pieces per token row of z
+  static constexpr int ZK = (16 * ZL + 63) / 64; // pieces per lane per tile
+  static constexpr int kThreads = 512;
+
+  struct Smem {
+    u16x8 Sh[NS][NB][64], Sl[NS][NB][64];  // state as split B operands, one d_k step each
+    Split4 R[NT][NB][64];
+    Split4 U[NT][NB][64];
+    Split4 DU[NT][NB][64];
+    uint4 z[NT][16 * ZL];                  // per output wave: one token tile of z
+  };
+
+  struct Gates {
+    float4 gam, bt, dl;  // gate factors of the owned tile (D-register order)
+    float glast;         // gamma of the chunk's last token
+  };
+
+  struct ChainOps {
+    u16x8 kh[NS], kl[NS];              // K of the owned tile, A operand per d_k step
+    float4 v[NB];                      // V of the owned tile (D-register order)
+    Gates g;
+    u16x8 tm[KSC];                     // (I+A)^{-1} rows of the owned tile
+    u16x8 th[NDT][KSC], tl[NDT][KSC];  // K^T of the owned d_k slice
+  };
+
+  struct OutOps {
+    u16x8 qh[NS], ql[NS];  // Q of the owned tile
+    float4 gam;
+    u16x8 ph[KSC], pl[KSC];
+    uint4 z[ZK];
+  };
+
+  struct Ctx {
+    const char *ktok_hi, *ktok_lo, *qtok_hi, *qtok_lo;  // slice 0 of this key head
+    size_t slice_bytes;                                  // T_pad * 32 * 2
+    const uint16_t *kThi, *kTlo;
+    const float *vT;
+    const uint16_t *Tm, *Ph, *Pl;
+    const float *gates;
+    const void *z;
+    void *y;
+    int64_t T;
+    int H_v, NC, m, lane, gq;
+    uint32_t o_tok, o_kT, o_v, o_mat, o_zy, o_gate;
+  };
+
+  static __device__ __forceinline__ int valid_of(const Ctx &x, int chunk) {
+    const int64_t r = x.T - static_cast<int64_t>(chunk) * C;
+    return static_cast<int>(r < C ? r : C);
+  }
+
+  static __device__ __forceinline__ Split4 split4(const f32x4 &v) {
+    uint32_t h0, h1, l0, l1;
+    split2(v[0], v[1], h0, l0);
+    split2(v[2], v[3], h1, l1);
+    return Split4{make_uint2(h0, h1), make_uint2(l0, l1)};
+  }
+
+  static __device__ __forceinline__ void operand(const Split4 &a, const Split4 &b, u16x8 &hi,
+                                                 u16x8 &lo) {
+    const u32x4 h = {a.hi.x, a.hi.y, b.hi.x, b.hi.y}, l = {a.lo.x, a.lo.y, b.lo.x, b.lo.y};
+    hi = __builtin_bit_cast(u16x8, h);
+    lo = __builtin_bit_cast(u16x8, l);
+  }
+
+  // Token-major rows of the owned tile, every d_k step (slice-major layout).
+  static __device__ __forceinline__ void load_tok(const char *hi, const char *lo, const Ctx &x,
+                                                  int chunk, u16x8 (&h)[NS], u16x8 (&l)[NS]) {
+    const size_t row = static_cast<size_t>(chunk) * C * 32 * 2;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      h[s] = ldb<u16x8>(hi + row + s * x.slice_bytes, x.o_tok);
+      l[s] = ldb<u16x8>(lo + row + s * x.slice_bytes, x.o_tok);
+    }
+  }
+
+  static __device__ __forceinline__ void load_v(const Ctx &x, int chunk, ChainOps &o) {
+    const float *base = x.vT + static_cast<size_t>(chunk) * C * D;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) o.v[n] = ldb<float4>(base, x.o_v + n * 16 * 16 * 4);
+  }
+
+  // The four factors of lane group gq from the 16 of the owned token tile.
+  // The address is wave-uniform, so these are scalar loads (sixteen lanes
+  // share every value; the vector memory path is left to the operands).
+  // readfirstlane keeps each value a single wave-wide one, so the compiler
+  // selects among registers instead of turning the selects back into a
+  // per-lane load.
+  static __device__ __forceinline__ float uni(const float *p) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*p)));
+  }
+
+  static __device__ __forceinline__ float4 tile_gate(const float *p, int gq) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = uni(p + i);
+    const bool b1 = gq & 1, b2 = gq & 2;
+    float4 r;
+    r.x = b2 ? (b1 ? v[12] : v[8]) : (b1 ? v[4] : v[0]);
+    r.y = b2 ? (b1 ? v[13] : v[9]) : (b1 ? v[5] : v[1]);
+    r.z = b2 ? (b1 ? v[14] : v[10]) : (b1 ? v[6] : v[2]);
+    r.w = b2 ? (b1 ? v[15] : v[11]) : (b1 ? v[7] : v[3]);
+    return r;
+  }
+
+  static __device__ __forceinline__ Gates load_gates(const Ctx &x, int chunk) {
+    const float *gb = x.gates + static_cast<size_t>(chunk) * 3 * C;
+    Gates o;
+    o.gam = tile_gate(gb + 16 * x.m, x.gq);
+    o.dl = tile_gate(gb + C + 16 * x.m, x.gq);
+    o.bt = tile_gate(gb + 2 * C + 16 * x.m, x.gq);
+    o.glast = uni(gb + C - 1);
+    return o;
+  }
+
+  // Rows of a chunk matrix (Tm or P) for the owned tile; K steps past the
+  // diagonal re-read the last needed one (they are not used).
+  static __device__ __forceinline__ void load_rows(const uint16_t *mat, const Ctx &x, int chunk,
+                                                   u16x8 (&r)[KSC]) {
+    const uint16_t *base = mat + static_cast<size_t>(chunk) * C * Cp;
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks) {
+      const int kk = ks <= x.m / 2 ? ks : x.m / 2;
+      r[ks] = ldb<u16x8>(base, x.o_mat + 32 * kk * 2);
+    }
+  }
+
+  static __device__ __forceinline__ void load_kT(const Ctx &x, int chunk, ChainOps &o) {
+    const size_t base = static_cast<size_t>(chunk) * C * D;
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t ao = x.o_kT + (ks * D + 16 * dt) * 32 * 2;
+        o.th[dt][ks] = ldb<u16x8>(x.kThi + base, ao);
+        o.tl[dt][ks] = ldb<u16x8>(x.kTlo + base, ao);
+      }
+  }
+
+  static __device__ __forceinline__ void load_z(const Ctx &x, int chunk, OutOps &o) {
+    const int n_valid = valid_of(x, chunk);
+    const char *zb = static_cast<const char *>(x.z) + static_cast<size_t>(chunk) * C * x.H_v * D * EZ;
+    const uint32_t tstride = x.H_v * D * EZ;
+#pragma unroll
+    for (int k = 0; k < ZK; ++k) {
+      int idx = x.lane + 64 * k;
+      idx = idx < 16 * ZL ? idx : 16 * ZL - 1;
+      int t = 16 * x.m + idx / ZL;
+      t = t < n_valid ? t : n_valid - 1;  // rows past the end re-read the last one
+      o.z[k] = ldb<uint4>(zb, t * tstride + (idx % ZL) * 16);
+    }
+  }
+
+  static __device__ __forceinline__ void load_gam(const Ctx &x, int chunk, OutOps &o) {
+    o.gam = tile_gate(x.gates + static_cast<size_t>(chunk) * 3 * C + 16 * x.m, x.gq);
+  }
+
+
+  static __device__ void chain(const Ctx &x, Smem &sm, float *Sh, int w) {
+    const int lane = x.lane, m = x.m;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const Split4 none = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+    // State slice d_k = 32w..32w+31 of the block's rows, as S^T tiles.
+    f32x4 st[NB][NDT];
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const float4 v = *reinterpret_cast<const float4 *>(Sh + 16 * n * D + 32 * w + 16 * dt + 4 * x.gq);
+        st[n][dt] = f32x4{v.x, v.y, v.z, v.w};
+      }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) pack_split(st[n][0], st[n][1], sm.Sh[w][n][lane], sm.Sl[w][n][lane]);
+    ChainOps o;
+    o.g = load_gates(x, 0);
+    asm volatile("" ::: "memory");
+    load_tok(x.ktok_hi, x.ktok_lo, x, 0, o.kh, o.kl);
+    asm volatile("" ::: "memory");
+    load_v(x, 0, o);
+    asm volatile("" ::: "memory");
+    load_rows(x.Tm, x, 0, o.tm);
+    asm volatile("" ::: "memory");
+    load_kT(x, 0, o);
+    asm volatile("" ::: "memory");
+    __syncthreads();
+
+    for (int chunk = 0; chunk < x.NC; ++chunk) {
+      const int next = chunk + 1 < x.NC ? chunk + 1 : chunk;
+      // The next chunk's gate factors are needed first (phase 1) and fetched
+      // first, a whole chunk ahead, into registers of their own.
+      const Gates gn = load_gates(x, next);
+      asm volatile("" ::: "memory");
+      // 1. KS over the full depth, then R of the owned tile.
+      u16x8 bh[NS][NB], bl[NS][NB];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          bh[s][n] = sm.Sh[s][n][lane];
+          bl[s][n] = sm.Sl[s][n][lane];
+        }
+      f32x4 ks[NB] = {zero, zero};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) ks[n] = mfma_split3(o.kh[s], o.kl[s], bh[s][n], bl[s][n], ks[n]);
+      load_tok(x.ktok_hi, x.ktok_lo, x, next, o.kh, o.kl);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const float4 vv = o.v[n];
+        const float4 bt = o.g.bt, ga = o.g.gam;
+        const f32x4 r = {bt.x * (vv.x - ga.x * ks[n][0]), bt.y * (vv.y - ga.y * ks[n][1]),
+                         bt.z * (vv.z - ga.z * ks[n][2]), bt.w * (vv.w - ga.w * ks[n][3])};
+        sm.R[m][n][lane] = split4(r);
+      }
+      load_v(x, next, o);
+      __syncthreads();
+
+      // 2. U = Tm R for the owned tile, and its decayed copy for the update.
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        f32x4 acc = zero;
+#pragma unroll
+        for (int kk = 0; kk < KSC; ++kk)
+          if (kk <= m / 2) {
+            u16x8 bh, bl;
+            operand(sm.R[2 * kk][n][lane], sm.R[2 * kk + 1][n][lane], bh, bl);
+            acc = mfma_split2(o.tm[kk], bh, bl, acc);
+          }
+        sm.U[m][n][lane] = split4(acc);
+        const float4 dl = o.g.dl;
+        const f32x4 du = {dl.x * acc[0], dl.y * acc[1], dl.z * acc[2], dl.w * acc[3]};
+        sm.DU[m][n][lane] = split4(du);
+      }
+      load_rows(x.Tm, x, next, o.tm);
+      __syncthreads();
+
+      // 3. S^T <- gamma_last S^T + K^T DU over the owned d_k slice.
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) st[n][dt] *= o.g.glast;
+#pragma unroll
+        for (int kk = 0; kk < KSC; ++kk) {
+          u16x8 bh, bl;
+          operand(sm.DU[2 * kk][n][lane], sm.DU[2 * kk + 1][n][lane], bh, bl);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            st[n][dt] = mfma_split3(o.th[dt][kk], o.tl[dt][kk], bh, bl, st[n][dt]);
+        }
+      }
+      load_kT(x, next, o);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) pack_split(st[n][0], st[n][1], sm.Sh[w][n][lane], sm.Sl[w][n][lane]);
+      o.g = gn;
+      __syncthreads();
+    }
+    (void)none;
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<float4 *>(Sh + 16 * n * D + 32 * w + 16 * dt + 4 * x.gq) =
+            make_float4(st[n][dt][0], st[n][dt][1], st[n][dt][2], st[n][dt][3]);
+  }
+
+  static __device__ void output(const Ctx &x, Smem &sm) {
+    const int lane = x.lane, m = x.m, gq = x.gq, c = lane & 15;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    OutOps o;
+    load_tok(x.qtok_hi, x.qtok_lo, x, 0, o.qh, o.ql);
+    asm volatile("" ::: "memory");
+    load_z(x, 0, o);
+    asm volatile("" ::: "memory");
+    load_rows(x.Ph, x, 0, o.ph);
+    load_rows(x.Pl, x, 0, o.pl);
+    load_gam(x, 0, o);
+    asm volatile("" ::: "memory");
+    __syncthreads();
+    constexpr int ey = DTY == 0 ? 4 : 2;
+    const uint32_t ystride = x.H_v * D * ey;
+
+    // One chunk; `last` (a compile-time flag) marks the final chunk, the only
+    // one whose tokens may end early.  Every other chunk stores all of its
+    // outputs unconditionally and after its loads, which keeps the stores out
+    // of branches: the wait counts then see them, and a wait for a load never
+    // waits for a store issued after it.
+    auto step = [&](int chunk, auto last) {
+      constexpr bool kLast = decltype(last)::value;
+      const int next = kLast ? chunk : chunk + 1;
+      // 1. QS over the full depth.
+      u16x8 bh[NS][NB], bl[NS][NB];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          bh[s][n] = sm.Sh[s][n][lane];
+          bl[s][n] = sm.Sl[s][n][lane];
+        }
+      f32x4 qs[NB] = {zero, zero};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) qs[n] = mfma_split3(o.qh[s], o.ql[s], bh[s][n], bl[s][n], qs[n]);
+      if (!kLast) load_tok(x.qtok_hi, x.qtok_lo, x, next, o.qh, o.ql);
+      __syncthreads();
+
+      // 2. Gate of the owned tile: z arrives token-major; the wave's LDS slot
+      //    turns it into D-register order.  Only this wave touches the slot,
+      //    and LDS keeps one wave's accesses in order.
+      float sg[NB][4];
+      {
+#pragma unroll
+        for (int k = 0; k < ZK; ++k)
+          if (lane + 64 * k < 16 * ZL) sm.z[m][lane + 64 * k] = o.z[k];
+        asm volatile("" ::: "memory");
+        const char *zt = reinterpret_cast<const char *>(sm.z[m]);
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int off = ((4 * gq + r) * ROWS + 16 * n + c) * EZ;
+            float zz;
+            if constexpr (DTZ == 0)
+              zz = *reinterpret_cast<const float *>(zt + off);
+            else
+              zz = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(zt + off));
+            sg[n][r] = sigmoidf_(zz);
+          }
+        asm volatile("" ::: "memory");
+      }
+      if (!kLast) load_z(x, next, o);
+      __syncthreads();
+
+      // 3. O = gamma QS + P U, gated, stored.
+      char *yb = static_cast<char *>(x.y) + static_cast<size_t>(chunk) * C * x.H_v * D * ey;
+      f32x4 out[NB];
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        f32x4 acc = {o.gam.x * qs[n][0], o.gam.y * qs[n][1], o.gam.z * qs[n][2], o.gam.w * qs[n][3]};
+#pragma unroll
+        for (int kk = 0; kk < KSC; ++kk)
+          if (kk <= m / 2) {
+            u16x8 uh, ul;
+            operand(sm.U[2 * kk][n][lane], sm.U[2 * kk + 1][n][lane], uh, ul);
+            acc = mfma_split3(o.ph[kk], o.pl[kk], uh, ul, acc);
+          }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[n][r] = acc[r] * sg[n][r];
+      }
+      if (!kLast) {
+        load_rows(x.Ph, x, next, o.ph);
+        load_rows(x.Pl, x, next, o.pl);
+        load_gam(x, next, o);
+      }
+      const int n_valid = valid_of(x, chunk);
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * m + 4 * gq + r;
+          if (!kLast || t < n_valid) {
+            char *dst = yb + (x.o_zy + 16 * n) * ey + (16 * m + r) * ystride;
+            if constexpr (DTY == 0)
+              *reinterpret_cast<float *>(dst) = out[n][r];
+            else
+              *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16_bits(out[n][r]);
+          }
+        }
+      __syncthreads();
+    };
+    // The first chunk runs ahead of the loop so that the loop is entered with
+    // the same memory operations in flight as on its back edge (loads of
+    // the next chunk, then this chunk's stores): the wait counts inside the
+    // loop are then exact instead of also covering the previous stores.
+    if (x.NC > 1) {
+      step(0, std::false_type{});
+      for (int chunk = 1; chunk + 1 < x.NC; ++chunk) step(chunk, std::false_type{});
+    }
+    step(x.NC - 1, std::true_type{});
+  }
+};
+
+template <int DTZ, int DTY>
+__global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
+                                                       const void *__restrict__ z,
+                                                       float *__restrict__ S,
+                                                       void *__restrict__ y,
+                                                       const char *__restrict__ ws) {
+  using K = StateKernelWS<DTZ, DTY>;
+  constexpr int D = K::D, C = K::C, Cp = K::Cp, ROWS = K::ROWS;
+  __shared__ typename K::Smem sm;
+
+  const int RB = D / ROWS;
+  const int lid = xcd_remap(blockIdx.x, g.B * g.H_v * RB);
+  const int rb = lid % RB;
+  const int h = (lid / RB) % g.H_v;
+  const int b = lid / (RB * g.H_v);
+  const int kh = h / g.G;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool is_chain = wave < 4;
+  const int c = lane & 15, gq = lane >> 4;
+
+  typename K::Ctx x;
+  const size_t slice0 = (static_cast<size_t>(b) * g.H_k + kh) * (D / 32) * L.T_pad * 32 * 2;
+  x.ktok_hi = ws + L.k_hi + slice0;
+  x.ktok_lo = ws + L.k_lo + slice0;
+  x.qtok_hi = ws + L.q_hi + slice0;
+  x.qtok_lo = ws + L.q_lo + slice0;
+  x.slice_bytes = static_cast<size_t>(L.T_pad) * 32 * 2;
+  const size_t kbase = (static_cast<size_t>(b) * g.H_k + kh) * L.T_pad;
+  x.kThi = reinterpret_cast<const uint16_t *>(ws + L.kT_hi) + kbase * D;
+  x.kTlo = reinterpret_cast<const uint16_t *>(ws + L.kT_lo) + kbase * D;
+  x.vT = reinterpret_cast<const float *>(ws + L.vT) + (static_cast<size_t>(b) * g.H_v + h) * L.T_pad * D;
+  const size_t mat = (static_cast<size_t>(b) * g.H_v + h) * L.NC * C * Cp;
+  x.Tm = reinterpret_cast<const uint16_t *>(ws + L.Tm) + mat;
+  x.Ph = reinterpret_cast<const uint16_t *>(ws + L.P_hi) + mat;
+  x.Pl = reinterpret_cast<const uint16_t *>(ws + L.P_lo) + mat;
+  x.gates = reinterpret_cast<const float *>(ws + L.gates) + (static_cast<size_t>(b) * g.H_v + h) * L.NC * 3 * C;
+  const size_t zy = (static_cast<size_t>(b) * L.T * g.H_v + h) * D + ROWS * rb;
+  x.z = static_cast<const char *>(z) + zy * K::EZ;
+  x.y = static_cast<char *>(y) + zy * (DTY == 0 ? 4 : 2);
+  x.T = L.T;
+  x.H_v = g.H_v;
+  x.NC = L.NC;
+  x.m = is_chain ? wave : wave - 4;
+  x.lane = lane;
+  x.gq = gq;
+  x.o_tok = ((16 * x.m + c) * 32 + 8 * gq) * 2;
+  x.o_kT = ((32 * wave + c) * 32 + 8 * gq) * 2;
+  x.o_v = ((ROWS * rb + c) * 16 + 4 * gq) * 4 + x.m * 16 * D * 4;
+  x.o_mat = ((16 * x.m + c) * Cp + 8 * gq) * 2;
+  x.o_zy = 4 * gq * g.H_v * D + c;
+  x.o_gate = (16 * x.m + 4 * gq) * 4;
+
+  float *Sh = S + ((static_cast<size_t>(b) * g.H_v + h) * D + ROWS * rb + c) * D;
+  if (is_chain)
+    K::chain(x, sm, Sh, wave);
+  else
+    K::output(x, sm);
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <int D, int C>
@@ -745,6 +1214,18 @@ hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *g
 template <int D, int C>
 static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, float *S, void *y,
                            const char *ws, hipStream_t s) {
+  if constexpr (D == 128 && C == 64) {
+    dim3 grid(g.B * g.H_v * (D / StateKernelWS<0, 0>::ROWS));
+    dim3 block(StateKernelWS<0, 0>::kThreads);
+    const int key = (g.in_dt << 1) | g.out_dt;
+    switch (key) {
+      case 0: hipLaunchKernelGGL((state_kernel_ws<0, 0>), grid, block, 0, s, g, L, z, S, y, ws); break;
+      case 1: hipLaunchKernelGGL((state_kernel_ws<0, 1>), grid, block, 0, s, g, L, z, S, y, ws); break;
+      case 2: hipLaunchKernelGGL((state_kernel_ws<1, 0>), grid, block, 0, s, g, L, z, S, y, ws); break;
+      default: hipLaunchKernelGGL((state_kernel_ws<1, 1>), grid, block, 0, s, g, L, z, S, y, ws); break;
+    }
+    return;
+  }
   dim3 grid(g.B * g.H_v * (D / StateShape<D, C>::ROWS));
   dim3 block(StateShape<D, C>::NWV * 64);
   const int key = (g.in_dt << 1) | g.out_dt;
