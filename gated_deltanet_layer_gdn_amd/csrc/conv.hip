@@ -228,6 +228,8 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
     }
   } else if constexpr (TT == kConvTT) {
     const PrefillWs &L = a.L;
+    // 16 KB: one head's dim-major block (v: 2 x 16 tokens fp32; k: hi and lo).
+    __shared__ uint4 stage[D == kConvThreads ? 1024 : 1];
     const int j = ch % D;
     if (is_q || is_k) {
       const int kh = (is_q ? ch : ch - nq) / D;
@@ -265,24 +267,58 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
           rl[sl >> 3][sl & 7] = lo[t];
         }
         const size_t blk = (static_cast<size_t>(b) * g.H_k + kh) * (L.T_pad / 32) + t0 / 32;
-        u16x8 *dh = reinterpret_cast<u16x8 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_hi) + (blk * D + j) * 32);
-        u16x8 *dl = reinterpret_cast<u16x8 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_lo) + (blk * D + j) * 32);
+        if constexpr (D == kConvThreads) {
+          // The head's rows form one 8 KB block per half (hi, lo): gather it
+          // in LDS and write it with lane-contiguous 16-byte stores.
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          dh[q] = rh[q];
-          dl[q] = rl[q];
+          for (int q = 0; q < 4; ++q) {
+            stage[j * 4 + q] = __builtin_bit_cast(uint4, rh[q]);
+            stage[512 + j * 4 + q] = __builtin_bit_cast(uint4, rl[q]);
+          }
+          __syncthreads();
+          uint4 *dh = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_hi) + blk * D * 32);
+          uint4 *dl = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_lo) + blk * D * 32);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dh[threadIdx.x + kConvThreads * u] = stage[threadIdx.x + kConvThreads * u];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dl[threadIdx.x + kConvThreads * u] = stage[512 + threadIdx.x + kConvThreads * u];
+        } else {
+          u16x8 *dh = reinterpret_cast<u16x8 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_hi) + (blk * D + j) * 32);
+          u16x8 *dl = reinterpret_cast<u16x8 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_lo) + (blk * D + j) * 32);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            dh[q] = rh[q];
+            dl[q] = rl[q];
+          }
         }
       }
     } else {
       const int h = (ch - nqk) / D;
+      if constexpr (D == kConvThreads) {
+        // Both 16-token blocks of the head are one contiguous 16 KB run:
+        // gather it in LDS and write it with lane-contiguous 16-byte stores.
 #pragma unroll
-      for (int half = 0; half < TT / 16; ++half) {
-        const size_t blk = (static_cast<size_t>(b) * g.H_v + h) * (L.T_pad / 16) + t0 / 16 + half;
-        float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.ws + L.vT) + (blk * D + j) * 16);
+        for (int half = 0; half < TT / 16; ++half)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dst[q] = make_float4(val[16 * half + 4 * q], val[16 * half + 4 * q + 1],
-                               val[16 * half + 4 * q + 2], val[16 * half + 4 * q + 3]);
+          for (int q = 0; q < 4; ++q)
+            stage[(half * D + j) * 4 + q] = __builtin_bit_cast(
+                uint4, make_float4(val[16 * half + 4 * q], val[16 * half + 4 * q + 1],
+                                   val[16 * half + 4 * q + 2], val[16 * half + 4 * q + 3]));
+        __syncthreads();
+        const size_t blk = (static_cast<size_t>(b) * g.H_v + h) * (L.T_pad / 16) + t0 / 16;
+        uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<float *>(a.ws + L.vT) + blk * D * 16);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dst[threadIdx.x + kConvThreads * u] = stage[threadIdx.x + kConvThreads * u];
+      } else {
+#pragma unroll
+        for (int half = 0; half < TT / 16; ++half) {
+          const size_t blk = (static_cast<size_t>(b) * g.H_v + h) * (L.T_pad / 16) + t0 / 16 + half;
+          float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.ws + L.vT) + (blk * D + j) * 16);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dst[q] = make_float4(val[16 * half + 4 * q], val[16 * half + 4 * q + 1],
+                                 val[16 * half + 4 * q + 2], val[16 * half + 4 * q + 3]);
+        }
       }
     }
   }

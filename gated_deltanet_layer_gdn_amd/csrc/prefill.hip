@@ -753,9 +753,11 @@ struct StateKernelWS {
     uint4 z[NT][16 * ZL];                  // per output wave: one token tile of z
   };
 
+  // Gate factors of the owned tile.  Lane (c, g) holds the factor of token
+  // 4g + (c % 4); quad_bcast hands every lane the four of its own rows.
   struct Gates {
-    float4 gam, bt, dl;  // gate factors of the owned tile (D-register order)
-    float glast;         // gamma of the chunk's last token
+    float gam, bt, dl;
+    float glast;  // gamma of the chunk's last token (wave-uniform)
   };
 
   struct ChainOps {
@@ -768,7 +770,7 @@ struct StateKernelWS {
 
   struct OutOps {
     u16x8 qh[NS], ql[NS];  // Q of the owned tile
-    float4 gam;
+    float gam;             // gamma of token 4g + (c % 4), as in Gates
     u16x8 ph[KSC], pl[KSC];
     uint4 z[ZK];
   };
@@ -823,36 +825,25 @@ struct StateKernelWS {
     for (int n = 0; n < NB; ++n) o.v[n] = ldb<float4>(base, x.o_v + n * 16 * 16 * 4);
   }
 
-  // The four factors of lane group gq from the 16 of the owned token tile.
-  // The address is wave-uniform, so these are scalar loads (sixteen lanes
-  // share every value; the vector memory path is left to the operands).
-  // readfirstlane keeps each value a single wave-wide one, so the compiler
-  // selects among registers instead of turning the selects back into a
-  // per-lane load.
-  static __device__ __forceinline__ float uni(const float *p) {
-    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*p)));
+  // Lane r of each group of four lanes to all four (DPP quad_perm r,r,r,r).
+  template <int R>
+  static __device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), R * 0x55, 0xf, 0xf, false));
   }
 
-  static __device__ __forceinline__ float4 tile_gate(const float *p, int gq) {
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = uni(p + i);
-    const bool b1 = gq & 1, b2 = gq & 2;
-    float4 r;
-    r.x = b2 ? (b1 ? v[12] : v[8]) : (b1 ? v[4] : v[0]);
-    r.y = b2 ? (b1 ? v[13] : v[9]) : (b1 ? v[5] : v[1]);
-    r.z = b2 ? (b1 ? v[14] : v[10]) : (b1 ? v[6] : v[2]);
-    r.w = b2 ? (b1 ? v[15] : v[11]) : (b1 ? v[7] : v[3]);
-    return r;
+  static __device__ __forceinline__ float4 quad4(float v) {
+    return make_float4(quad_bcast<0>(v), quad_bcast<1>(v), quad_bcast<2>(v), quad_bcast<3>(v));
   }
 
+  // One dword per lane: sixteen lanes share each group's four values, so
+  // the loads return a quarter of what per-lane float4 loads would.
   static __device__ __forceinline__ Gates load_gates(const Ctx &x, int chunk) {
     const float *gb = x.gates + static_cast<size_t>(chunk) * 3 * C;
     Gates o;
-    o.gam = tile_gate(gb + 16 * x.m, x.gq);
-    o.dl = tile_gate(gb + C + 16 * x.m, x.gq);
-    o.bt = tile_gate(gb + 2 * C + 16 * x.m, x.gq);
-    o.glast = uni(gb + C - 1);
+    o.gam = ldb<float>(gb, x.o_gate);
+    o.dl = ldb<float>(gb, x.o_gate + C * 4);
+    o.bt = ldb<float>(gb, x.o_gate + 2 * C * 4);
+    o.glast = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gb[C - 1])));
     return o;
   }
 
@@ -895,8 +886,9 @@ struct StateKernelWS {
   }
 
   static __device__ __forceinline__ void load_gam(const Ctx &x, int chunk, OutOps &o) {
-    o.gam = tile_gate(x.gates + static_cast<size_t>(chunk) * 3 * C + 16 * x.m, x.gq);
+    o.gam = ldb<float>(x.gates + static_cast<size_t>(chunk) * 3 * C, x.o_gate);
   }
+
 
 
   static __device__ void chain(const Ctx &x, Smem &sm, float *Sh, int w) {
@@ -951,7 +943,7 @@ struct StateKernelWS {
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         const float4 vv = o.v[n];
-        const float4 bt = o.g.bt, ga = o.g.gam;
+        const float4 bt = quad4(o.g.bt), ga = quad4(o.g.gam);
         const f32x4 r = {bt.x * (vv.x - ga.x * ks[n][0]), bt.y * (vv.y - ga.y * ks[n][1]),
                          bt.z * (vv.z - ga.z * ks[n][2]), bt.w * (vv.w - ga.w * ks[n][3])};
         sm.R[m][n][lane] = split4(r);
@@ -971,7 +963,7 @@ struct StateKernelWS {
             acc = mfma_split2(o.tm[kk], bh, bl, acc);
           }
         sm.U[m][n][lane] = split4(acc);
-        const float4 dl = o.g.dl;
+        const float4 dl = quad4(o.g.dl);
         const f32x4 du = {dl.x * acc[0], dl.y * acc[1], dl.z * acc[2], dl.w * acc[3]};
         sm.DU[m][n][lane] = split4(du);
       }
@@ -1080,7 +1072,8 @@ struct StateKernelWS {
       f32x4 out[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        f32x4 acc = {o.gam.x * qs[n][0], o.gam.y * qs[n][1], o.gam.z * qs[n][2], o.gam.w * qs[n][3]};
+        const float4 ga = quad4(o.gam);
+        f32x4 acc = {ga.x * qs[n][0], ga.y * qs[n][1], ga.z * qs[n][2], ga.w * qs[n][3]};
 #pragma unroll
         for (int kk = 0; kk < KSC; ++kk)
           if (kk <= m / 2) {
@@ -1175,7 +1168,7 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   x.o_v = ((ROWS * rb + c) * 16 + 4 * gq) * 4 + x.m * 16 * D * 4;
   x.o_mat = ((16 * x.m + c) * Cp + 8 * gq) * 2;
   x.o_zy = 4 * gq * g.H_v * D + c;
-  x.o_gate = (16 * x.m + 4 * gq) * 4;
+  x.o_gate = (16 * x.m + 4 * gq + (lane & 3)) * 4;
 
   float *Sh = S + ((static_cast<size_t>(b) * g.H_v + h) * D + ROWS * rb + c) * D;
   if (is_chain)
