@@ -87,7 +87,7 @@ struct PrepShape {
 };
 
 template <int D, int C>
-__global__ __launch_bounds__(256) void prep_kernel(Geom g, PrefillWs L,
+__global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, PrefillWs L,
                                                    const float *__restrict__ gl,
                                                    const float *__restrict__ beta,
                                                    char *__restrict__ ws) {
@@ -95,8 +95,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Geom g, PrefillWs L,
   constexpr int NT = Sh::NT, NTRI = Sh::NTRI, Dp = Sh::Dp, Cp = Sh::Cp;
   __shared__ float KK[NTRI][256];  // Gram tiles, row-major 16 x 16
   __shared__ float QK[NTRI][256];
-  __shared__ float TI[NTRI][256];  // (I + A)^{-1}
-  __shared__ float XS[NT > 1 ? NT - 1 : 1][256];
+  __shared__ float TI[NTRI][256];  // A, then (I + A)^{-1} in place
   __shared__ float Gs[C], Bs[C];
 
   const int chunk = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
@@ -164,74 +163,125 @@ __global__ __launch_bounds__(256) void prep_kernel(Geom g, PrefillWs L,
       }
     }
 
-    // A[t][s] = beta_t exp(G_t - G_s) KK[t][s] for s < t.
-    auto Aval = [&](int t, int s) -> float {
-      return Bs[t] * __expf(Gs[t] - Gs[s]) * KK[tri_index(t >> 4, s >> 4)][(t & 15) * 16 + (s & 15)];
-    };
-
-    // 2a. Diagonal 16 x 16 blocks by forward substitution, one column per thread.
+    // 2. Tm = (I + A)^{-1}, A[t][s] = beta_t exp(G_t - G_s) KK[t][s] (s < t),
+    //    blocked by 16 x 16 tiles and computed in place in TI:
+    //    (a) A, one exponential per entry;
+    //    (b) diagonal blocks X_ii = (I + A_ii)^{-1} by forward substitution;
+    //    (c) Y_ik = X_ii A_ik for k < i;
+    //    (d) block row by block row, X_ij = -sum_{k=j}^{i-1} Y_ik X_kj
+    //        (from sum_{k=j}^{i} L_ik X_kj = 0 for the block lower triangular
+    //        L = I + A).
+    // (The opaque copies keep per-lane constants inside this loop: hoisted
+    // out of it they would live across all value heads and spill.)
+    int r16 = threadIdx.x >> 4, c16 = threadIdx.x & 15;
+    asm volatile("" : "+v"(r16), "+v"(c16));
+#pragma unroll
+    for (int tri = 0; tri < NTRI; ++tri) {
+      int mt = 0;
+      while (tri_index(mt + 1, 0) <= tri) ++mt;
+      const int nt = tri - tri_index(mt, 0);
+      const int t = 16 * mt + r16, sc = 16 * nt + c16;
+      TI[tri][threadIdx.x] = sc < t ? Bs[t] * __expf(Gs[t] - Gs[sc]) * KK[tri][threadIdx.x] : 0.f;
+    }
+    __syncthreads();
     if (threadIdx.x < NT * 16) {
-      const int blk = threadIdx.x >> 4, col = threadIdx.x & 15;
+      // Column col of diagonal block blk; the block's lanes share one wave and
+      // run in lockstep, so every read below precedes the writes that follow.
+      const int blk = r16, col = c16;
+      const float *Ad = TI[tri_index(blk, blk)];
+      // x[r] = [r == col] - sum_{k<r} A[r][k] x[k]; entries above col are
+      // zero, so the sum needs no per-lane bounds.
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v = (r == col) ? 1.f : 0.f;
-        if (r > col) {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < r; ++k) acc = __builtin_fmaf(Ad[r * 16 + k], x[k], acc);
+        x[r] = (r == col ? 1.f : 0.f) - acc;
+      }
+      float *Xd = TI[tri_index(blk, blk)];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Xd[r * 16 + col] = x[r];
+    }
+    __syncthreads();
+    if constexpr (NT > 1) {
+      constexpr int NY = NT * (NT - 1) / 2;
+      float y[NY];
+#pragma unroll
+      for (int i = 1, q = 0; i < NT; ++i)
+#pragma unroll
+        for (int k = 0; k < i; ++k, ++q) {
+          const float *Xi = TI[tri_index(i, i)];
+          const float *Aik = TI[tri_index(i, k)];
           float acc = 0.f;
 #pragma unroll
-          for (int k = 0; k < 16; ++k)
-            if (k >= col && k < r) acc = __builtin_fmaf(Aval(16 * blk + r, 16 * blk + k), x[k], acc);
-          v = -acc;
+          for (int m = 0; m < 16; ++m) acc = __builtin_fmaf(Xi[r16 * 16 + m], Aik[m * 16 + c16], acc);
+          y[q] = acc;
+          // One 16-term product at a time: keeps the LDS reads of the next
+          // product from being hoisted into registers all at once.
+          asm volatile("" ::: "memory");
         }
-        x[r] = v;
-      }
+      __syncthreads();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) TI[tri_index(blk, blk)][r * 16 + col] = x[r];
-    }
-    // 2b. Off-diagonal blocks, one block diagonal at a time:
-    //     Tm_ij = -Tm_ii sum_{k=j}^{i-1} A_ik Tm_kj.
-    for (int d = 1; d < NT; ++d) {
-      __syncthreads();
-      const int r = threadIdx.x >> 4, cc = threadIdx.x & 15;
-      for (int i = d; i < NT; ++i) {
-        const int j = i - d;
-        float acc = 0.f;
-        for (int k = j; k < i; ++k)
-          for (int m = 0; m < 16; ++m)
-            acc = __builtin_fmaf(Aval(16 * i + r, 16 * k + m), TI[tri_index(k, j)][m * 16 + cc], acc);
-        XS[i - d][r * 16 + cc] = acc;
-      }
-      __syncthreads();
-      for (int i = d; i < NT; ++i) {
-        const int j = i - d;
-        float acc = 0.f;
-        for (int m = 0; m < 16; ++m)
-          acc = __builtin_fmaf(TI[tri_index(i, i)][r * 16 + m], XS[i - d][m * 16 + cc], acc);
-        TI[tri_index(i, j)][r * 16 + cc] = -acc;
+      for (int i = 1, q = 0; i < NT; ++i)
+#pragma unroll
+        for (int k = 0; k < i; ++k, ++q) TI[tri_index(i, k)][threadIdx.x] = y[q];
+      // Block row i, left to right: element (r, c) of X_ij reads only row r
+      // of Y_i. (and finished rows above), and the sixteen threads of a row
+      // share one wave, so X_ij can replace Y_ij as soon as it is formed;
+      // Y_ij is not read again (later blocks of the row use k > j).
+#pragma unroll
+      for (int i = 1; i < NT; ++i) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
+          float acc = 0.f;
+#pragma unroll
+          for (int k = j; k < i; ++k) {
+            const float *Yik = TI[tri_index(i, k)];
+            const float *Xkj = TI[tri_index(k, j)];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) acc = __builtin_fmaf(Yik[r16 * 16 + m], Xkj[m * 16 + c16], acc);
+            asm volatile("" ::: "memory");
+          }
+          TI[tri_index(i, j)][threadIdx.x] = -acc;
+        }
       }
     }
     __syncthreads();
 
     // 3. Store Tm (bf16) and P (hi/lo) as A operands: row t, column s at its
     //    permuted K slot; zero above the diagonal and in the padding columns.
+    //    One item is the 16-byte piece of slots 8q..8q+7 of a 32-column step,
+    //    which holds columns 4q..4q+3 and 16+4q..16+4q+3 of that step.
     const size_t mat = ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C * Cp;
     uint16_t *Tm = reinterpret_cast<uint16_t *>(ws + L.Tm) + mat;
     uint16_t *Ph = reinterpret_cast<uint16_t *>(ws + L.P_hi) + mat;
     uint16_t *Pl = reinterpret_cast<uint16_t *>(ws + L.P_lo) + mat;
-    for (int e = threadIdx.x; e < C * Cp; e += 256) {
-      const int t = e / Cp, s = e % Cp;
-      float tv = 0.f, pv = 0.f;
-      if (s < C && s <= t) {
-        const int tr = tri_index(t >> 4, s >> 4), off = (t & 15) * 16 + (s & 15);
-        tv = TI[tr][off];
-        pv = __expf(Gs[t] - Gs[s]) * QK[tr][off];
+    constexpr int ITEMS = C * (Cp / 32) * 4;
+    for (int it = threadIdx.x; it < ITEMS; it += 256) {
+      const int t = it / (Cp / 8), rem = it % (Cp / 8);
+      const int kk = rem >> 2, q = rem & 3;
+      u16x8 tv8, ph8, pl8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int sc = 32 * kk + (i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4));
+        float tv = 0.f, pv = 0.f;
+        if (sc < C && sc <= t) {
+          const int tr = tri_index(t >> 4, sc >> 4), off = (t & 15) * 16 + (sc & 15);
+          tv = TI[tr][off];
+          pv = __expf(Gs[t] - Gs[sc]) * QK[tr][off];
+        }
+        uint16_t hi, lo;
+        split_bf16(pv, hi, lo);
+        tv8[i] = f32_to_bf16_bits(tv);
+        ph8[i] = hi;
+        pl8[i] = lo;
       }
-      const size_t o = static_cast<size_t>(t) * Cp + (s & ~31) + kslot(s & 31);
-      Tm[o] = f32_to_bf16_bits(tv);
-      uint16_t hi, lo;
-      split_bf16(pv, hi, lo);
-      Ph[o] = hi;
-      Pl[o] = lo;
+      const size_t o = static_cast<size_t>(t) * Cp + 32 * kk + 8 * q;
+      *reinterpret_cast<u16x8 *>(Tm + o) = tv8;
+      *reinterpret_cast<u16x8 *>(Ph + o) = ph8;
+      *reinterpret_cast<u16x8 *>(Pl + o) = pl8;
     }
   }
 }
