@@ -144,7 +144,7 @@ def main():
     tok_s = G.B * G.T / (ms_step * 1e-3)
     log(f"[bench] prefill: {ms_step * 1e3:.1f} us/step, {tok_s:.4g} tokens/s")
 
-    names = ["conv", "prep", "roll", "state"]
+    names = ["conv", "prep", "state"]
     per = {n: [] for n in names}
     for _ in range(args.steps):
         km = []

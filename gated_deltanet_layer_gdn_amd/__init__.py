@@ -127,7 +127,8 @@ def prefill_chunked(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, chunk
                     y=None, ws=None, kernel_ms=None):
     """Whole layer over T tokens; updates conv_state and rec_state in place and
     returns y [B,T,H_v,d_v].  With ``kernel_ms`` (a list), calls the timed
-    entry point and appends the 4 per-kernel durations in ms."""
+    entry point and appends the 3 per-kernel durations in ms (conv, prep with the history
+    roll, state)."""
     torch = _torch()
     L = _lib.load()
     T = x.shape[1]
@@ -152,7 +153,7 @@ def prefill_chunked(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, chunk
     if kernel_ms is None:
         rc = L.gdn_prefill_chunked(ctypes.byref(d.c()), T, chunk, *args, *tail)
     else:
-        ms = (ctypes.c_float * 4)()
+        ms = (ctypes.c_float * 3)()
         rc = L.gdn_prefill_chunked_timed(ctypes.byref(d.c()), T, chunk, *args, *tail, ms)
         kernel_ms.extend(float(v) for v in ms)
     _lib.check(rc, "gdn_prefill_chunked")

@@ -301,9 +301,7 @@ static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const vo
   hipError_t e = tm.mark(s);
   if (e == hipSuccess) e = launch_conv_prefill(g, L, x, conv_w, conv_state, w, s);
   if (e == hipSuccess) e = tm.mark(s);
-  if (e == hipSuccess) e = launch_prefill_prep(g, L, gl, beta, w, s);
-  if (e == hipSuccess) e = tm.mark(s);
-  if (e == hipSuccess) e = launch_conv_roll(g, T, x, conv_state, s);
+  if (e == hipSuccess) e = launch_prefill_prep(g, L, gl, beta, w, x, conv_state, s);
   if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = launch_prefill_state(g, L, z, rec_state, y, w, s);
   if (e == hipSuccess) e = tm.mark(s);

@@ -49,8 +49,10 @@ hipError_t launch_conv_roll(const Geom &g, int64_t T, const void *x, void *hist,
                             hipStream_t s);
 hipError_t launch_decode(const Geom &g, const float *qkv, const void *z, const float *gl,
                          const float *beta, float *S, void *y, hipStream_t s);
+// Also rolls the conv history (x, hist) after the sequence.
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
-                               const float *beta, char *ws, hipStream_t s);
+                               const float *beta, char *ws, const void *x, void *hist,
+                               hipStream_t s);
 hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z, float *S,
                                 void *y, const char *ws, hipStream_t s);
 

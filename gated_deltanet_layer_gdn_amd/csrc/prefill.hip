@@ -86,11 +86,32 @@ struct PrepShape {
   static constexpr int KS_D = Dp / 32;  // K steps over the head dimension
 };
 
+// Conv history after the whole sequence: the last three rows of
+// concat(history, x), copied bit for bit, for the channels [c0, c1).  Each
+// thread reads its channel's three values before writing them.
+template <typename E>
+__device__ __forceinline__ void roll_history(int C_ch, int64_t T, int b, int c0, int c1,
+                                             const E *__restrict__ x, E *__restrict__ hist) {
+  for (int ch = c0 + static_cast<int>(threadIdx.x); ch < c1; ch += blockDim.x) {
+    E v[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int64_t src = T + r;  // index into concat(history[0..2], x[0..T-1])
+      v[r] = src < 3 ? hist[(static_cast<size_t>(b) * 3 + src) * C_ch + ch]
+                     : x[(static_cast<size_t>(b) * T + (src - 3)) * C_ch + ch];
+    }
+#pragma unroll
+    for (int r = 0; r < 3; ++r) hist[(static_cast<size_t>(b) * 3 + r) * C_ch + ch] = v[r];
+  }
+}
+
 template <int D, int C>
 __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, PrefillWs L,
                                                    const float *__restrict__ gl,
                                                    const float *__restrict__ beta,
-                                                   char *__restrict__ ws) {
+                                                   char *__restrict__ ws,
+                                                   const void *__restrict__ x,
+                                                   void *__restrict__ hist) {
   using Sh = PrepShape<D, C>;
   constexpr int NT = Sh::NT, NTRI = Sh::NTRI, Dp = Sh::Dp, Cp = Sh::Cp;
   __shared__ float KK[NTRI][256];  // Gram tiles, row-major 16 x 16
@@ -103,6 +124,18 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
   const int c = lane & 15, gq = lane >> 4;
   const int64_t tau0 = static_cast<int64_t>(chunk) * C;
   const int n_valid = static_cast<int>((L.T - tau0) < C ? (L.T - tau0) : C);
+
+  // 0. The conv history roll rides on the first chunk's blocks (one slice of
+  //    the channels per key head): the conv pass, its only reader, has
+  //    finished before this kernel starts.
+  if (chunk == 0) {
+    const int per = (g.C_ch + g.H_k - 1) / g.H_k;
+    const int c0 = kh * per, c1 = c0 + per < g.C_ch ? c0 + per : g.C_ch;
+    if (g.in_dt == 0)
+      roll_history(g.C_ch, L.T, b, c0, c1, static_cast<const uint32_t *>(x), static_cast<uint32_t *>(hist));
+    else
+      roll_history(g.C_ch, L.T, b, c0, c1, static_cast<const uint16_t *>(x), static_cast<uint16_t *>(hist));
+  }
 
   // 1. K K^T and Q K^T, lower tiles only, split operands.
   {
@@ -1231,19 +1264,20 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
 
 template <int D, int C>
 static void launch_prep_t(const Geom &g, const PrefillWs &L, const float *gl, const float *beta,
-                          char *ws, hipStream_t s) {
+                          char *ws, const void *x, void *hist, hipStream_t s) {
   dim3 grid(L.NC, g.H_k, g.B);
-  hipLaunchKernelGGL((prep_kernel<D, C>), grid, dim3(256), 0, s, g, L, gl, beta, ws);
+  hipLaunchKernelGGL((prep_kernel<D, C>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
 }
 
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
-                               const float *beta, char *ws, hipStream_t s) {
-#define GDN_PREP(Dv)                                              \
-  switch (L.C) {                                                  \
-    case 16: launch_prep_t<Dv, 16>(g, L, gl, beta, ws, s); break; \
-    case 32: launch_prep_t<Dv, 32>(g, L, gl, beta, ws, s); break; \
-    case 64: launch_prep_t<Dv, 64>(g, L, gl, beta, ws, s); break; \
-    default: launch_prep_t<Dv, 128>(g, L, gl, beta, ws, s); break; \
+                               const float *beta, char *ws, const void *x, void *hist,
+                               hipStream_t s) {
+#define GDN_PREP(Dv)                                                       \
+  switch (L.C) {                                                           \
+    case 16: launch_prep_t<Dv, 16>(g, L, gl, beta, ws, x, hist, s); break;  \
+    case 32: launch_prep_t<Dv, 32>(g, L, gl, beta, ws, x, hist, s); break;  \
+    case 64: launch_prep_t<Dv, 64>(g, L, gl, beta, ws, x, hist, s); break;  \
+    default: launch_prep_t<Dv, 128>(g, L, gl, beta, ws, x, hist, s); break; \
   }
   if (g.D == 128) {
     GDN_PREP(128)

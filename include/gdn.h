@@ -160,8 +160,8 @@ GDN_API int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, 
  * `kernel_ms`, which receives the duration of each kernel launch of the call,
  * taken from HIP events that the library records on `stream` between its
  * launches:
- *   prefill: [0] conv + L2 norm, [1] chunk-local prep (Gram, (I+A)^{-1}, P),
- *            [2] conv history roll, [3] state pass + gate          (4 floats)
+ *   prefill: [0] conv + L2 norm, [1] chunk-local prep (Gram, (I+A)^{-1}, P)
+ *            and the conv history roll, [2] state pass + gate     (3 floats)
  *   decode:  [0] conv step + L2 norm, [1] state stream + gate      (2 floats)
  * These variants create HIP events and wait for the last one before they
  * return. */
