@@ -32,6 +32,7 @@ struct ConvArgs {
   int64_t T;       // real tokens
   int64_t T_iter;  // tokens the grid walks (T, or T_pad for the prefill layout)
   int fuse_roll;   // single tile holds every token: roll the history in place
+  int write_kT;    // prefill layout: also write the dim-major copy of k
 };
 
 // Sums of squares over the D consecutive threads of one head, for all kConvTT
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
           plo[(row0 + t) * 32 + kslot(j + 16)] = 0;
         }
       }
-      if (is_k) {
+      if (is_k && a.write_kT) {
         // Dim-major row of this channel: 32 tokens in permuted K order.
         u16x8 rh[4], rl[4];
 #pragma unroll
@@ -400,6 +401,7 @@ hipError_t launch_conv_prefill(const Geom &g, const PrefillWs &L, const void *x,
   a.T = L.T;
   a.T_iter = L.T_pad;
   a.fuse_roll = 0;
+  a.write_kT = prefill_needs_kT(g, L);
   return launch_conv<kOutPrefill, kConvTT>(g, a, s);
 }
 

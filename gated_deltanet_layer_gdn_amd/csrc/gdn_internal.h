@@ -38,6 +38,9 @@ struct PrefillWs {
 };
 
 bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *ws);
+// Whether the state pass reads the dim-major copy of k from the workspace
+// (the d = 128, 64-token-chunk pass builds it in LDS instead).
+inline bool prefill_needs_kT(const Geom &g, const PrefillWs &L) { return !(g.D == 128 && L.C == 64); }
 size_t decode_ws_bytes(const Geom &g);
 
 // Kernel launchers (enqueue only; return the launch status).

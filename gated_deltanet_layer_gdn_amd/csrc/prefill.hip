@@ -828,8 +828,14 @@ struct StateKernelWS {
   static constexpr int ZK = (16 * ZL + 63) / 64; // pieces per lane per tile
   static constexpr int kThreads = 512;
 
+  static constexpr int KTS = C + 8;  // row stride of the dim-major K copy (padded)
+
   struct Smem {
     u16x8 Sh[NS][NB][64], Sl[NS][NB][64];  // state as split B operands, one d_k step each
+    // K of the chunk, dim-major (row d_k, tokens in permuted K order), hi
+    // and lo: the A operands of the state update, gathered from the chain
+    // waves' token-major tiles instead of a second copy in HBM.
+    alignas(16) uint16_t KT[2][D][KTS];
     Split4 R[NT][NB][64];
     Split4 U[NT][NB][64];
     Split4 DU[NT][NB][64];
@@ -848,7 +854,6 @@ struct StateKernelWS {
     float4 v[NB];                      // V of the owned tile (D-register order)
     Gates g;
     u16x8 tm[KSC];                     // (I+A)^{-1} rows of the owned tile
-    u16x8 th[NDT][KSC], tl[NDT][KSC];  // K^T of the owned d_k slice
   };
 
   struct OutOps {
@@ -861,7 +866,6 @@ struct StateKernelWS {
   struct Ctx {
     const char *ktok_hi, *ktok_lo, *qtok_hi, *qtok_lo;  // slice 0 of this key head
     size_t slice_bytes;                                  // T_pad * 32 * 2
-    const uint16_t *kThi, *kTlo;
     const float *vT;
     const uint16_t *Tm, *Ph, *Pl;
     const float *gates;
@@ -869,7 +873,7 @@ struct StateKernelWS {
     void *y;
     int64_t T;
     int H_v, NC, m, lane, gq;
-    uint32_t o_tok, o_kT, o_v, o_mat, o_zy, o_gate;
+    uint32_t o_tok, o_v, o_mat, o_zy, o_gate;
   };
 
   static __device__ __forceinline__ int valid_of(const Ctx &x, int chunk) {
@@ -942,17 +946,7 @@ struct StateKernelWS {
     }
   }
 
-  static __device__ __forceinline__ void load_kT(const Ctx &x, int chunk, ChainOps &o) {
-    const size_t base = static_cast<size_t>(chunk) * C * D;
-#pragma unroll
-    for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint32_t ao = x.o_kT + (ks * D + 16 * dt) * 32 * 2;
-        o.th[dt][ks] = ldb<u16x8>(x.kThi + base, ao);
-        o.tl[dt][ks] = ldb<u16x8>(x.kTlo + base, ao);
-      }
-  }
+
 
   static __device__ __forceinline__ void load_z(const Ctx &x, int chunk, OutOps &o) {
     const int n_valid = valid_of(x, chunk);
@@ -998,9 +992,10 @@ struct StateKernelWS {
     asm volatile("" ::: "memory");
     load_rows(x.Tm, x, 0, o.tm);
     asm volatile("" ::: "memory");
-    load_kT(x, 0, o);
-    asm volatile("" ::: "memory");
     __syncthreads();
+    // Row of the owned tile's tokens in the dim-major copy.
+    const int t_own = 16 * m + (lane & 15);
+    const int t_slot = 32 * (t_own >> 5) + kslot(t_own & 31);
 
     for (int chunk = 0; chunk < x.NC; ++chunk) {
       const int next = chunk + 1 < x.NC ? chunk + 1 : chunk;
@@ -1022,6 +1017,16 @@ struct StateKernelWS {
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int n = 0; n < NB; ++n) ks[n] = mfma_split3(o.kh[s], o.kl[s], bh[s][n], bl[s][n], ks[n]);
+      // The owned K tile into the dim-major copy: slot 8g + i of d_k step s
+      // holds d_k = 32 s + (4g + i, or 16 + 4g + i - 4 for i >= 4).
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int dk = 32 * s + (i < 4 ? 4 * x.gq + i : 16 + 4 * x.gq + i - 4);
+          sm.KT[0][dk][t_slot] = o.kh[s][i];
+          sm.KT[1][dk][t_slot] = o.kl[s][i];
+        }
       load_tok(x.ktok_hi, x.ktok_lo, x, next, o.kh, o.kl);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
@@ -1063,11 +1068,14 @@ struct StateKernelWS {
           u16x8 bh, bl;
           operand(sm.DU[2 * kk][n][lane], sm.DU[2 * kk + 1][n][lane], bh, bl);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-            st[n][dt] = mfma_split3(o.th[dt][kk], o.tl[dt][kk], bh, bl, st[n][dt]);
+          for (int dt = 0; dt < NDT; ++dt) {
+            const int dk = 32 * w + 16 * dt + (lane & 15);
+            const u16x8 th = *reinterpret_cast<const u16x8 *>(&sm.KT[0][dk][32 * kk + 8 * x.gq]);
+            const u16x8 tl = *reinterpret_cast<const u16x8 *>(&sm.KT[1][dk][32 * kk + 8 * x.gq]);
+            st[n][dt] = mfma_split3(th, tl, bh, bl, st[n][dt]);
+          }
         }
       }
-      load_kT(x, next, o);
 #pragma unroll
       for (int n = 0; n < NB; ++n) pack_split(st[n][0], st[n][1], sm.Sh[w][n][lane], sm.Sl[w][n][lane]);
       o.g = gn;
@@ -1228,9 +1236,6 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   x.qtok_hi = ws + L.q_hi + slice0;
   x.qtok_lo = ws + L.q_lo + slice0;
   x.slice_bytes = static_cast<size_t>(L.T_pad) * 32 * 2;
-  const size_t kbase = (static_cast<size_t>(b) * g.H_k + kh) * L.T_pad;
-  x.kThi = reinterpret_cast<const uint16_t *>(ws + L.kT_hi) + kbase * D;
-  x.kTlo = reinterpret_cast<const uint16_t *>(ws + L.kT_lo) + kbase * D;
   x.vT = reinterpret_cast<const float *>(ws + L.vT) + (static_cast<size_t>(b) * g.H_v + h) * L.T_pad * D;
   const size_t mat = (static_cast<size_t>(b) * g.H_v + h) * L.NC * C * Cp;
   x.Tm = reinterpret_cast<const uint16_t *>(ws + L.Tm) + mat;
@@ -1247,7 +1252,6 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   x.lane = lane;
   x.gq = gq;
   x.o_tok = ((16 * x.m + c) * 32 + 8 * gq) * 2;
-  x.o_kT = ((32 * wave + c) * 32 + 8 * gq) * 2;
   x.o_v = ((ROWS * rb + c) * 16 + 4 * gq) * 4 + x.m * 16 * D * 4;
   x.o_mat = ((16 * x.m + c) * Cp + 8 * gq) * 2;
   x.o_zy = 4 * gq * g.H_v * D + c;
