@@ -343,6 +343,79 @@ __global__ __launch_bounds__(256) void roll_kernel(int C_ch, int64_t T, const E 
   for (int r = 0; r < 3; ++r) hist[(static_cast<size_t>(b) * 3 + r) * C_ch + ch] = v[r];
 }
 
+// One token per sequence (decode step): one thread owns one channel for BB
+// sequences, so a block does BB rows of work and the per-head sums of all BB
+// rows share one LDS exchange.  The history roll (rows 1, 2 and the new
+// token become rows 0..2) stays with the thread that read those rows.
+template <int DT, int D, int BB>
+__global__ __launch_bounds__(kConvThreads) void conv_step_kernel(Geom g, const void *x,
+                                                                 const void *w, void *hist,
+                                                                 float *out) {
+  __shared__ float red[2][kConvTT];
+  const int ch = blockIdx.x * kConvThreads + threadIdx.x;
+  const int b0 = blockIdx.y * BB;
+  const bool active = ch < g.C_ch;
+  const int chc = active ? ch : g.C_ch - 1;
+  const int nq = g.H_k * D;
+  const int head0 = (D == 128) ? static_cast<int>(blockIdx.x) * kConvThreads : ch;
+  const bool is_q = head0 < nq;
+  const bool is_k = !is_q && head0 < 2 * nq;
+  const bool qk_block = (D == 128) ? (is_q || is_k) : true;
+  const size_t C = g.C_ch;
+  const float w0 = load_elem<DT>(w, static_cast<size_t>(chc) * 4 + 0);
+  const float w1 = load_elem<DT>(w, static_cast<size_t>(chc) * 4 + 1);
+  const float w2 = load_elem<DT>(w, static_cast<size_t>(chc) * 4 + 2);
+  const float w3 = load_elem<DT>(w, static_cast<size_t>(chc) * 4 + 3);
+  float xv[BB][4], val[BB], ss[BB];
+#pragma unroll
+  for (int r = 0; r < BB; ++r) {
+    const int b = b0 + r < g.B ? b0 + r : g.B - 1;  // rows past B re-read the last one
+#pragma unroll
+    for (int k = 0; k < 3; ++k) xv[r][k] = load_elem<DT>(hist, (static_cast<size_t>(b) * 3 + k) * C + chc);
+    xv[r][3] = load_elem<DT>(x, static_cast<size_t>(b) * C + chc);
+    val[r] = siluf_(conv4(w0, w1, w2, w3, xv[r][0], xv[r][1], xv[r][2], xv[r][3]));
+    ss[r] = val[r] * val[r];
+  }
+  if (qk_block) {
+    head_sums<D, BB>(ss, red);
+    if (is_q || is_k) {
+      const float sc = is_q ? g.q_scale : 1.0f;
+#pragma unroll
+      for (int r = 0; r < BB; ++r) val[r] *= __builtin_amdgcn_rsqf(ss[r] + g.eps) * sc;
+    }
+  }
+  if (!active) return;
+#pragma unroll
+  for (int r = 0; r < BB; ++r) {
+    const int b = b0 + r;
+    if (b < g.B) {
+      out[static_cast<size_t>(b) * C + ch] = val[r];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) store_elem<DT>(hist, (static_cast<size_t>(b) * 3 + k) * C + ch, xv[r][k + 1]);
+    }
+  }
+}
+
+template <int D, int BB>
+static hipError_t launch_conv_step_t(const Geom &g, const void *x, const void *w, void *hist,
+                                     float *out, hipStream_t s) {
+  dim3 grid((g.C_ch + kConvThreads - 1) / kConvThreads, (g.B + BB - 1) / BB);
+  if (g.in_dt == 0)
+    hipLaunchKernelGGL((conv_step_kernel<0, D, BB>), grid, dim3(kConvThreads), 0, s, g, x, w, hist, out);
+  else
+    hipLaunchKernelGGL((conv_step_kernel<1, D, BB>), grid, dim3(kConvThreads), 0, s, g, x, w, hist, out);
+  return hipGetLastError();
+}
+
+static hipError_t launch_conv_step(const Geom &g, const void *x, const void *w, void *hist,
+                                   float *out, hipStream_t s) {
+  if (g.D == 128)
+    return g.B >= 8 ? launch_conv_step_t<128, 8>(g, x, w, hist, out, s)
+                    : launch_conv_step_t<128, 1>(g, x, w, hist, out, s);
+  return g.B >= 8 ? launch_conv_step_t<16, 8>(g, x, w, hist, out, s)
+                  : launch_conv_step_t<16, 1>(g, x, w, hist, out, s);
+}
+
 template <int MODE, int TT>
 static hipError_t launch_conv(const Geom &g, const ConvArgs &a, hipStream_t s) {
   const int64_t tiles = (a.T_iter + TT - 1) / TT;
@@ -384,8 +457,8 @@ hipError_t launch_conv_plain(const Geom &g, int64_t T, const void *x, const void
   a.T = T;
   a.T_iter = T;
   a.fuse_roll = T <= kConvTT;
-  // One token per sequence (decode): a one-token tile does no wasted work.
-  hipError_t e = (T == 1) ? launch_conv<kOutPlain, 1>(g, a, s) : launch_conv<kOutPlain, kConvTT>(g, a, s);
+  if (T == 1) return launch_conv_step(g, x, w, hist, out, s);
+  hipError_t e = launch_conv<kOutPlain, kConvTT>(g, a, s);
   if (e != hipSuccess || a.fuse_roll) return e;
   return launch_conv_roll(g, T, x, hist, s);
 }

@@ -22,6 +22,14 @@
 
 namespace gdn {
 
+// The state is read exactly once per step: nontemporal loads keep that
+// stream from displacing cached data (measured: about 12% faster at B = 64).
+__device__ __forceinline__ float4 load_stream(const float4 *p) {
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  const f4v r = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p));
+  return make_float4(r[0], r[1], r[2], r[3]);
+}
+
 template <int D>
 struct DecodeShape {
   static constexpr int NPL = (D >= 128) ? 16 : 4;  // floats per lane per row
@@ -44,6 +52,83 @@ __global__ __launch_bounds__(256) void decode_kernel(Geom g, const float *__rest
   const int j = lane % LPR;  // column slot of this lane
   const int64_t base_row = static_cast<int64_t>(blockIdx.x) * (PASSES * Sh::RPB);
 
+  if constexpr (PASSES * Sh::RPB == D) {
+    // The block is exactly one (sequence, value head): k, q, k.q and the
+    // gates are loaded once, then the PASSES groups of rows stream through.
+    const int64_t bh = blockIdx.x;
+    const int h = static_cast<int>(bh % g.H_v);
+    const int b = static_cast<int>(bh / g.H_v);
+    const int kh = h / g.G;
+    float *Sb = S + bh * D * D;
+    float4 s[PASSES][NV];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int i = p * Sh::RPB + wave * Sh::RPW + lane / LPR;
+      const float4 *src = reinterpret_cast<const float4 *>(Sb + static_cast<size_t>(i) * D);
+#pragma unroll
+      for (int m = 0; m < NV; ++m) s[p][m] = load_stream(src + j + LPR * m);
+    }
+    const float *qrow = qkv + static_cast<size_t>(b) * g.C_ch + kh * D;
+    const float *krow = qrow + g.H_k * D;
+    float4 kv[NV], qv[NV];
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      kv[m] = reinterpret_cast<const float4 *>(krow)[j + LPR * m];
+      qv[m] = reinterpret_cast<const float4 *>(qrow)[j + LPR * m];
+    }
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      kq = __builtin_fmaf(kv[m].x, qv[m].x, kq);
+      kq = __builtin_fmaf(kv[m].y, qv[m].y, kq);
+      kq = __builtin_fmaf(kv[m].z, qv[m].z, kq);
+      kq = __builtin_fmaf(kv[m].w, qv[m].w, kq);
+    }
+#pragma unroll
+    for (int msk = LPR / 2; msk >= 1; msk >>= 1) kq += __shfl_xor(kq, msk, kWave);
+    const float a = __expf(gl[bh]);
+    const float bt = beta[bh];
+    const float *vrow = qkv + static_cast<size_t>(b) * g.C_ch + 2 * g.H_k * D + h * D;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int i = p * Sh::RPB + wave * Sh::RPW + lane / LPR;
+      float pk = 0.f, pq = 0.f;
+#pragma unroll
+      for (int m = 0; m < NV; ++m) {
+        const float4 sv = s[p][m];
+        pk = __builtin_fmaf(sv.x, kv[m].x, pk);
+        pk = __builtin_fmaf(sv.y, kv[m].y, pk);
+        pk = __builtin_fmaf(sv.z, kv[m].z, pk);
+        pk = __builtin_fmaf(sv.w, kv[m].w, pk);
+        pq = __builtin_fmaf(sv.x, qv[m].x, pq);
+        pq = __builtin_fmaf(sv.y, qv[m].y, pq);
+        pq = __builtin_fmaf(sv.z, qv[m].z, pq);
+        pq = __builtin_fmaf(sv.w, qv[m].w, pq);
+      }
+#pragma unroll
+      for (int msk = LPR / 2; msk >= 1; msk >>= 1) {
+        pk += __shfl_xor(pk, msk, kWave);
+        pq += __shfl_xor(pq, msk, kWave);
+      }
+      const float u = bt * (vrow[i] - a * pk);
+      const float o = a * pq + u * kq;
+      float4 *dst = reinterpret_cast<float4 *>(Sb + static_cast<size_t>(i) * D);
+#pragma unroll
+      for (int m = 0; m < NV; ++m) {
+        float4 n;
+        n.x = __builtin_fmaf(u, kv[m].x, a * s[p][m].x);
+        n.y = __builtin_fmaf(u, kv[m].y, a * s[p][m].y);
+        n.z = __builtin_fmaf(u, kv[m].z, a * s[p][m].z);
+        n.w = __builtin_fmaf(u, kv[m].w, a * s[p][m].w);
+        dst[j + LPR * m] = n;
+      }
+      if (j == 0) {
+        const size_t yi = static_cast<size_t>(bh) * D + i;
+        store_elem<DTY>(y, yi, o * sigmoidf_(load_elem<DTZ>(z, yi)));
+      }
+    }
+    return;
+  }
   float4 s[PASSES][NV];
   int64_t rows[PASSES];
 #pragma unroll
@@ -52,7 +137,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Geom g, const float *__rest
     if (rows[p] < total_rows) {
       const float4 *src = reinterpret_cast<const float4 *>(S + rows[p] * D);
 #pragma unroll
-      for (int m = 0; m < NV; ++m) s[p][m] = src[j + LPR * m];
+      for (int m = 0; m < NV; ++m) s[p][m] = load_stream(src + j + LPR * m);
     }
   }
 #pragma unroll
