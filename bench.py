@@ -311,7 +311,7 @@ def main():
                "sample": f"the whole prefill workload (B=1, T={G.T}, all {G.H_v} value heads) "
                          f"through the fp64 oracle {passes} times, {dt:.2f} s wall on {nth} "
                          f"threads"}
-        log(f"[bench] cpu oracle: {G.T / dt:.1f} tokens/s on {nth} threads ({dt:.2f} s)")
+        log(f"[bench] cpu oracle: {cpu['value']:.1f} tokens/s on {nth} threads ({passes} passes, {dt:.2f} s)")
 
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
