@@ -33,6 +33,7 @@ struct ConvArgs {
   int64_t T_iter;  // tokens the grid walks (T, or T_pad for the prefill layout)
   int fuse_roll;   // single tile holds every token: roll the history in place
   int write_kT;    // prefill layout: also write the dim-major copy of k
+  int write_v;     // prefill layout: also compute and write v (else q, k only)
 };
 
 // Sums of squares over the D consecutive threads of one head, for all kConvTT
@@ -419,7 +420,9 @@ static hipError_t launch_conv_step(const Geom &g, const void *x, const void *w, 
 template <int MODE, int TT>
 static hipError_t launch_conv(const Geom &g, const ConvArgs &a, hipStream_t s) {
   const int64_t tiles = (a.T_iter + TT - 1) / TT;
-  dim3 grid(static_cast<unsigned>(tiles), (g.C_ch + kConvThreads - 1) / kConvThreads, g.B);
+  // Without v the grid covers the q and k channels only (whole heads at d = 128).
+  const int chans = (MODE == kOutPrefill && !a.write_v) ? 2 * g.H_k * g.D : g.C_ch;
+  dim3 grid(static_cast<unsigned>(tiles), (chans + kConvThreads - 1) / kConvThreads, g.B);
   dim3 block(kConvThreads);
   if (g.D == 128) {
     if (g.in_dt == 0)
@@ -450,6 +453,7 @@ hipError_t launch_conv_roll(const Geom &g, int64_t T, const void *x, void *hist,
 hipError_t launch_conv_plain(const Geom &g, int64_t T, const void *x, const void *w,
                              void *hist, float *out, hipStream_t s) {
   ConvArgs a{};
+  a.write_v = 1;
   a.x = x;
   a.w = w;
   a.hist = hist;
@@ -474,7 +478,8 @@ hipError_t launch_conv_prefill(const Geom &g, const PrefillWs &L, const void *x,
   a.T = L.T;
   a.T_iter = L.T_pad;
   a.fuse_roll = 0;
-  a.write_kT = prefill_needs_kT(g, L);
+  a.write_kT = !prefill_split_roles(g, L);
+  a.write_v = !prefill_split_roles(g, L);
   return launch_conv<kOutPrefill, kConvTT>(g, a, s);
 }
 

@@ -283,12 +283,13 @@ static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const vo
   if (!prefill_ws_layout(g, T, chunk, &L)) return GDN_ERR_UNSUPPORTED;
   const size_t es = esize(g.in_dt), eo = esize(g.out_dt);
   const size_t bt = static_cast<size_t>(g.B) * T;
-  const Buf in[] = {{x, bt * g.C_ch * es, es},
+  // x and the conv history are read in 16-byte pieces by the state pass.
+  const Buf in[] = {{x, bt * g.C_ch * es, 16},
                     {z, bt * g.H_v * g.D * es, 16},
                     {gl, bt * g.H_v * 4, 4},
                     {beta, bt * g.H_v * 4, 4},
                     {conv_w, static_cast<size_t>(g.C_ch) * g.W * es, es}};
-  const Buf out[] = {{conv_state, conv_state_bytes(g), es},
+  const Buf out[] = {{conv_state, conv_state_bytes(g), 16},
                      {rec_state, rec_state_bytes(g), 16},
                      {y, bt * g.H_v * g.D * eo, eo},
                      {ws, L.total, 16}};
@@ -303,7 +304,7 @@ static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const vo
   if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = launch_prefill_prep(g, L, gl, beta, w, x, conv_state, s);
   if (e == hipSuccess) e = tm.mark(s);
-  if (e == hipSuccess) e = launch_prefill_state(g, L, z, rec_state, y, w, s);
+  if (e == hipSuccess) e = launch_prefill_state(g, L, z, rec_state, y, w, x, conv_w, conv_state, s);
   if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = tm.elapsed();
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_prefill_chunked");

@@ -38,9 +38,13 @@ struct PrefillWs {
 };
 
 bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *ws);
-// Whether the state pass reads the dim-major copy of k from the workspace
-// (the d = 128, 64-token-chunk pass builds it in LDS instead).
-inline bool prefill_needs_kT(const Geom &g, const PrefillWs &L) { return !(g.D == 128 && L.C == 64); }
+// Whether prefill runs the split-role state pass (d = 128, 64-token chunks).
+// That pass builds the dim-major copy of k in LDS, computes v from x itself
+// and rolls the conv history of the v channels; the conv pass then writes
+// neither k dim-major nor v, and the prep pass rolls the q and k channels only.
+__host__ __device__ inline bool prefill_split_roles(const Geom &g, const PrefillWs &L) {
+  return g.D == 128 && L.C == 64;
+}
 size_t decode_ws_bytes(const Geom &g);
 
 // Kernel launchers (enqueue only; return the launch status).
@@ -56,7 +60,9 @@ hipError_t launch_decode(const Geom &g, const float *qkv, const void *z, const f
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
                                const float *beta, char *ws, const void *x, void *hist,
                                hipStream_t s);
+// x, conv_w and hist are used by the split-role pass (v and its history).
 hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z, float *S,
-                                void *y, const char *ws, hipStream_t s);
+                                void *y, const char *ws, const void *x, const void *conv_w,
+                                void *hist, hipStream_t s);
 
 }  // namespace gdn

@@ -129,8 +129,10 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
   //    the channels per key head): the conv pass, its only reader, has
   //    finished before this kernel starts.
   if (chunk == 0) {
-    const int per = (g.C_ch + g.H_k - 1) / g.H_k;
-    const int c0 = kh * per, c1 = c0 + per < g.C_ch ? c0 + per : g.C_ch;
+    // With the split-role state pass, that pass rolls the v channels itself.
+    const int nroll = prefill_split_roles(g, L) ? 2 * g.H_k * g.D : g.C_ch;
+    const int per = (nroll + g.H_k - 1) / g.H_k;
+    const int c0 = kh * per, c1 = c0 + per < nroll ? c0 + per : nroll;
     if (g.in_dt == 0)
       roll_history(g.C_ch, L.T, b, c0, c1, static_cast<const uint32_t *>(x), static_cast<uint32_t *>(hist));
     else
@@ -830,6 +832,13 @@ struct StateKernelWS {
 
   static constexpr int KTS = C + 8;  // row stride of the dim-major K copy (padded)
 
+  // x as stored (raw input bits: fp32 or bf16), for V computed in the pass.
+  using XE = typename std::conditional<DTZ == 0, uint32_t, uint16_t>::type;
+  static constexpr int XR = C + 3;                        // tile rows: tokens -3 .. C-1 of a chunk
+  static constexpr int XPR = ROWS * sizeof(XE) / 16;      // 16-byte pieces per tile row
+  static constexpr int XPIECES = XR * XPR;
+  static constexpr int XK = (XPIECES + 255) / 256;        // pieces per output-wave lane
+
   struct Smem {
     u16x8 Sh[NS][NB][64], Sl[NS][NB][64];  // state as split B operands, one d_k step each
     // K of the chunk, dim-major (row d_k, tokens in permuted K order), hi
@@ -840,6 +849,9 @@ struct StateKernelWS {
     Split4 U[NT][NB][64];
     Split4 DU[NT][NB][64];
     uint4 z[NT][16 * ZL];                  // per output wave: one token tile of z
+    // x of the block's 32 v channels for a chunk and the three tokens before
+    // it, double-buffered by chunk parity (staged by the output waves).
+    alignas(16) XE XT[2][XR][ROWS];
   };
 
   // Gate factors of the owned tile.  Lane (c, g) holds the factor of token
@@ -851,7 +863,6 @@ struct StateKernelWS {
 
   struct ChainOps {
     u16x8 kh[NS], kl[NS];              // K of the owned tile, A operand per d_k step
-    float4 v[NB];                      // V of the owned tile (D-register order)
     Gates g;
     u16x8 tm[KSC];                     // (I+A)^{-1} rows of the owned tile
   };
@@ -866,14 +877,17 @@ struct StateKernelWS {
   struct Ctx {
     const char *ktok_hi, *ktok_lo, *qtok_hi, *qtok_lo;  // slice 0 of this key head
     size_t slice_bytes;                                  // T_pad * 32 * 2
-    const float *vT;
+    const char *xv;    // x at (b, token 0, the block's first v channel)
+    const char *hv;    // conv history at (b, row 0, the block's first v channel)
+    const void *w;     // conv weights at the block's first v channel
+    size_t xrow;       // bytes per token row of x (and of the history)
     const uint16_t *Tm, *Ph, *Pl;
     const float *gates;
     const void *z;
     void *y;
     int64_t T;
     int H_v, NC, m, lane, gq;
-    uint32_t o_tok, o_v, o_mat, o_zy, o_gate;
+    uint32_t o_tok, o_mat, o_zy, o_gate;
   };
 
   static __device__ __forceinline__ int valid_of(const Ctx &x, int chunk) {
@@ -906,11 +920,83 @@ struct StateKernelWS {
     }
   }
 
-  static __device__ __forceinline__ void load_v(const Ctx &x, int chunk, ChainOps &o) {
-    const float *base = x.vT + static_cast<size_t>(chunk) * C * D;
-#pragma unroll
-    for (int n = 0; n < NB; ++n) o.v[n] = ldb<float4>(base, x.o_v + n * 16 * 16 * 4);
+  // ---- V from x in the pass.  The output waves stage the x tile of chunk
+  // c + 1 (tokens -3 .. C-1 relative to it, the block's 32 v channels) in
+  // phase 2 of chunk c; the chain waves apply the width-4 conv and SiLU to it
+  // in phase 3, beside the state update, with the same operations as the conv
+  // pass (so V is the same to the bit), and carry it into chunk c + 1.
+  static __device__ __forceinline__ float xval(XE r) {
+    if constexpr (DTZ == 0)
+      return __uint_as_float(r);
+    else
+      return bf16_bits_to_f32(r);
   }
+
+  // Loads of the x tile of `chunk` (stored for chunks >= 1 only, whose rows
+  // are all tokens >= 0); rows past the sequence end re-read its last row
+  // (zeroed when stored), and token rows before 0 re-read row 0 (such a tile,
+  // of the first chunk, is never stored: it comes from stage_first_xtile).
+  static __device__ __forceinline__ void load_xtile(const Ctx &x, int chunk, int olane,
+                                                    uint4 (&xr)[XK]) {
+#pragma unroll
+    for (int k = 0; k < XK; ++k) {
+      int piece = olane + 256 * k;
+      piece = piece < XPIECES ? piece : XPIECES - 1;
+      const int row = piece / XPR, part = piece % XPR;
+      int64_t tok = static_cast<int64_t>(chunk) * C - 3 + row;
+      tok = tok < x.T ? tok : x.T - 1;
+      tok = tok > 0 ? tok : 0;
+      xr[k] = ldb<uint4>(x.xv + static_cast<size_t>(tok) * x.xrow, part * 16);
+    }
+  }
+
+  static __device__ __forceinline__ void store_xtile(const Ctx &x, Smem &sm, int chunk,
+                                                     int olane, const uint4 (&xr)[XK]) {
+#pragma unroll
+    for (int k = 0; k < XK; ++k) {
+      const int piece = olane + 256 * k;
+      if (piece < XPIECES) {
+        const int row = piece / XPR, part = piece % XPR;
+        const int64_t tok = static_cast<int64_t>(chunk) * C - 3 + row;
+        // A mask rather than a select of two vectors (which the compiler
+        // lowers to a stack slot).
+        const uint32_t keep = tok < x.T ? 0xffffffffu : 0u;
+        const uint4 v = make_uint4(xr[k].x & keep, xr[k].y & keep, xr[k].z & keep, xr[k].w & keep);
+        *reinterpret_cast<uint4 *>(&sm.XT[chunk & 1][row][part * 16 / sizeof(XE)]) = v;
+      }
+    }
+  }
+
+  // The first chunk's tile: its three leading rows come from the history.
+  static __device__ __forceinline__ void stage_first_xtile(const Ctx &x, Smem &sm, int olane) {
+    for (int piece = olane; piece < XPIECES; piece += 256) {
+      const int row = piece / XPR, part = piece % XPR;
+      const int tok = row - 3;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (tok < 0)
+        v = ldb<uint4>(x.hv + static_cast<size_t>(3 + tok) * x.xrow, part * 16);
+      else if (tok < x.T)
+        v = ldb<uint4>(x.xv + static_cast<size_t>(tok) * x.xrow, part * 16);
+      *reinterpret_cast<uint4 *>(&sm.XT[0][row][part * 16 / sizeof(XE)]) = v;
+    }
+  }
+
+  // V of the owned tile, D-register order: lane (c, g) gets channel row
+  // 16 n + c for tokens 16 m + 4 g + r, r = 0..3 (tile rows 16 m + 4 g + r .. + 3).
+  static __device__ __forceinline__ float4 v_tile(const Smem &sm, int buf, int m, int gq, int row,
+                                                  const float (&w)[4]) {
+    const int t0 = 16 * m + 4 * gq;
+    float xs[7];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) xs[i] = xval(sm.XT[buf][t0 + i][row]);
+    float4 v;
+    v.x = siluf_(conv4(w[0], w[1], w[2], w[3], xs[0], xs[1], xs[2], xs[3]));
+    v.y = siluf_(conv4(w[0], w[1], w[2], w[3], xs[1], xs[2], xs[3], xs[4]));
+    v.z = siluf_(conv4(w[0], w[1], w[2], w[3], xs[2], xs[3], xs[4], xs[5]));
+    v.w = siluf_(conv4(w[0], w[1], w[2], w[3], xs[3], xs[4], xs[5], xs[6]));
+    return v;
+  }
+
 
   // Lane r of each group of four lanes to all four (DPP quad_perm r,r,r,r).
   template <int R>
@@ -983,16 +1069,23 @@ struct StateKernelWS {
       }
 #pragma unroll
     for (int n = 0; n < NB; ++n) pack_split(st[n][0], st[n][1], sm.Sh[w][n][lane], sm.Sl[w][n][lane]);
+    // Conv weights of the two v channels this lane turns into V.
+    float wv[NB][4];
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) wv[n][k] = load_elem<DTZ>(x.w, (16 * n + (lane & 15)) * 4 + k);
     ChainOps o;
+    float4 vc[NB];  // V of the current chunk, from the staged x tile
     o.g = load_gates(x, 0);
     asm volatile("" ::: "memory");
     load_tok(x.ktok_hi, x.ktok_lo, x, 0, o.kh, o.kl);
     asm volatile("" ::: "memory");
-    load_v(x, 0, o);
-    asm volatile("" ::: "memory");
     load_rows(x.Tm, x, 0, o.tm);
     asm volatile("" ::: "memory");
     __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NB; ++n) vc[n] = v_tile(sm, 0, m, x.gq, 16 * n + (lane & 15), wv[n]);
     // Row of the owned tile's tokens in the dim-major copy.
     const int t_own = 16 * m + (lane & 15);
     const int t_slot = 32 * (t_own >> 5) + kslot(t_own & 31);
@@ -1030,13 +1123,12 @@ struct StateKernelWS {
       load_tok(x.ktok_hi, x.ktok_lo, x, next, o.kh, o.kl);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const float4 vv = o.v[n];
+        const float4 vv = vc[n];
         const float4 bt = quad4(o.g.bt), ga = quad4(o.g.gam);
         const f32x4 r = {bt.x * (vv.x - ga.x * ks[n][0]), bt.y * (vv.y - ga.y * ks[n][1]),
                          bt.z * (vv.z - ga.z * ks[n][2]), bt.w * (vv.w - ga.w * ks[n][3])};
         sm.R[m][n][lane] = split4(r);
       }
-      load_v(x, next, o);
       __syncthreads();
 
       // 2. U = Tm R for the owned tile, and its decayed copy for the update.
@@ -1058,7 +1150,10 @@ struct StateKernelWS {
       load_rows(x.Tm, x, next, o.tm);
       __syncthreads();
 
-      // 3. S^T <- gamma_last S^T + K^T DU over the owned d_k slice.
+      // 3. S^T <- gamma_last S^T + K^T DU over the owned d_k slice, and V of
+      //    the next chunk from its x tile (staged in phase 2).
+#pragma unroll
+      for (int n = 0; n < NB; ++n) vc[n] = v_tile(sm, next & 1, m, x.gq, 16 * n + (lane & 15), wv[n]);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
 #pragma unroll
@@ -1092,7 +1187,11 @@ struct StateKernelWS {
 
   static __device__ void output(const Ctx &x, Smem &sm) {
     const int lane = x.lane, m = x.m, gq = x.gq, c = lane & 15;
+    const int olane = 64 * m + lane;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    stage_first_xtile(x, sm, olane);
+    uint4 xr[XK];  // x tile of the chunk after next, in flight
+    load_xtile(x, x.NC > 1 ? 1 : 0, olane, xr);
     OutOps o;
     load_tok(x.qtok_hi, x.qtok_lo, x, 0, o.qh, o.ql);
     asm volatile("" ::: "memory");
@@ -1155,7 +1254,13 @@ struct StateKernelWS {
           }
         asm volatile("" ::: "memory");
       }
-      if (!kLast) load_z(x, next, o);
+      if (!kLast) {
+        load_z(x, next, o);
+        // The next chunk's x tile, for the chain waves' phase 3; then the
+        // one after it (the last chunk's tile stands in past the end).
+        store_xtile(x, sm, next, olane, xr);
+        load_xtile(x, next + 1 < x.NC ? next + 1 : next, olane, xr);
+      }
       __syncthreads();
 
       // 3. O = gamma QS + P U, gated, stored.
@@ -1205,6 +1310,17 @@ struct StateKernelWS {
       for (int chunk = 1; chunk + 1 < x.NC; ++chunk) step(chunk, std::false_type{});
     }
     step(x.NC - 1, std::true_type{});
+    // Conv history of the block's v channels after the sequence: the last
+    // three rows of concat(history, x), still in the last chunk's tile.  This
+    // block alone reads and writes these channels' history.
+    if (m == 0 && lane < ROWS) {
+      const int last = x.NC - 1;
+      const int row0 = static_cast<int>(x.T - static_cast<int64_t>(last) * C);
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        *reinterpret_cast<XE *>(const_cast<char *>(x.hv) + r * x.xrow + lane * sizeof(XE)) =
+            sm.XT[last & 1][row0 + r][lane];
+    }
   }
 };
 
@@ -1213,7 +1329,10 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
                                                        const void *__restrict__ z,
                                                        float *__restrict__ S,
                                                        void *__restrict__ y,
-                                                       const char *__restrict__ ws) {
+                                                       const char *__restrict__ ws,
+                                                       const void *__restrict__ xin,
+                                                       const void *__restrict__ conv_w,
+                                                       void *__restrict__ hist) {
   using K = StateKernelWS<DTZ, DTY>;
   constexpr int D = K::D, C = K::C, Cp = K::Cp, ROWS = K::ROWS;
   __shared__ typename K::Smem sm;
@@ -1236,7 +1355,11 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   x.qtok_hi = ws + L.q_hi + slice0;
   x.qtok_lo = ws + L.q_lo + slice0;
   x.slice_bytes = static_cast<size_t>(L.T_pad) * 32 * 2;
-  x.vT = reinterpret_cast<const float *>(ws + L.vT) + (static_cast<size_t>(b) * g.H_v + h) * L.T_pad * D;
+  const int v_ch0 = 2 * g.H_k * D + h * D + ROWS * rb;  // first conv channel of the block's rows
+  x.xrow = static_cast<size_t>(g.C_ch) * sizeof(typename K::XE);
+  x.xv = static_cast<const char *>(xin) + (static_cast<size_t>(b) * L.T * g.C_ch + v_ch0) * sizeof(typename K::XE);
+  x.hv = static_cast<const char *>(hist) + (static_cast<size_t>(b) * 3 * g.C_ch + v_ch0) * sizeof(typename K::XE);
+  x.w = static_cast<const char *>(conv_w) + static_cast<size_t>(v_ch0) * 4 * sizeof(typename K::XE);
   const size_t mat = (static_cast<size_t>(b) * g.H_v + h) * L.NC * C * Cp;
   x.Tm = reinterpret_cast<const uint16_t *>(ws + L.Tm) + mat;
   x.Ph = reinterpret_cast<const uint16_t *>(ws + L.P_hi) + mat;
@@ -1252,7 +1375,6 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   x.lane = lane;
   x.gq = gq;
   x.o_tok = ((16 * x.m + c) * 32 + 8 * gq) * 2;
-  x.o_v = ((ROWS * rb + c) * 16 + 4 * gq) * 4 + x.m * 16 * D * 4;
   x.o_mat = ((16 * x.m + c) * Cp + 8 * gq) * 2;
   x.o_zy = 4 * gq * g.H_v * D + c;
   x.o_gate = (16 * x.m + 4 * gq + (lane & 3)) * 4;
@@ -1294,19 +1416,23 @@ hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *g
 
 template <int D, int C>
 static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, float *S, void *y,
-                           const char *ws, hipStream_t s) {
+                           const char *ws, const void *x, const void *cw, void *hist,
+                           hipStream_t s) {
   if constexpr (D == 128 && C == 64) {
     dim3 grid(g.B * g.H_v * (D / StateKernelWS<0, 0>::ROWS));
     dim3 block(StateKernelWS<0, 0>::kThreads);
     const int key = (g.in_dt << 1) | g.out_dt;
     switch (key) {
-      case 0: hipLaunchKernelGGL((state_kernel_ws<0, 0>), grid, block, 0, s, g, L, z, S, y, ws); break;
-      case 1: hipLaunchKernelGGL((state_kernel_ws<0, 1>), grid, block, 0, s, g, L, z, S, y, ws); break;
-      case 2: hipLaunchKernelGGL((state_kernel_ws<1, 0>), grid, block, 0, s, g, L, z, S, y, ws); break;
-      default: hipLaunchKernelGGL((state_kernel_ws<1, 1>), grid, block, 0, s, g, L, z, S, y, ws); break;
+      case 0: hipLaunchKernelGGL((state_kernel_ws<0, 0>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist); break;
+      case 1: hipLaunchKernelGGL((state_kernel_ws<0, 1>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist); break;
+      case 2: hipLaunchKernelGGL((state_kernel_ws<1, 0>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist); break;
+      default: hipLaunchKernelGGL((state_kernel_ws<1, 1>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist); break;
     }
     return;
   }
+  (void)x;
+  (void)cw;
+  (void)hist;
   dim3 grid(g.B * g.H_v * (D / StateShape<D, C>::ROWS));
   dim3 block(StateShape<D, C>::NWV * 64);
   const int key = (g.in_dt << 1) | g.out_dt;
@@ -1319,13 +1445,14 @@ static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, flo
 }
 
 hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z, float *S,
-                                void *y, const char *ws, hipStream_t s) {
-#define GDN_STATE(Dv)                                                 \
-  switch (L.C) {                                                      \
-    case 16: launch_state_t<Dv, 16>(g, L, z, S, y, ws, s); break;     \
-    case 32: launch_state_t<Dv, 32>(g, L, z, S, y, ws, s); break;     \
-    case 64: launch_state_t<Dv, 64>(g, L, z, S, y, ws, s); break;     \
-    default: launch_state_t<Dv, 128>(g, L, z, S, y, ws, s); break;    \
+                                void *y, const char *ws, const void *x, const void *conv_w,
+                                void *hist, hipStream_t s) {
+#define GDN_STATE(Dv)                                                                   \
+  switch (L.C) {                                                                        \
+    case 16: launch_state_t<Dv, 16>(g, L, z, S, y, ws, x, conv_w, hist, s); break;     \
+    case 32: launch_state_t<Dv, 32>(g, L, z, S, y, ws, x, conv_w, hist, s); break;     \
+    case 64: launch_state_t<Dv, 64>(g, L, z, S, y, ws, x, conv_w, hist, s); break;     \
+    default: launch_state_t<Dv, 128>(g, L, z, S, y, ws, x, conv_w, hist, s); break;    \
   }
   if (g.D == 128) {
     GDN_STATE(128)

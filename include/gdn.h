@@ -35,8 +35,9 @@
  *      rec_state  [B][H_v][d_v][d_k]  fp32; o = S q
  *      y          [B][T][H_v][d_v]    out_dtype
  *  - Device pointers are device memory of the current HIP device, aligned to
- *    their element size; rec_state, the workspace and the prefill z 16-byte
- *    aligned.  The
+ *    their element size; rec_state, the workspaces, and the prefill x, z and
+ *    conv_state 16-byte aligned (every token offset of a 16-byte aligned x
+ *    stays 16-byte aligned).  The
  *    caller owns every buffer; the library allocates nothing,
  *    keeps no state between calls and is safe to call from several threads.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Compute calls

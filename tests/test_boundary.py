@@ -136,6 +136,8 @@ def test_prefill_rejects_and_leaves_buffers_untouched(lib, dims):
         (dict(S=b.p("S", 4)), ALIGN),          # state must be 16-byte aligned
         (dict(ws=b.p("ws", 8)), ALIGN),
         (dict(x=b.p("x", 1)), ALIGN),          # bf16 input at an odd address
+        (dict(x=b.p("x", 2)), ALIGN),          # prefill x must be 16-byte aligned
+        (dict(hist=b.p("hist", 2)), ALIGN),    # and so must the conv history
         (dict(y=b.p("x")), ALIAS),             # output over an input
         (dict(ws=b.p("S")), ALIAS),            # workspace over the state
         (dict(hist=b.p("S")), ALIAS),          # conv state over the recurrent state
