@@ -20,7 +20,10 @@ namespace gdn {
 constexpr int kConvThreads = 128;  // channels per block
 constexpr int kConvTT = 32;        // tokens per block
 
-enum { kOutPlain = 0, kOutPrefill = 1 };
+// kOutPrefillQK: the prefill layout for the q and k channels only, without
+// the dim-major k copy (so without the LDS staging buffer, which would cap
+// the blocks per CU).
+enum { kOutPlain = 0, kOutPrefill = 1, kOutPrefillQK = 2 };
 
 struct ConvArgs {
   const void *x;
@@ -130,12 +133,16 @@ __device__ __forceinline__ void head_scale_128x32(float (&ss)[32], float eps, fl
 // loads are in flight together; the per-channel outputs stay in registers,
 // which makes the dim-major workspace rows contiguous per thread.
 template <int DT, int D, int MODE, int TT>
-__global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) {
+__global__ __launch_bounds__(kConvThreads, (MODE == kOutPrefillQK && D == 128 ? 8 : 1)) void conv_kernel(Geom g, ConvArgs a) {
   __shared__ float red[2][kConvTT];
   __shared__ float bc[2][kConvTT];
-  const int ch = blockIdx.y * kConvThreads + threadIdx.x;
+  // One grid dimension over (tile, channel block), channel block fastest: the
+  // blocks in flight together read whole token rows of x.
+  const int nchb = (MODE == kOutPrefillQK ? 2 * g.H_k * D : g.C_ch + kConvThreads - 1) / kConvThreads;
+  const int cb = static_cast<int>(blockIdx.x % nchb);
+  const int ch = cb * kConvThreads + threadIdx.x;
   const int b = blockIdx.z;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TT;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x / nchb) * TT;
   const bool active = ch < g.C_ch;
   // Lanes past the last channel load a valid channel and drop their results,
   // so every load below is unconditional per lane.
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
   const int nq = g.H_k * D;
   const int nqk = 2 * nq;
   // For D = 128 a block is exactly one head: the kind is uniform per block.
-  const int head0 = (D == 128) ? static_cast<int>(blockIdx.y) * kConvThreads : ch;
+  const int head0 = (D == 128) ? cb * kConvThreads : ch;
   const bool is_q = head0 < nq;
   const bool is_k = !is_q && head0 < nqk;
   const bool qk_block = (D == 128) ? (is_q || is_k) : true;
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
   } else if constexpr (TT == kConvTT) {
     const PrefillWs &L = a.L;
     // 16 KB: one head's dim-major block (v: 2 x 16 tokens fp32; k: hi and lo).
-    __shared__ uint4 stage[D == kConvThreads ? 1024 : 1];
+    __shared__ uint4 stage[(D == kConvThreads && MODE == kOutPrefill) ? 1024 : 1];
     const int j = ch % D;
     if (is_q || is_k) {
       const int kh = (is_q ? ch : ch - nq) / D;
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
           plo[(row0 + t) * 32 + kslot(j + 16)] = 0;
         }
       }
-      if (is_k && a.write_kT) {
+      if (MODE == kOutPrefill && is_k && a.write_kT) {
         // Dim-major row of this channel: 32 tokens in permuted K order.
         u16x8 rh[4], rl[4];
 #pragma unroll
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
           }
         }
       }
-    } else {
+    } else if constexpr (MODE == kOutPrefill) {
       const int h = (ch - nqk) / D;
       if constexpr (D == kConvThreads) {
         // Both 16-token blocks of the head are one contiguous 16 KB run:
@@ -322,6 +329,121 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(Geom g, ConvArgs a) 
                                  val[16 * half + 4 * q + 2], val[16 * half + 4 * q + 3]);
         }
       }
+    }
+  }
+}
+
+// Prefill conv of the q and k channels at d = 128, one head per block, for
+// NTL consecutive 32-token tiles: the next tile's inputs are loaded while the
+// current tile is computed and stored, so the loads, arithmetic and stores of
+// different tiles overlap inside every wave (with one tile per block all
+// waves run the three phases in lockstep).  Same arithmetic and outputs as
+// conv_kernel's prefill layout.
+template <int DT, int NTL>
+__global__ __launch_bounds__(kConvThreads) void conv_qk_kernel(Geom g, ConvArgs a) {
+  constexpr int TT = kConvTT, D = 128;
+  __shared__ float red[2][kConvTT];
+  __shared__ float bc[2][kConvTT];
+  const PrefillWs &L = a.L;
+  // One grid dimension over (tile group, head), head fastest: the blocks in
+  // flight together read whole token rows of x (each block 256 bytes of a row).
+  const int nheads = 2 * g.H_k;
+  const int hd = static_cast<int>(blockIdx.x % nheads);
+  const int ch = hd * kConvThreads + threadIdx.x;  // a q or k channel
+  const int b = blockIdx.z;
+  const int nq = g.H_k * D;
+  const bool is_q = hd < g.H_k;  // uniform
+  const int kh = (is_q ? ch : ch - nq) / D;
+  const int j = ch % D;
+  const float sc = is_q ? g.q_scale : 1.0f;
+  constexpr int ES = DT == 0 ? 4 : 2;
+  const size_t rowb = static_cast<size_t>(g.C_ch) * ES;
+  const uint32_t lane_off = static_cast<uint32_t>(ch) * ES;
+  auto ld = [&](const char *row_base) -> float {
+    if constexpr (DT == 0)
+      return *reinterpret_cast<const float *>(row_base + lane_off);
+    else
+      return bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(row_base + lane_off));
+  };
+  const float w0 = load_elem<DT>(a.w, static_cast<size_t>(ch) * 4 + 0);
+  const float w1 = load_elem<DT>(a.w, static_cast<size_t>(ch) * 4 + 1);
+  const float w2 = load_elem<DT>(a.w, static_cast<size_t>(ch) * 4 + 2);
+  const float w3 = load_elem<DT>(a.w, static_cast<size_t>(ch) * 4 + 3);
+  const char *xb = static_cast<const char *>(a.x) + static_cast<size_t>(b) * a.T * rowb;
+  const char *hb = static_cast<const char *>(a.hist) + static_cast<size_t>(b) * 3 * rowb;
+  auto load_tile = [&](int64_t t0, float (&xv)[TT + 3]) {
+    if (t0 >= 3 && t0 + TT <= a.T) {
+      const char *r0 = xb + static_cast<size_t>(t0 - 3) * rowb;
+#pragma unroll
+      for (int i = 0; i < TT + 3; ++i) xv[i] = ld(r0 + i * rowb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TT + 3; ++i) {
+        const int64_t tau = t0 - 3 + i;  // uniform per block
+        float v = 0.f;
+        if (tau < 0)
+          v = ld(hb + static_cast<size_t>(3 + tau) * rowb);
+        else if (tau < a.T)
+          v = ld(xb + static_cast<size_t>(tau) * rowb);
+        xv[i] = v;
+      }
+    }
+  };
+  uint16_t *phi = reinterpret_cast<uint16_t *>(a.ws + (is_q ? L.q_hi : L.k_hi));
+  uint16_t *plo = reinterpret_cast<uint16_t *>(a.ws + (is_q ? L.q_lo : L.k_lo));
+  // Slice 0 of this head: [b][kh][slice][T_pad][32] token-major layout.
+  const size_t slice0 = (static_cast<size_t>(b) * g.H_k + kh) * (L.Dp / 32) * L.T_pad;
+  const int pos = kslot(j & 31);
+  __shared__ __attribute__((aligned(16))) uint16_t stage[2][4][TT][32];
+  const int64_t first = static_cast<int64_t>(blockIdx.x / nheads) * NTL * TT;
+  const int64_t last_t0 = a.T_iter - TT;  // last tile of the sequence
+  float xa[TT + 3];
+  load_tile(first, xa);
+#pragma unroll
+  for (int it = 0; it < NTL; ++it) {
+    const int64_t t0 = first + it * TT;
+    if (t0 > last_t0) break;  // uniform: the grid's last block may hold fewer tiles
+    float xn[TT + 3];
+    if (it + 1 < NTL) load_tile(t0 + TT <= last_t0 ? t0 + TT : t0, xn);
+    float val[TT], ss[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      val[t] = siluf_(conv4(w0, w1, w2, w3, xa[t], xa[t + 1], xa[t + 2], xa[t + 3]));
+      ss[t] = val[t] * val[t];
+    }
+    head_scale_128x32(ss, g.eps, sc, red, bc);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) val[t] *= ss[t];
+    if (t0 + TT > a.T) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        if (t0 + t >= a.T) val[t] = 0.f;  // padding tokens of the prefill layout
+    }
+    // The head's token-major output for the tile is four 2 KB runs (one per
+    // 32-channel slice) for hi and for lo: gather them in LDS, then write
+    // 16-byte pieces (eight store instructions per thread instead of 64).
+#pragma unroll
+    for (int t = 0; t < TT; t += 2) {
+      uint32_t h2, l2;
+      split2(val[t], val[t + 1], h2, l2);
+      stage[0][j >> 5][t][pos] = static_cast<uint16_t>(h2);
+      stage[0][j >> 5][t + 1][pos] = static_cast<uint16_t>(h2 >> 16);
+      stage[1][j >> 5][t][pos] = static_cast<uint16_t>(l2);
+      stage[1][j >> 5][t + 1][pos] = static_cast<uint16_t>(l2 >> 16);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int piece = threadIdx.x + kConvThreads * u;  // 16-byte piece of the 16 KB
+      const int hl = piece >> 9, sl = (piece >> 7) & 3, tok = (piece >> 2) & 31, part = piece & 3;
+      uint16_t *dst = (hl ? plo : phi) + ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 8 * part);
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stage[hl][sl][tok][8 * part]);
+    }
+    if (it + 1 < NTL) {
+      // red, bc and stage are reused by the next tile.
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < TT + 3; ++i) xa[i] = xn[i];
     }
   }
 }
@@ -421,8 +543,8 @@ template <int MODE, int TT>
 static hipError_t launch_conv(const Geom &g, const ConvArgs &a, hipStream_t s) {
   const int64_t tiles = (a.T_iter + TT - 1) / TT;
   // Without v the grid covers the q and k channels only (whole heads at d = 128).
-  const int chans = (MODE == kOutPrefill && !a.write_v) ? 2 * g.H_k * g.D : g.C_ch;
-  dim3 grid(static_cast<unsigned>(tiles), (chans + kConvThreads - 1) / kConvThreads, g.B);
+  const int chans = (MODE == kOutPrefillQK) ? 2 * g.H_k * g.D : g.C_ch;
+  dim3 grid(static_cast<unsigned>(tiles * ((chans + kConvThreads - 1) / kConvThreads)), 1, g.B);
   dim3 block(kConvThreads);
   if (g.D == 128) {
     if (g.in_dt == 0)
@@ -480,7 +602,16 @@ hipError_t launch_conv_prefill(const Geom &g, const PrefillWs &L, const void *x,
   a.fuse_roll = 0;
   a.write_kT = !prefill_split_roles(g, L);
   a.write_v = !prefill_split_roles(g, L);
-  return launch_conv<kOutPrefill, kConvTT>(g, a, s);
+  if (a.write_v) return launch_conv<kOutPrefill, kConvTT>(g, a, s);
+  // q and k only (the split-role state pass computes v): d = 128.
+  constexpr int NTL = 1;
+  const int64_t tiles = a.T_iter / kConvTT;
+  dim3 grid(static_cast<unsigned>(2 * g.H_k * ((tiles + NTL - 1) / NTL)), 1, g.B);
+  if (g.in_dt == 0)
+    hipLaunchKernelGGL((conv_qk_kernel<0, NTL>), grid, dim3(kConvThreads), 0, s, g, a);
+  else
+    hipLaunchKernelGGL((conv_qk_kernel<1, NTL>), grid, dim3(kConvThreads), 0, s, g, a);
+  return hipGetLastError();
 }
 
 }  // namespace gdn
