@@ -240,47 +240,55 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
     }
     __syncthreads();
     if constexpr (NT > 1) {
-      constexpr int NY = NT * (NT - 1) / 2;
-      float y[NY];
+      // 16 x 16 x 16 fp32 products on the fp32 MFMA, one wave per output
+      // block.  v_mfma_f32_16x16x4_f32: lane (c, g) supplies A[c][k] and
+      // B[k][c] of one 4-wide K step and holds D[4g + r][c].  The K index of
+      // step s for lane group g is 4g + s, so a lane's A values of all four
+      // steps are one contiguous row piece.
+      const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      const int c = lane & 15, g4 = lane >> 4;
+      auto prod = [&](const float *A, const float *Bm, f32x4 acc) {
+        const float4 av = *reinterpret_cast<const float4 *>(A + c * 16 + 4 * g4);
+        const float a4[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[st], Bm[(4 * g4 + st) * 16 + c], acc, 0, 0, 0);
+        return acc;
+      };
+      // (c) Y_ik = X_ii A_ik, in place: only the wave that forms Y_ik reads A_ik.
 #pragma unroll
       for (int i = 1, q = 0; i < NT; ++i)
 #pragma unroll
-        for (int k = 0; k < i; ++k, ++q) {
-          const float *Xi = TI[tri_index(i, i)];
-          const float *Aik = TI[tri_index(i, k)];
-          float acc = 0.f;
+        for (int k = 0; k < i; ++k, ++q)
+          if (q % 4 == wave) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 y = prod(TI[tri_index(i, i)], TI[tri_index(i, k)], zero);
+            float *dst = TI[tri_index(i, k)];
 #pragma unroll
-          for (int m = 0; m < 16; ++m) acc = __builtin_fmaf(Xi[r16 * 16 + m], Aik[m * 16 + c16], acc);
-          y[q] = acc;
-          // One 16-term product at a time: keeps the LDS reads of the next
-          // product from being hoisted into registers all at once.
-          asm volatile("" ::: "memory");
-        }
-      __syncthreads();
-#pragma unroll
-      for (int i = 1, q = 0; i < NT; ++i)
-#pragma unroll
-        for (int k = 0; k < i; ++k, ++q) TI[tri_index(i, k)][threadIdx.x] = y[q];
-      // Block row i, left to right: element (r, c) of X_ij reads only row r
-      // of Y_i. (and finished rows above), and the sixteen threads of a row
-      // share one wave, so X_ij can replace Y_ij as soon as it is formed;
-      // Y_ij is not read again (later blocks of the row use k > j).
+            for (int r = 0; r < 4; ++r) dst[(4 * g4 + r) * 16 + c] = y[r];
+          }
+      // (d) block row i: X_ij = -sum_{k=j}^{i-1} Y_ik X_kj for j < i, block j
+      //     on wave j % 4; all of the row's reads precede its writes.
 #pragma unroll
       for (int i = 1; i < NT; ++i) {
         __syncthreads();
+        f32x4 xr[(NT + 2) / 4];
 #pragma unroll
-        for (int j = 0; j < i; ++j) {
-          float acc = 0.f;
+        for (int j = 0; j < i; ++j)
+          if (j % 4 == wave) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int k = j; k < i; ++k) {
-            const float *Yik = TI[tri_index(i, k)];
-            const float *Xkj = TI[tri_index(k, j)];
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc = __builtin_fmaf(Yik[r16 * 16 + m], Xkj[m * 16 + c16], acc);
-            asm volatile("" ::: "memory");
+            for (int k = j; k < i; ++k) acc = prod(TI[tri_index(i, k)], TI[tri_index(k, j)], acc);
+            xr[j / 4] = acc;
           }
-          TI[tri_index(i, j)][threadIdx.x] = -acc;
-        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < i; ++j)
+          if (j % 4 == wave) {
+            float *dst = TI[tri_index(i, j)];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(4 * g4 + r) * 16 + c] = -xr[j / 4][r];
+          }
       }
     }
     __syncthreads();
