@@ -180,10 +180,13 @@ bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *w) {
   w->q_lo = take(tok);
   w->k_hi = take(tok);
   w->k_lo = take(tok);
-  const size_t kt = static_cast<size_t>(g.B) * g.H_k * tp * g.D * 2;
+  // The split-role state pass builds the dim-major k in LDS and computes v
+  // from x: those regions are empty for it.
+  const bool split = prefill_split_roles(g, *w);
+  const size_t kt = split ? 0 : static_cast<size_t>(g.B) * g.H_k * tp * g.D * 2;
   w->kT_hi = take(kt);
   w->kT_lo = take(kt);
-  w->vT = take(static_cast<size_t>(g.B) * g.H_v * tp * g.D * 4);
+  w->vT = take(split ? 0 : static_cast<size_t>(g.B) * g.H_v * tp * g.D * 4);
   const size_t mat = static_cast<size_t>(g.B) * g.H_v * w->NC * C * w->Cp * 2;
   w->Tm = take(mat);
   w->P_hi = take(mat);

@@ -26,6 +26,7 @@ struct Geom {
 //   k dim-major       [B][H_k][T_pad/32][D][32] bf16 hi and lo, tokens in
 //                                               permuted K order
 //   v dim-major       [B][H_v][T_pad/16][D][16] fp32
+//   (both empty for the split-role pass)
 //   T = (I + A)^{-1}  [B][H_v][NC][C][Cp]      bf16, columns permuted
 //   P = tril(D) * QK^T [B][H_v][NC][C][Cp]     bf16 hi and lo, columns permuted
 //   gates             [B][H_v][NC][3][C]       fp32: gamma_t = exp(G_t),

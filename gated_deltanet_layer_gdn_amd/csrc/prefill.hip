@@ -838,7 +838,6 @@ struct StateKernelWS {
   static constexpr int ZK = (16 * ZL + 63) / 64; // pieces per lane per tile
   static constexpr int kThreads = 512;
 
-  static constexpr int KTS = C + 8;  // row stride of the dim-major K copy (padded)
 
   // x as stored (raw input bits: fp32 or bf16), for V computed in the pass.
   using XE = typename std::conditional<DTZ == 0, uint32_t, uint16_t>::type;
@@ -849,10 +848,10 @@ struct StateKernelWS {
 
   struct Smem {
     u16x8 Sh[NS][NB][64], Sl[NS][NB][64];  // state as split B operands, one d_k step each
-    // K of the chunk, dim-major (row d_k, tokens in permuted K order), hi
-    // and lo: the A operands of the state update, gathered from the chain
-    // waves' token-major tiles instead of a second copy in HBM.
-    alignas(16) uint16_t KT[2][D][KTS];
+    // K of the chunk, token-major as the chain waves hold it (d_k in the
+    // permuted K order), hi and lo, 16-byte pieces swizzled per token (see
+    // kq_piece).  The state update reads K^T from it with transposing loads.
+    alignas(16) uint16_t KQ[2][C][D];
     Split4 R[NT][NB][64];
     Split4 U[NT][NB][64];
     Split4 DU[NT][NB][64];
@@ -1006,6 +1005,36 @@ struct StateKernelWS {
   }
 
 
+  // Element offset in a token row of KQ of the 16-byte piece `piece` (0..15,
+  // d_k step piece / 4, lane group piece % 4).  The XOR spreads the sixteen
+  // tokens that one store or one transposing load touches over all banks.
+  static __device__ __forceinline__ int kq_piece(int tok, int piece) {
+    return 8 * (piece ^ (((tok >> 2) & 3) | ((tok & 3) << 2)));
+  }
+
+  // A operand K^T of the state update for d_k rows 32w + 16dt .. + 15 and
+  // tokens 32kk .. 32kk + 31 (permuted K order).  ds_read_b64_tr_b16 hands
+  // lane 4a + b of each 16-lane group element b of the 8 bytes that lanes
+  // a, a + 4, a + 8, a + 12 of the group address; so lane (a + 4j) of group
+  // g addresses d_k 32w + 16dt + 4a .. + 3 of token 32kk + 4g + j (then + 16),
+  // and lane (c, g) receives d_k row c for tokens 4g + j (then 16 + 4g + j),
+  // slots 8g .. 8g + 7.
+  static __device__ __forceinline__ u16x8 kt_operand(const uint16_t (&kq)[C][D], int kk, int w,
+                                                     int dt, int lane) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const int grp = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
+    const int t0 = 32 * kk + 4 * grp + j, t1 = t0 + 16;
+    const uint16_t *p0 = &kq[t0][kq_piece(t0, 4 * w + a) + 4 * dt];
+    const uint16_t *p1 = &kq[t1][kq_piece(t1, 4 * w + a) + 4 * dt];
+    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)(p0));
+    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)(p1));
+    const uint2 d0 = __builtin_bit_cast(uint2, r0), d1 = __builtin_bit_cast(uint2, r1);
+    const u32x4 v = {d0.x, d0.y, d1.x, d1.y};
+    return __builtin_bit_cast(u16x8, v);
+  }
+
   // Lane r of each group of four lanes to all four (DPP quad_perm r,r,r,r).
   template <int R>
   static __device__ __forceinline__ float quad_bcast(float v) {
@@ -1094,9 +1123,8 @@ struct StateKernelWS {
     __syncthreads();
 #pragma unroll
     for (int n = 0; n < NB; ++n) vc[n] = v_tile(sm, 0, m, x.gq, 16 * n + (lane & 15), wv[n]);
-    // Row of the owned tile's tokens in the dim-major copy.
+    // The owned token's row of the token-major K copy.
     const int t_own = 16 * m + (lane & 15);
-    const int t_slot = 32 * (t_own >> 5) + kslot(t_own & 31);
 
     for (int chunk = 0; chunk < x.NC; ++chunk) {
       const int next = chunk + 1 < x.NC ? chunk + 1 : chunk;
@@ -1118,16 +1146,13 @@ struct StateKernelWS {
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int n = 0; n < NB; ++n) ks[n] = mfma_split3(o.kh[s], o.kl[s], bh[s][n], bl[s][n], ks[n]);
-      // The owned K tile into the dim-major copy: slot 8g + i of d_k step s
-      // holds d_k = 32 s + (4g + i, or 16 + 4g + i - 4 for i >= 4).
+      // The owned K tile into the token-major copy, as held.
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int dk = 32 * s + (i < 4 ? 4 * x.gq + i : 16 + 4 * x.gq + i - 4);
-          sm.KT[0][dk][t_slot] = o.kh[s][i];
-          sm.KT[1][dk][t_slot] = o.kl[s][i];
-        }
+      for (int s = 0; s < NS; ++s) {
+        const int off = kq_piece(t_own, 4 * s + x.gq);
+        *reinterpret_cast<u16x8 *>(&sm.KQ[0][t_own][off]) = o.kh[s];
+        *reinterpret_cast<u16x8 *>(&sm.KQ[1][t_own][off]) = o.kl[s];
+      }
       load_tok(x.ktok_hi, x.ktok_lo, x, next, o.kh, o.kl);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
@@ -1162,6 +1187,14 @@ struct StateKernelWS {
       //    the next chunk from its x tile (staged in phase 2).
 #pragma unroll
       for (int n = 0; n < NB; ++n) vc[n] = v_tile(sm, next & 1, m, x.gq, 16 * n + (lane & 15), wv[n]);
+      u16x8 th[KSC][NDT], tl[KSC][NDT];
+#pragma unroll
+      for (int kk = 0; kk < KSC; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          th[kk][dt] = kt_operand(sm.KQ[0], kk, w, dt, lane);
+          tl[kk][dt] = kt_operand(sm.KQ[1], kk, w, dt, lane);
+        }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
 #pragma unroll
@@ -1171,12 +1204,7 @@ struct StateKernelWS {
           u16x8 bh, bl;
           operand(sm.DU[2 * kk][n][lane], sm.DU[2 * kk + 1][n][lane], bh, bl);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const int dk = 32 * w + 16 * dt + (lane & 15);
-            const u16x8 th = *reinterpret_cast<const u16x8 *>(&sm.KT[0][dk][32 * kk + 8 * x.gq]);
-            const u16x8 tl = *reinterpret_cast<const u16x8 *>(&sm.KT[1][dk][32 * kk + 8 * x.gq]);
-            st[n][dt] = mfma_split3(th, tl, bh, bl, st[n][dt]);
-          }
+          for (int dt = 0; dt < NDT; ++dt) st[n][dt] = mfma_split3(th[kk][dt], tl[kk][dt], bh, bl, st[n][dt]);
         }
       }
 #pragma unroll
