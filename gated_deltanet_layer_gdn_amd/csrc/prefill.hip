@@ -358,6 +358,14 @@ __device__ __forceinline__ V ldb(const void *base, uint32_t byte_off) {
   return *reinterpret_cast<const V *>(static_cast<const char *>(base) + byte_off);
 }
 
+// A value at a wave-uniform address through a vector load.  A scalar load
+// would share its wait counter with LDS, so every LDS wait issued while it
+// is in flight would also wait for its L2 round trip.
+__device__ __forceinline__ float ld_uniform_vec(const float *base, uint32_t byte_off) {
+  asm volatile("" : "+v"(byte_off));
+  return ldb<float>(base, byte_off);
+}
+
 // Per-chunk operands of one wave.  None of them depends on the state, so
 // each is fetched for the next chunk as soon as this chunk has consumed it
 // (into the same registers): every load has about one chunk of compute to
@@ -469,7 +477,7 @@ struct StateKernel {
       o.dl[i] = ldb<float4>(gb, x.o_gate + m * 64 + C * 4);
       o.bt[i] = ldb<float4>(gb, x.o_gate + m * 64 + 2 * C * 4);
     }
-    o.glast = ldb<float>(gb, (C - 1) * 4);
+    o.glast = ld_uniform_vec(gb, (C - 1) * 4);
   }
 
   static __device__ __forceinline__ void load_v(const Ctx &x, int chunk, Ops &o) {
@@ -865,7 +873,7 @@ struct StateKernelWS {
   // 4g + (c % 4); quad_bcast hands every lane the four of its own rows.
   struct Gates {
     float gam, bt, dl;
-    float glast;  // gamma of the chunk's last token (wave-uniform)
+    float glast;  // gamma of the chunk's last token (same in every lane)
   };
 
   struct ChainOps {
@@ -1053,7 +1061,7 @@ struct StateKernelWS {
     o.gam = ldb<float>(gb, x.o_gate);
     o.dl = ldb<float>(gb, x.o_gate + C * 4);
     o.bt = ldb<float>(gb, x.o_gate + 2 * C * 4);
-    o.glast = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gb[C - 1])));
+    o.glast = ld_uniform_vec(gb, (C - 1) * 4);
     return o;
   }
 
