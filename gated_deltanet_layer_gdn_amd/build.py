@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "conv.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["gdn_api.cpp", "conv.hip", "decode.hip", "prep.hip", "prefill.hip"]
 HEADERS = ["gdn_device.h", "gdn_internal.h"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
