@@ -390,11 +390,13 @@ __global__ __launch_bounds__(kConvThreads) void conv_qk_kernel(Geom g, ConvArgs 
     }
   };
   uint16_t *phi = reinterpret_cast<uint16_t *>(a.ws + (is_q ? L.q_hi : L.k_hi));
-  uint16_t *plo = reinterpret_cast<uint16_t *>(a.ws + (is_q ? L.q_lo : L.k_lo));
+  uint8_t *plo = reinterpret_cast<uint8_t *>(a.ws + (is_q ? L.q_lo : L.k_lo));  // e4m3 low halves
+  const float lo_scale = is_q ? L.q_lo_scale : L.k_lo_scale;
   // Slice 0 of this head: [b][kh][slice][T_pad][32] token-major layout.
   const size_t slice0 = (static_cast<size_t>(b) * g.H_k + kh) * (L.Dp / 32) * L.T_pad;
   const int pos = kslot(j & 31);
-  __shared__ __attribute__((aligned(16))) uint16_t stage[2][4][TT][32];
+  __shared__ __attribute__((aligned(16))) uint16_t stage_hi[4][TT][32];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_lo[4][TT][32];
   const int64_t first = static_cast<int64_t>(blockIdx.x / nheads) * NTL * TT;
   const int64_t last_t0 = a.T_iter - TT;  // last tile of the sequence
   float xa[TT + 3];
@@ -419,28 +421,37 @@ __global__ __launch_bounds__(kConvThreads) void conv_qk_kernel(Geom g, ConvArgs 
       for (int t = 0; t < TT; ++t)
         if (t0 + t >= a.T) val[t] = 0.f;  // padding tokens of the prefill layout
     }
-    // The head's token-major output for the tile is four 2 KB runs (one per
-    // 32-channel slice) for hi and for lo: gather them in LDS, then write
-    // 16-byte pieces (eight store instructions per thread instead of 64).
+    // The head's token-major output for the tile is four 2 KB runs of hi
+    // (bf16) and four 1 KB runs of lo (e4m3), one per 32-channel slice:
+    // gather them in LDS, then write 16-byte pieces (six store instructions
+    // per thread instead of 64).
 #pragma unroll
     for (int t = 0; t < TT; t += 2) {
-      uint32_t h2, l2;
-      split2(val[t], val[t + 1], h2, l2);
-      stage[0][j >> 5][t][pos] = static_cast<uint16_t>(h2);
-      stage[0][j >> 5][t + 1][pos] = static_cast<uint16_t>(h2 >> 16);
-      stage[1][j >> 5][t][pos] = static_cast<uint16_t>(l2);
-      stage[1][j >> 5][t + 1][pos] = static_cast<uint16_t>(l2 >> 16);
+      uint32_t h2;
+      uint16_t l2;
+      split2_lo8(val[t], val[t + 1], lo_scale, h2, l2);
+      stage_hi[j >> 5][t][pos] = static_cast<uint16_t>(h2);
+      stage_hi[j >> 5][t + 1][pos] = static_cast<uint16_t>(h2 >> 16);
+      stage_lo[j >> 5][t][pos] = static_cast<uint8_t>(l2);
+      stage_lo[j >> 5][t + 1][pos] = static_cast<uint8_t>(l2 >> 8);
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int piece = threadIdx.x + kConvThreads * u;  // 16-byte piece of the 16 KB
-      const int hl = piece >> 9, sl = (piece >> 7) & 3, tok = (piece >> 2) & 31, part = piece & 3;
-      uint16_t *dst = (hl ? plo : phi) + ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 8 * part);
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stage[hl][sl][tok][8 * part]);
+    for (int u = 0; u < 4; ++u) {
+      const int piece = threadIdx.x + kConvThreads * u;  // 16-byte piece of the 8 KB of hi
+      const int sl = piece >> 7, tok = (piece >> 2) & 31, part = piece & 3;
+      uint16_t *dst = phi + ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 8 * part);
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stage_hi[sl][tok][8 * part]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int piece = threadIdx.x + kConvThreads * u;  // 16-byte piece of the 4 KB of lo
+      const int sl = piece >> 6, tok = (piece >> 1) & 31, part = piece & 1;
+      uint8_t *dst = plo + ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 16 * part);
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stage_lo[sl][tok][16 * part]);
     }
     if (it + 1 < NTL) {
-      // red, bc and stage are reused by the next tile.
+      // red, bc and the stages are reused by the next tile.
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < TT + 3; ++i) xa[i] = xn[i];

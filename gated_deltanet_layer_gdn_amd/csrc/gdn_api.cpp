@@ -7,6 +7,8 @@
 // execution, without mutating session state).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -176,10 +178,18 @@ bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *w) {
   };
   const size_t tp = static_cast<size_t>(w->T_pad);
   const size_t tok = static_cast<size_t>(g.B) * g.H_k * tp * w->Dp * 2;
+  // The split-role pass keeps the low halves of q and k as e4m3 bytes with a
+  // power-of-two scale 2^(e - 15), where 2^e bounds the values: normalised k
+  // is at most 1 in magnitude, q at most q_scale.
+  const bool lo8 = prefill_split_roles(g, *w);
+  const float qmax = std::fabs(g.q_scale);
+  const int qe = qmax > 0.f ? std::max(-60, std::min(60, static_cast<int>(std::ceil(std::log2(qmax))))) : 0;
+  w->q_lo_scale = lo8 ? std::ldexp(1.0f, qe - 15) : 0.f;
+  w->k_lo_scale = lo8 ? std::ldexp(1.0f, -15) : 0.f;
   w->q_hi = take(tok);
-  w->q_lo = take(tok);
+  w->q_lo = take(lo8 ? tok / 2 : tok);
   w->k_hi = take(tok);
-  w->k_lo = take(tok);
+  w->k_lo = take(lo8 ? tok / 2 : tok);
   // The split-role state pass builds the dim-major k in LDS and computes v
   // from x: those regions are empty for it.
   const bool split = prefill_split_roles(g, *w);

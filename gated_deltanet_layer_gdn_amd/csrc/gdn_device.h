@@ -52,6 +52,35 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
+// The same split with the low half narrowed to fp8 (OCP e4m3): lo8 =
+// e4m3((x - hi) / scale), two bytes per pair, low element first.  With
+// |x| <= 2^e and scale = 2^(e - 15), |x - hi| / scale <= 128 stays inside
+// e4m3's range (448); hi + lo8 * scale carries about 13 significant bits.
+__device__ __forceinline__ void split2_lo8(float a, float b, float scale, uint32_t &hi,
+                                           uint16_t &lo8) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  const bf16x2 h = __builtin_convertvector(v, bf16x2);
+  const f32x2 r = v - __builtin_convertvector(h, f32x2);
+  const s16x2 zero = {0, 0};
+  const s16x2 c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero, r[0], r[1], scale, false);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo8 = static_cast<uint16_t>(__builtin_bit_cast(uint32_t, c));
+}
+
+// Eight fp8 low halves (as stored by split2_lo8) back to a bf16 operand:
+// element i = e4m3 byte i * scale, exact in bf16.
+__device__ __forceinline__ u16x8 lo8_to_bf16x8(uint2 q, float scale) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, scale, false);
+  const bf2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, scale, true);
+  const bf2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, scale, false);
+  const bf2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, scale, true);
+  const u32x4 v = {__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
+                   __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3)};
+  return __builtin_bit_cast(u16x8, v);
+}
+
 __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
   uint32_t h, l;
   split2(x, 0.f, h, l);

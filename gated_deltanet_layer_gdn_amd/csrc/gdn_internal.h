@@ -22,7 +22,10 @@ struct Geom {
 // to a multiple of Cp; NC = ceil(T / C) chunks.
 //   q/k token-major   [B][H_k][Dp/32][T_pad][32] bf16 hi and lo: each 32-wide
 //                                               slice of the head dimension in
-//                                               permuted K order, slice-major
+//                                               permuted K order, slice-major;
+//                                               for the split-role pass the lo
+//                                               halves are e4m3 bytes scaled by
+//                                               q_lo_scale / k_lo_scale
 //   k dim-major       [B][H_k][T_pad/32][D][32] bf16 hi and lo, tokens in
 //                                               permuted K order
 //   v dim-major       [B][H_v][T_pad/16][D][16] fp32
@@ -36,6 +39,8 @@ struct PrefillWs {
   int C, Cp, Dp, NC;
   size_t q_hi, q_lo, k_hi, k_lo, kT_hi, kT_lo, vT, Tm, P_hi, P_lo, gates;
   size_t total;
+  // Split-role pass: scales of the fp8 low halves of q and k (0 otherwise).
+  float q_lo_scale, k_lo_scale;
 };
 
 bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *ws);

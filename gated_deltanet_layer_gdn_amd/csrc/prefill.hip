@@ -586,13 +586,15 @@ struct StateKernelWS {
   };
 
   struct ChainOps {
-    u16x8 kh[NS], kl[NS];              // K of the owned tile, A operand per d_k step
+    u16x8 kh[NS];                      // K of the owned tile, A operand per d_k step
+    uint2 kl8[NS];                     // its low halves, e4m3
     Gates g;
     u16x8 tm[KSC];                     // (I+A)^{-1} rows of the owned tile
   };
 
   struct OutOps {
-    u16x8 qh[NS], ql[NS];  // Q of the owned tile
+    u16x8 qh[NS];          // Q of the owned tile
+    uint2 ql8[NS];         // its low halves, e4m3
     float gam;             // gamma of token 4g + (c % 4), as in Gates
     u16x8 ph[KSC], pl[KSC];
     uint4 z[ZK];
@@ -600,7 +602,8 @@ struct StateKernelWS {
 
   struct Ctx {
     const char *ktok_hi, *ktok_lo, *qtok_hi, *qtok_lo;  // slice 0 of this key head
-    size_t slice_bytes;                                  // T_pad * 32 * 2
+    size_t slice_bytes;                                  // T_pad * 32 * 2 (hi; lo: half)
+    float k_lo_scale, q_lo_scale;                        // scales of the e4m3 low halves
     const char *xv;    // x at (b, token 0, the block's first v channel)
     const char *hv;    // conv history at (b, row 0, the block's first v channel)
     const void *w;     // conv weights at the block's first v channel
@@ -633,15 +636,24 @@ struct StateKernelWS {
     lo = __builtin_bit_cast(u16x8, l);
   }
 
-  // Token-major rows of the owned tile, every d_k step (slice-major layout).
+  // Token-major rows of the owned tile, every d_k step (slice-major layout):
+  // bf16 hi, and the e4m3 low halves (one byte per element) widened to bf16.
+  // The low halves of the next chunk stay packed until it starts (lo8 holds
+  // them), so only 8 bytes per lane and step are in flight for them.
   static __device__ __forceinline__ void load_tok(const char *hi, const char *lo, const Ctx &x,
-                                                  int chunk, u16x8 (&h)[NS], u16x8 (&l)[NS]) {
+                                                  int chunk, u16x8 (&h)[NS], uint2 (&l8)[NS]) {
     const size_t row = static_cast<size_t>(chunk) * C * 32 * 2;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       h[s] = ldb<u16x8>(hi + row + s * x.slice_bytes, x.o_tok);
-      l[s] = ldb<u16x8>(lo + row + s * x.slice_bytes, x.o_tok);
+      l8[s] = ldb<uint2>(lo + (row + s * x.slice_bytes) / 2, x.o_tok / 2);
     }
+  }
+
+  static __device__ __forceinline__ void widen_lo(const uint2 (&l8)[NS], float scale,
+                                                  u16x8 (&l)[NS]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) l[s] = lo8_to_bf16x8(l8[s], scale);
   }
 
   // ---- V from x in the pass.  The output waves stage the x tile of chunk
@@ -833,7 +845,7 @@ struct StateKernelWS {
     float4 vc[NB];  // V of the current chunk, from the staged x tile
     o.g = load_gates(x, 0);
     asm volatile("" ::: "memory");
-    load_tok(x.ktok_hi, x.ktok_lo, x, 0, o.kh, o.kl);
+    load_tok(x.ktok_hi, x.ktok_lo, x, 0, o.kh, o.kl8);
     asm volatile("" ::: "memory");
     load_rows(x.Tm, x, 0, o.tm);
     asm volatile("" ::: "memory");
@@ -850,6 +862,8 @@ struct StateKernelWS {
       const Gates gn = load_gates(x, next);
       asm volatile("" ::: "memory");
       // 1. KS over the full depth, then R of the owned tile.
+      u16x8 kl[NS];
+      widen_lo(o.kl8, x.k_lo_scale, kl);
       u16x8 bh[NS][NB], bl[NS][NB];
 #pragma unroll
       for (int s = 0; s < NS; ++s)
@@ -862,15 +876,15 @@ struct StateKernelWS {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int n = 0; n < NB; ++n) ks[n] = mfma_split3(o.kh[s], o.kl[s], bh[s][n], bl[s][n], ks[n]);
+        for (int n = 0; n < NB; ++n) ks[n] = mfma_split3(o.kh[s], kl[s], bh[s][n], bl[s][n], ks[n]);
       // The owned K tile into the token-major copy, as held.
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int off = kq_piece(t_own, 4 * s + x.gq);
         *reinterpret_cast<u16x8 *>(&sm.KQ[0][t_own][off]) = o.kh[s];
-        *reinterpret_cast<u16x8 *>(&sm.KQ[1][t_own][off]) = o.kl[s];
+        *reinterpret_cast<u16x8 *>(&sm.KQ[1][t_own][off]) = kl[s];
       }
-      load_tok(x.ktok_hi, x.ktok_lo, x, next, o.kh, o.kl);
+      load_tok(x.ktok_hi, x.ktok_lo, x, next, o.kh, o.kl8);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         const float4 vv = vc[n];
@@ -946,7 +960,7 @@ struct StateKernelWS {
     uint4 xr[XK];  // x tile of the chunk after next, in flight
     load_xtile(x, x.NC > 1 ? 1 : 0, olane, xr);
     OutOps o;
-    load_tok(x.qtok_hi, x.qtok_lo, x, 0, o.qh, o.ql);
+    load_tok(x.qtok_hi, x.qtok_lo, x, 0, o.qh, o.ql8);
     asm volatile("" ::: "memory");
     load_z(x, 0, o);
     asm volatile("" ::: "memory");
@@ -967,6 +981,8 @@ struct StateKernelWS {
       constexpr bool kLast = decltype(last)::value;
       const int next = kLast ? chunk : chunk + 1;
       // 1. QS over the full depth.
+      u16x8 ql[NS];
+      widen_lo(o.ql8, x.q_lo_scale, ql);
       u16x8 bh[NS][NB], bl[NS][NB];
 #pragma unroll
       for (int s = 0; s < NS; ++s)
@@ -979,8 +995,8 @@ struct StateKernelWS {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int n = 0; n < NB; ++n) qs[n] = mfma_split3(o.qh[s], o.ql[s], bh[s][n], bl[s][n], qs[n]);
-      if (!kLast) load_tok(x.qtok_hi, x.qtok_lo, x, next, o.qh, o.ql);
+        for (int n = 0; n < NB; ++n) qs[n] = mfma_split3(o.qh[s], ql[s], bh[s][n], bl[s][n], qs[n]);
+      if (!kLast) load_tok(x.qtok_hi, x.qtok_lo, x, next, o.qh, o.ql8);
       __syncthreads();
 
       // 2. Gate of the owned tile: z arrives token-major; the wave's LDS slot
@@ -1104,10 +1120,12 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   typename K::Ctx x;
   const size_t slice0 = (static_cast<size_t>(b) * g.H_k + kh) * (D / 32) * L.T_pad * 32 * 2;
   x.ktok_hi = ws + L.k_hi + slice0;
-  x.ktok_lo = ws + L.k_lo + slice0;
+  x.ktok_lo = ws + L.k_lo + slice0 / 2;
   x.qtok_hi = ws + L.q_hi + slice0;
-  x.qtok_lo = ws + L.q_lo + slice0;
+  x.qtok_lo = ws + L.q_lo + slice0 / 2;
   x.slice_bytes = static_cast<size_t>(L.T_pad) * 32 * 2;
+  x.k_lo_scale = L.k_lo_scale;
+  x.q_lo_scale = L.q_lo_scale;
   const int v_ch0 = 2 * g.H_k * D + h * D + ROWS * rb;  // first conv channel of the block's rows
   x.xrow = static_cast<size_t>(g.C_ch) * sizeof(typename K::XE);
   x.xv = static_cast<const char *>(xin) + (static_cast<size_t>(b) * L.T * g.C_ch + v_ch0) * sizeof(typename K::XE);

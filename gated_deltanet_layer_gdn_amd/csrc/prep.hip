@@ -132,13 +132,19 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
     const uint16_t *klo = reinterpret_cast<const uint16_t *>(ws + L.k_lo);
     const uint16_t *qhi = reinterpret_cast<const uint16_t *>(ws + L.q_hi);
     const uint16_t *qlo = reinterpret_cast<const uint16_t *>(ws + L.q_lo);
-    auto load_tile = [&](const uint16_t *hi, const uint16_t *lo, int t, u16x8 (&h)[KS],
-                         u16x8 (&l)[KS]) {
+    // With the split-role state pass (d = 128, C = 64) the low halves are
+    // e4m3 bytes (same element index) with a power-of-two scale.
+    constexpr bool kLo8 = D == 128 && C == 64;
+    auto load_tile = [&](const uint16_t *hi, const uint16_t *lo, float lo_scale, int t,
+                         u16x8 (&h)[KS], u16x8 (&l)[KS]) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const size_t o = (((head0 + ks) * L.T_pad + tau0) + 16 * t + c) * 32 + 8 * gq;
         h[ks] = load8(hi + o);
-        l[ks] = load8(lo + o);
+        if constexpr (kLo8)
+          l[ks] = lo8_to_bf16x8(*reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(lo) + o), lo_scale);
+        else
+          l[ks] = load8(lo + o);
       }
     };
     // Owner of the tile at column-major position cm.
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
       const int cm0 = nt * NT - nt * (nt - 1) / 2;  // column-major position of (nt, nt)
       if (owner(cm0) > wave || owner(cm0 + NT - 1 - nt) < wave) continue;
       u16x8 bh[KS], bl[KS];
-      load_tile(khi, klo, nt, bh, bl);
+      load_tile(khi, klo, L.k_lo_scale, nt, bh, bl);
 #pragma unroll
       for (int mt = nt; mt < NT; ++mt) {
         if (owner(cm0 + mt - nt) != wave) continue;
@@ -160,9 +166,9 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
             akl[ks] = bl[ks];
           }
         } else {
-          load_tile(khi, klo, mt, akh, akl);
+          load_tile(khi, klo, L.k_lo_scale, mt, akh, akl);
         }
-        load_tile(qhi, qlo, mt, aqh, aql);
+        load_tile(qhi, qlo, L.q_lo_scale, mt, aqh, aql);
         f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
