@@ -200,7 +200,7 @@ bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *w) {
   const size_t mat = static_cast<size_t>(g.B) * g.H_v * w->NC * C * w->Cp * 2;
   w->Tm = take(mat);
   w->P_hi = take(mat);
-  w->P_lo = take(mat);
+  w->P_lo = take(lo8 ? mat / 2 : mat);  // e4m3 low halves for the split-role pass
   w->gates = take(static_cast<size_t>(g.B) * g.H_v * w->NC * 3 * C * 4);
   w->total = off;
   return true;

@@ -596,7 +596,8 @@ struct StateKernelWS {
     u16x8 qh[NS];          // Q of the owned tile
     uint2 ql8[NS];         // its low halves, e4m3
     float gam;             // gamma of token 4g + (c % 4), as in Gates
-    u16x8 ph[KSC], pl[KSC];
+    u16x8 ph[KSC];
+    uint2 pl8[KSC];        // P's low halves, e4m3
     uint4 z[ZK];
   };
 
@@ -608,7 +609,8 @@ struct StateKernelWS {
     const char *hv;    // conv history at (b, row 0, the block's first v channel)
     const void *w;     // conv weights at the block's first v channel
     size_t xrow;       // bytes per token row of x (and of the history)
-    const uint16_t *Tm, *Ph, *Pl;
+    const uint16_t *Tm, *Ph;
+    const uint8_t *Pl8;  // P's e4m3 low halves
     const float *gates;
     const void *z;
     void *y;
@@ -798,6 +800,17 @@ struct StateKernelWS {
     }
   }
 
+  // The same rows of a matrix of e4m3 bytes (P's low halves).
+  static __device__ __forceinline__ void load_rows8(const uint8_t *mat, const Ctx &x, int chunk,
+                                                    uint2 (&r)[KSC]) {
+    const uint8_t *base = mat + static_cast<size_t>(chunk) * C * Cp;
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks) {
+      const int kk = ks <= x.m / 2 ? ks : x.m / 2;
+      r[ks] = ldb<uint2>(base, x.o_mat / 2 + 32 * kk);
+    }
+  }
+
 
 
   static __device__ __forceinline__ void load_z(const Ctx &x, int chunk, OutOps &o) {
@@ -965,7 +978,7 @@ struct StateKernelWS {
     load_z(x, 0, o);
     asm volatile("" ::: "memory");
     load_rows(x.Ph, x, 0, o.ph);
-    load_rows(x.Pl, x, 0, o.pl);
+    load_rows8(x.Pl8, x, 0, o.pl8);
     load_gam(x, 0, o);
     asm volatile("" ::: "memory");
     __syncthreads();
@@ -1044,14 +1057,14 @@ struct StateKernelWS {
           if (kk <= m / 2) {
             u16x8 uh, ul;
             operand(sm.U[2 * kk][n][lane], sm.U[2 * kk + 1][n][lane], uh, ul);
-            acc = mfma_split3(o.ph[kk], o.pl[kk], uh, ul, acc);
+            acc = mfma_split3(o.ph[kk], lo8_to_bf16x8(o.pl8[kk], x.q_lo_scale), uh, ul, acc);
           }
 #pragma unroll
         for (int r = 0; r < 4; ++r) out[n][r] = acc[r] * sg[n][r];
       }
       if (!kLast) {
         load_rows(x.Ph, x, next, o.ph);
-        load_rows(x.Pl, x, next, o.pl);
+        load_rows8(x.Pl8, x, next, o.pl8);
         load_gam(x, next, o);
       }
       const int n_valid = valid_of(x, chunk);
@@ -1134,7 +1147,7 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   const size_t mat = (static_cast<size_t>(b) * g.H_v + h) * L.NC * C * Cp;
   x.Tm = reinterpret_cast<const uint16_t *>(ws + L.Tm) + mat;
   x.Ph = reinterpret_cast<const uint16_t *>(ws + L.P_hi) + mat;
-  x.Pl = reinterpret_cast<const uint16_t *>(ws + L.P_lo) + mat;
+  x.Pl8 = reinterpret_cast<const uint8_t *>(ws + L.P_lo) + mat;
   x.gates = reinterpret_cast<const float *>(ws + L.gates) + (static_cast<size_t>(b) * g.H_v + h) * L.NC * 3 * C;
   const size_t zy = (static_cast<size_t>(b) * L.T * g.H_v + h) * D + ROWS * rb;
   x.z = static_cast<const char *>(z) + zy * K::EZ;

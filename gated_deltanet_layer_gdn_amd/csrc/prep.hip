@@ -318,30 +318,51 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
     uint16_t *Tm = reinterpret_cast<uint16_t *>(ws + L.Tm) + mat;
     uint16_t *Ph = reinterpret_cast<uint16_t *>(ws + L.P_hi) + mat;
     uint16_t *Pl = reinterpret_cast<uint16_t *>(ws + L.P_lo) + mat;
+    // For the split-role state pass (d = 128, C = 64) the low half of P is
+    // e4m3 bytes (|P| <= |q_scale|, so q's scale), at the same element index.
+    constexpr bool kLo8 = D == 128 && C == 64;
+    uint8_t *Pl8 = reinterpret_cast<uint8_t *>(ws + L.P_lo) + mat;
     constexpr int ITEMS = C * (Cp / 32) * 4;
     for (int it = threadIdx.x; it < ITEMS; it += 256) {
       const int t = it / (Cp / 8), rem = it % (Cp / 8);
       const int kk = rem >> 2, q = rem & 3;
-      u16x8 tv8, ph8, pl8;
+      u16x8 tv8;
+      float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int sc = 32 * kk + (i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4));
-        float tv = 0.f, pv = 0.f;
+        float tv = 0.f;
+        pv[i] = 0.f;
         if (sc < C && sc <= t) {
           const int tr = tri_index(t >> 4, sc >> 4), off = (t & 15) * 16 + (sc & 15);
           tv = TI[tr][off];
-          pv = __expf(Gs[t] - Gs[sc]) * QK[tr][off];
+          pv[i] = __expf(Gs[t] - Gs[sc]) * QK[tr][off];
         }
-        uint16_t hi, lo;
-        split_bf16(pv, hi, lo);
         tv8[i] = f32_to_bf16_bits(tv);
-        ph8[i] = hi;
-        pl8[i] = lo;
       }
       const size_t o = static_cast<size_t>(t) * Cp + 32 * kk + 8 * q;
       *reinterpret_cast<u16x8 *>(Tm + o) = tv8;
-      *reinterpret_cast<u16x8 *>(Ph + o) = ph8;
-      *reinterpret_cast<u16x8 *>(Pl + o) = pl8;
+      if constexpr (kLo8) {
+        uint32_t h[4];
+        uint16_t l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split2_lo8(pv[2 * i], pv[2 * i + 1], L.q_lo_scale, h[i], l[i]);
+        const u32x4 hv = {h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<u16x8 *>(Ph + o) = __builtin_bit_cast(u16x8, hv);
+        *reinterpret_cast<uint2 *>(Pl8 + o) =
+            make_uint2(l[0] | (static_cast<uint32_t>(l[1]) << 16), l[2] | (static_cast<uint32_t>(l[3]) << 16));
+      } else {
+        u16x8 ph8, pl8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint16_t hi, lo;
+          split_bf16(pv[i], hi, lo);
+          ph8[i] = hi;
+          pl8[i] = lo;
+        }
+        *reinterpret_cast<u16x8 *>(Ph + o) = ph8;
+        *reinterpret_cast<u16x8 *>(Pl + o) = pl8;
+      }
     }
   }
 }
