@@ -64,6 +64,17 @@ def test_prefill_ragged_small(T, chunk):
     check_layer(f"ragged T={T} C={chunk}", gpu_prefill(geom, I, chunk), oracle_run(geom, I))
 
 
+@pytest.mark.parametrize("q_scale", [128 ** -0.5, 3.7, -0.5])
+def test_prefill_q_scale(q_scale):
+    # d = 128, chunk 64 keeps the low halves of q and P as e4m3 bytes scaled by
+    # |q_scale|; a ragged tail and B = 2 ride along.
+    geom = Geometry(B=2, T=333, H_k=4, H_v=12, d_k=128, d_v=128, zero_state=False)
+    I = make_inputs(geom, seed=41)
+    dims = dims_of(geom, q_scale=q_scale)
+    check_layer(f"q_scale={q_scale:.4g} T=333 C=64", gpu_prefill(geom, I, 64, dims=dims),
+                oracle_run(geom, I, q_scale=q_scale))
+
+
 @pytest.mark.parametrize("chunk", [64, 128])
 def test_prefill_weak_decay(chunk):
     # a close to 1 (g = -0.02 softplus(N)): the inter-chunk state dominates.
