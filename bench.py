@@ -36,8 +36,8 @@ ROTATE_BYTES = 512 << 20   # rotated state sets per decode timing
 # file the bench reports the traffic as null until the counters are taken again.
 MEASURED_TRAFFIC = {
     "prefill_state": {"source": "gated_deltanet_layer_gdn_amd/csrc/prefill.hip",
-        "sha256": "b718c20f27b57bafafca27d3917ae6f3202b40035a5b55ddd1de8d0e5491f5e7",
-        "read_bytes": 232339418, "write_bytes": 103845888},
+        "sha256": "19fca2fb01d4217858123a93d7e28e0f4618a2126708fddf719bd86396401ecd",
+        "read_bytes": 219764009, "write_bytes": 103845888},
     "decode_b64": {"source": "gated_deltanet_layer_gdn_amd/csrc/decode.hip",
         "sha256": "1cb61099c38a89d236d4e790f0ce552d7b02c440f98cb1d160d6dfff6482c483",
         "read_bytes": 207301072, "write_bytes": 202916593},
