@@ -546,6 +546,11 @@ __global__ __launch_bounds__((StateShape<D, C>::NWV * 64)) void state_kernel(
 //            output z tile -> sigmoid, through the wave's LDS slot
 //   phase 3: chain  S^T <- gamma_last S^T + K^T DU, new state operands -> LDS
 //            output O = gamma QS + P U, y = O sigmoid(z) -> HBM
+// K^T of the update comes from a token-major LDS copy of the chunk's K (the
+// chain waves' A operand registers, stored as held) through transposing
+// loads; V is SiLU(conv x) of the block's v channels, from x tiles the output
+// waves stage; the low halves of q, k and P arrive as scaled e4m3 bytes and
+// are widened to bf16 in registers.
 template <int DTZ, int DTY>
 struct StateKernelWS {
   static constexpr int D = 128, C = 64, NT = 4, NB = 2, ROWS = 32, NDT = 2, KSC = 2, Cp = 64;
