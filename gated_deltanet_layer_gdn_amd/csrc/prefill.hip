@@ -895,14 +895,6 @@ struct StateKernelWS {
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int n = 0; n < NB; ++n) ks[n] = mfma_split3(o.kh[s], kl[s], bh[s][n], bl[s][n], ks[n]);
-      // The owned K tile into the token-major copy, as held.
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int off = kq_piece(t_own, 4 * s + x.gq);
-        *reinterpret_cast<u16x8 *>(&sm.KQ[0][t_own][off]) = o.kh[s];
-        *reinterpret_cast<u16x8 *>(&sm.KQ[1][t_own][off]) = kl[s];
-      }
-      load_tok(x.ktok_hi, x.ktok_lo, x, next, o.kh, o.kl8);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         const float4 vv = vc[n];
@@ -914,6 +906,16 @@ struct StateKernelWS {
       __syncthreads();
 
       // 2. U = Tm R for the owned tile, and its decayed copy for the update.
+      //    First the owned K tile into the token-major copy, as held (read in
+      //    phase 3; phase 1 already carries the state-operand reads), and the
+      //    next chunk's K in flight.
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int off = kq_piece(t_own, 4 * s + x.gq);
+        *reinterpret_cast<u16x8 *>(&sm.KQ[0][t_own][off]) = o.kh[s];
+        *reinterpret_cast<u16x8 *>(&sm.KQ[1][t_own][off]) = kl[s];
+      }
+      load_tok(x.ktok_hi, x.ktok_lo, x, next, o.kh, o.kl8);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         f32x4 acc = zero;
