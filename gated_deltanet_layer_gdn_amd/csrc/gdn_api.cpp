@@ -178,21 +178,22 @@ bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *w) {
   };
   const size_t tp = static_cast<size_t>(w->T_pad);
   const size_t tok = static_cast<size_t>(g.B) * g.H_k * tp * w->Dp * 2;
-  // The split-role pass keeps the low halves of q and k as e4m3 bytes with a
-  // power-of-two scale 2^(e - 15), where 2^e bounds the values: normalised k
-  // is at most 1 in magnitude, q at most q_scale.
-  const bool lo8 = prefill_split_roles(g, *w);
+  // The split-role pass keeps the low halves of q, k and P as e4m3 bytes with
+  // a power-of-two scale 2^(e - 15), where 2^e bounds the values: normalised k
+  // is at most 1 in magnitude, q and P at most |q_scale|.  Validation keeps
+  // |q_scale| below 1e30 < 2^100, so e <= 100; below 2^-100 the low halves of
+  // q and P lose precision but cannot overflow.
+  const bool split = prefill_split_roles(g, *w);
   const float qmax = std::fabs(g.q_scale);
-  const int qe = qmax > 0.f ? std::max(-60, std::min(60, static_cast<int>(std::ceil(std::log2(qmax))))) : 0;
-  w->q_lo_scale = lo8 ? std::ldexp(1.0f, qe - 15) : 0.f;
-  w->k_lo_scale = lo8 ? std::ldexp(1.0f, -15) : 0.f;
+  const int qe = qmax > 0.f ? std::max(-100, std::min(100, static_cast<int>(std::ceil(std::log2(qmax))))) : 0;
+  w->q_lo_scale = split ? std::ldexp(1.0f, qe - 15) : 0.f;
+  w->k_lo_scale = split ? std::ldexp(1.0f, -15) : 0.f;
   w->q_hi = take(tok);
-  w->q_lo = take(lo8 ? tok / 2 : tok);
+  w->q_lo = take(split ? tok / 2 : tok);
   w->k_hi = take(tok);
-  w->k_lo = take(lo8 ? tok / 2 : tok);
+  w->k_lo = take(split ? tok / 2 : tok);
   // The split-role state pass builds the dim-major k in LDS and computes v
   // from x: those regions are empty for it.
-  const bool split = prefill_split_roles(g, *w);
   const size_t kt = split ? 0 : static_cast<size_t>(g.B) * g.H_k * tp * g.D * 2;
   w->kT_hi = take(kt);
   w->kT_lo = take(kt);
@@ -200,7 +201,7 @@ bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *w) {
   const size_t mat = static_cast<size_t>(g.B) * g.H_v * w->NC * C * w->Cp * 2;
   w->Tm = take(mat);
   w->P_hi = take(mat);
-  w->P_lo = take(lo8 ? mat / 2 : mat);  // e4m3 low halves for the split-role pass
+  w->P_lo = take(split ? mat / 2 : mat);  // e4m3 low halves for the split-role pass
   w->gates = take(static_cast<size_t>(g.B) * g.H_v * w->NC * 3 * C * 4);
   w->total = off;
   return true;

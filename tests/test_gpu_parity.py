@@ -64,7 +64,7 @@ def test_prefill_ragged_small(T, chunk):
     check_layer(f"ragged T={T} C={chunk}", gpu_prefill(geom, I, chunk), oracle_run(geom, I))
 
 
-@pytest.mark.parametrize("q_scale", [128 ** -0.5, 3.7, -0.5])
+@pytest.mark.parametrize("q_scale", [128 ** -0.5, 3.7, -0.5, 1.5e21])
 def test_prefill_q_scale(q_scale):
     # d = 128, chunk 64 keeps the low halves of q and P as e4m3 bytes scaled by
     # |q_scale|; a ragged tail and B = 2 ride along.
