@@ -40,14 +40,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// x - float(hi) for a pair and its bf16 rounding, one bf16 dot2 per element
+// (x + (-1) hi_i + (-0) hi_j): the products are exact and the sum is rounded
+// once, so this is the exact residual, as the two-step subtraction gives it.
+// The zero weights are -0 so that neither weight pair is an inline constant:
+// (-1, +0) was encoded as the inline constant -1.0, which the unit reads as
+// the fp32 bits of -1.0, i.e. the pair (+0, -1).
+__device__ __forceinline__ f32x2 residual2(f32x2 v, bf16x2 h) {
+  const bf16x2 m0 = {static_cast<__bf16>(-1.0f), static_cast<__bf16>(-0.0f)};
+  const bf16x2 m1 = {static_cast<__bf16>(-0.0f), static_cast<__bf16>(-1.0f)};
+  const f32x2 r = {__builtin_amdgcn_fdot2_f32_bf16(h, m0, v[0], false),
+                   __builtin_amdgcn_fdot2_f32_bf16(h, m1, v[1], false)};
+  return r;
+}
+
 // Split a pair into hi + lo, both bf16 (round to nearest even, on gfx950's
 // packed convert): hi = bf16(x), lo = bf16(x - hi), so hi + lo carries 16
 // significant bits of x.  Returns each pair packed low element first.
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
   const f32x2 v = {a, b};
   const bf16x2 h = __builtin_convertvector(v, bf16x2);
-  const f32x2 hf = __builtin_convertvector(h, f32x2);
-  const bf16x2 l = __builtin_convertvector(v - hf, bf16x2);
+  const f32x2 r = residual2(v, h);
+  const bf16x2 l = __builtin_convertvector(r, bf16x2);
   hi = __builtin_bit_cast(uint32_t, h);
   lo = __builtin_bit_cast(uint32_t, l);
 }
@@ -61,7 +75,7 @@ __device__ __forceinline__ void split2_lo8(float a, float b, float scale, uint32
   typedef short s16x2 __attribute__((ext_vector_type(2)));
   const f32x2 v = {a, b};
   const bf16x2 h = __builtin_convertvector(v, bf16x2);
-  const f32x2 r = v - __builtin_convertvector(h, f32x2);
+  const f32x2 r = residual2(v, h);
   const s16x2 zero = {0, 0};
   const s16x2 c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero, r[0], r[1], scale, false);
   hi = __builtin_bit_cast(uint32_t, h);

@@ -574,9 +574,11 @@ struct StateKernelWS {
     // permuted K order), hi and lo, 16-byte pieces swizzled per token (see
     // kq_piece).  The state update reads K^T from it with transposing loads.
     alignas(16) uint16_t KQ[2][C][D];
-    Split4 R[NT][NB][64];
-    Split4 U[NT][NB][64];
-    Split4 DU[NT][NB][64];
+    // R, U and DU tiles, split, as B operands: entry [kk][n][lane] holds the
+    // hi (or lo) halves of token tiles 2kk (first 8 bytes) and 2kk + 1.
+    u16x8 Rh[NT / 2][NB][64], Rl[NT / 2][NB][64];
+    u16x8 Uh[NT / 2][NB][64], Ul[NT / 2][NB][64];
+    u16x8 DUh[NT / 2][NB][64], DUl[NT / 2][NB][64];
     uint4 z[NT][16 * ZL];                  // per output wave: one token tile of z
     // x of the block's 32 v channels for a chunk and the three tokens before
     // it, double-buffered by chunk parity (staged by the output waves).
@@ -636,11 +638,16 @@ struct StateKernelWS {
     return Split4{make_uint2(h0, h1), make_uint2(l0, l1)};
   }
 
-  static __device__ __forceinline__ void operand(const Split4 &a, const Split4 &b, u16x8 &hi,
-                                                 u16x8 &lo) {
-    const u32x4 h = {a.hi.x, a.hi.y, b.hi.x, b.hi.y}, l = {a.lo.x, a.lo.y, b.lo.x, b.lo.y};
-    hi = __builtin_bit_cast(u16x8, h);
-    lo = __builtin_bit_cast(u16x8, l);
+  static __device__ __forceinline__ u16x8 pair(const u16x8 (&a)[NT / 2][NB][64], int kk, int n,
+                                               int lane) {
+    return a[kk][n][lane];
+  }
+
+  // Tile m's half of its K step's operands.
+  static __device__ __forceinline__ void put(u16x8 (&h)[NT / 2][NB][64], u16x8 (&l)[NT / 2][NB][64],
+                                             int m, int n, int lane, const Split4 &v) {
+    reinterpret_cast<uint2 *>(&h[m / 2][n][lane])[m & 1] = v.hi;
+    reinterpret_cast<uint2 *>(&l[m / 2][n][lane])[m & 1] = v.lo;
   }
 
   // Token-major rows of the owned tile, every d_k step (slice-major layout):
@@ -901,7 +908,7 @@ struct StateKernelWS {
         const float4 bt = quad4(o.g.bt), ga = quad4(o.g.gam);
         const f32x4 r = {bt.x * (vv.x - ga.x * ks[n][0]), bt.y * (vv.y - ga.y * ks[n][1]),
                          bt.z * (vv.z - ga.z * ks[n][2]), bt.w * (vv.w - ga.w * ks[n][3])};
-        sm.R[m][n][lane] = split4(r);
+        put(sm.Rh, sm.Rl, m, n, lane, split4(r));
       }
       __syncthreads();
 
@@ -922,14 +929,12 @@ struct StateKernelWS {
 #pragma unroll
         for (int kk = 0; kk < KSC; ++kk)
           if (kk <= m / 2) {
-            u16x8 bh, bl;
-            operand(sm.R[2 * kk][n][lane], sm.R[2 * kk + 1][n][lane], bh, bl);
-            acc = mfma_split2(o.tm[kk], bh, bl, acc);
+            acc = mfma_split2(o.tm[kk], pair(sm.Rh, kk, n, lane), pair(sm.Rl, kk, n, lane), acc);
           }
-        sm.U[m][n][lane] = split4(acc);
+        put(sm.Uh, sm.Ul, m, n, lane, split4(acc));
         const float4 dl = quad4(o.g.dl);
         const f32x4 du = {dl.x * acc[0], dl.y * acc[1], dl.z * acc[2], dl.w * acc[3]};
-        sm.DU[m][n][lane] = split4(du);
+        put(sm.DUh, sm.DUl, m, n, lane, split4(du));
       }
       load_rows(x.Tm, x, next, o.tm);
       __syncthreads();
@@ -952,8 +957,7 @@ struct StateKernelWS {
         for (int dt = 0; dt < NDT; ++dt) st[n][dt] *= o.g.glast;
 #pragma unroll
         for (int kk = 0; kk < KSC; ++kk) {
-          u16x8 bh, bl;
-          operand(sm.DU[2 * kk][n][lane], sm.DU[2 * kk + 1][n][lane], bh, bl);
+          const u16x8 bh = pair(sm.DUh, kk, n, lane), bl = pair(sm.DUl, kk, n, lane);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) st[n][dt] = mfma_split3(th[kk][dt], tl[kk][dt], bh, bl, st[n][dt]);
         }
@@ -1062,8 +1066,7 @@ struct StateKernelWS {
 #pragma unroll
         for (int kk = 0; kk < KSC; ++kk)
           if (kk <= m / 2) {
-            u16x8 uh, ul;
-            operand(sm.U[2 * kk][n][lane], sm.U[2 * kk + 1][n][lane], uh, ul);
+            const u16x8 uh = pair(sm.Uh, kk, n, lane), ul = pair(sm.Ul, kk, n, lane);
             acc = mfma_split3(o.ph[kk], lo8_to_bf16x8(o.pl8[kk], x.q_lo_scale), uh, ul, acc);
           }
 #pragma unroll
