@@ -876,6 +876,10 @@ struct StateKernelWS {
     asm volatile("" ::: "memory");
     __syncthreads();
 #pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) st[n][dt] *= o.g.glast;
+#pragma unroll
     for (int n = 0; n < NB; ++n) vc[n] = v_tile(sm, 0, m, x.gq, 16 * n + (lane & 15), wv[n]);
     // The owned token's row of the token-major K copy.
     const int t_own = 16 * m + (lane & 15);
@@ -931,10 +935,11 @@ struct StateKernelWS {
           if (kk <= m / 2) {
             acc = mfma_split2(o.tm[kk], pair(sm.Rh, kk, n, lane), pair(sm.Rl, kk, n, lane), acc);
           }
-        put(sm.Uh, sm.Ul, m, n, lane, split4(acc));
+        // DU first: the split overwrites what it splits.
         const float4 dl = quad4(o.g.dl);
         const f32x4 du = {dl.x * acc[0], dl.y * acc[1], dl.z * acc[2], dl.w * acc[3]};
         put(sm.DUh, sm.DUl, m, n, lane, split4(du));
+        put(sm.Uh, sm.Ul, m, n, lane, split4(acc));
       }
       load_rows(x.Tm, x, next, o.tm);
       __syncthreads();
@@ -954,16 +959,27 @@ struct StateKernelWS {
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) st[n][dt] *= o.g.glast;
-#pragma unroll
         for (int kk = 0; kk < KSC; ++kk) {
           const u16x8 bh = pair(sm.DUh, kk, n, lane), bl = pair(sm.DUl, kk, n, lane);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) st[n][dt] = mfma_split3(th[kk][dt], tl[kk][dt], bh, bl, st[n][dt]);
         }
       }
+      // The state decayed for the next chunk's update, then the split of
+      // this state in place (it overwrites what it splits).  After the last
+      // chunk the factor is 1 and sc is the final state.
+      const float gl = chunk + 1 < x.NC ? gn.glast : 1.f;
+      f32x4 sc[NB][NDT];
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) sc[n][dt] = st[n][dt] * gl;
 #pragma unroll
       for (int n = 0; n < NB; ++n) pack_split(st[n][0], st[n][1], sm.Sh[w][n][lane], sm.Sl[w][n][lane]);
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) st[n][dt] = sc[n][dt];
       o.g = gn;
       __syncthreads();
     }
