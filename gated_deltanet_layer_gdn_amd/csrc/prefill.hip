@@ -67,6 +67,27 @@ __device__ __forceinline__ V ldb(const void *base, uint32_t byte_off) {
   return *reinterpret_cast<const V *>(static_cast<const char *>(base) + byte_off);
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (stride 0, gfx9 word 3):
+// loads take a wave-uniform base in scalar registers, a 32-bit vector
+// offset and a scalar offset, so they need no 64-bit address arithmetic on
+// the VALU; loads at or past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+template <typename V>
+__device__ __forceinline__ V bld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(V) == 4)
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+  else if constexpr (sizeof(V) == 8)
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+  else
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+constexpr uint32_t kAllBytes = 0xffffffffu;
+
 // A value at a wave-uniform address through a vector load.  A scalar load
 // would share its wait counter with LDS, so every LDS wait issued while it
 // is in flight would also wait for its L2 round trip.
@@ -657,10 +678,12 @@ struct StateKernelWS {
   static __device__ __forceinline__ void load_tok(const char *hi, const char *lo, const Ctx &x,
                                                   int chunk, u16x8 (&h)[NS], uint2 (&l8)[NS]) {
     const size_t row = static_cast<size_t>(chunk) * C * 32 * 2;
+    const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hi + row, kAllBytes), rl = buf_rsrc(lo + row / 2, kAllBytes);
+    const uint32_t sb = static_cast<uint32_t>(x.slice_bytes);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      h[s] = ldb<u16x8>(hi + row + s * x.slice_bytes, x.o_tok);
-      l8[s] = ldb<uint2>(lo + (row + s * x.slice_bytes) / 2, x.o_tok / 2);
+      h[s] = bld<u16x8>(rh, x.o_tok, s * sb);
+      l8[s] = bld<uint2>(rl, x.o_tok / 2, s * sb / 2);
     }
   }
 
@@ -688,15 +711,18 @@ struct StateKernelWS {
   // of the first chunk, is never stored: it comes from stage_first_xtile).
   static __device__ __forceinline__ void load_xtile(const Ctx &x, int chunk, int olane,
                                                     uint4 (&xr)[XK]) {
+    const int64_t t0 = static_cast<int64_t>(chunk) * C - 3;
+    if (t0 < 0) return;  // only a one-chunk sequence asks for it, and never stores it
+    // Rows at or past the sequence end lie past the resource and read zero.
+    const int64_t rows = x.T - t0 < XR ? x.T - t0 : XR;
+    const __amdgpu_buffer_rsrc_t r =
+        buf_rsrc(x.xv + static_cast<size_t>(t0) * x.xrow, static_cast<uint32_t>(rows * x.xrow));
 #pragma unroll
     for (int k = 0; k < XK; ++k) {
       int piece = olane + 256 * k;
       piece = piece < XPIECES ? piece : XPIECES - 1;
       const int row = piece / XPR, part = piece % XPR;
-      int64_t tok = static_cast<int64_t>(chunk) * C - 3 + row;
-      tok = tok < x.T ? tok : x.T - 1;
-      tok = tok > 0 ? tok : 0;
-      xr[k] = ldb<uint4>(x.xv + static_cast<size_t>(tok) * x.xrow, part * 16);
+      xr[k] = bld<uint4>(r, static_cast<uint32_t>(row * x.xrow + part * 16), 0);
     }
   }
 
@@ -791,12 +817,14 @@ struct StateKernelWS {
   // One dword per lane: sixteen lanes share each group's four values, so
   // the loads return a quarter of what per-lane float4 loads would.
   static __device__ __forceinline__ Gates load_gates(const Ctx &x, int chunk) {
-    const float *gb = x.gates + static_cast<size_t>(chunk) * 3 * C;
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(x.gates + static_cast<size_t>(chunk) * 3 * C, kAllBytes);
     Gates o;
-    o.gam = ldb<float>(gb, x.o_gate);
-    o.dl = ldb<float>(gb, x.o_gate + C * 4);
-    o.bt = ldb<float>(gb, x.o_gate + 2 * C * 4);
-    o.glast = ld_uniform_vec(gb, (C - 1) * 4);
+    o.gam = bld<float>(r, x.o_gate, 0);
+    o.dl = bld<float>(r, x.o_gate, C * 4);
+    o.bt = bld<float>(r, x.o_gate, 2 * C * 4);
+    uint32_t z0 = 0;
+    asm volatile("" : "+v"(z0));  // a vector offset, so the load stays a vector one
+    o.glast = bld<float>(r, z0, (C - 1) * 4);
     return o;
   }
 
@@ -804,22 +832,22 @@ struct StateKernelWS {
   // diagonal re-read the last needed one (they are not used).
   static __device__ __forceinline__ void load_rows(const uint16_t *mat, const Ctx &x, int chunk,
                                                    u16x8 (&r)[KSC]) {
-    const uint16_t *base = mat + static_cast<size_t>(chunk) * C * Cp;
+    const __amdgpu_buffer_rsrc_t rr = buf_rsrc(mat + static_cast<size_t>(chunk) * C * Cp, kAllBytes);
 #pragma unroll
     for (int ks = 0; ks < KSC; ++ks) {
       const int kk = ks <= x.m / 2 ? ks : x.m / 2;
-      r[ks] = ldb<u16x8>(base, x.o_mat + 32 * kk * 2);
+      r[ks] = bld<u16x8>(rr, x.o_mat, 32 * kk * 2);
     }
   }
 
   // The same rows of a matrix of e4m3 bytes (P's low halves).
   static __device__ __forceinline__ void load_rows8(const uint8_t *mat, const Ctx &x, int chunk,
                                                     uint2 (&r)[KSC]) {
-    const uint8_t *base = mat + static_cast<size_t>(chunk) * C * Cp;
+    const __amdgpu_buffer_rsrc_t rr = buf_rsrc(mat + static_cast<size_t>(chunk) * C * Cp, kAllBytes);
 #pragma unroll
     for (int ks = 0; ks < KSC; ++ks) {
       const int kk = ks <= x.m / 2 ? ks : x.m / 2;
-      r[ks] = ldb<uint2>(base, x.o_mat / 2 + 32 * kk);
+      r[ks] = bld<uint2>(rr, x.o_mat / 2, 32 * kk);
     }
   }
 
@@ -829,18 +857,19 @@ struct StateKernelWS {
     const int n_valid = valid_of(x, chunk);
     const char *zb = static_cast<const char *>(x.z) + static_cast<size_t>(chunk) * C * x.H_v * D * EZ;
     const uint32_t tstride = x.H_v * D * EZ;
+    // Rows past the sequence end lie past the resource and read zero.
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(zb, n_valid * tstride);
 #pragma unroll
     for (int k = 0; k < ZK; ++k) {
       int idx = x.lane + 64 * k;
       idx = idx < 16 * ZL ? idx : 16 * ZL - 1;
-      int t = 16 * x.m + idx / ZL;
-      t = t < n_valid ? t : n_valid - 1;  // rows past the end re-read the last one
-      o.z[k] = ldb<uint4>(zb, t * tstride + (idx % ZL) * 16);
+      const int t = 16 * x.m + idx / ZL;
+      o.z[k] = bld<uint4>(r, t * tstride + (idx % ZL) * 16, 0);
     }
   }
 
   static __device__ __forceinline__ void load_gam(const Ctx &x, int chunk, OutOps &o) {
-    o.gam = ldb<float>(x.gates + static_cast<size_t>(chunk) * 3 * C, x.o_gate);
+    o.gam = bld<float>(buf_rsrc(x.gates + static_cast<size_t>(chunk) * 3 * C, kAllBytes), x.o_gate, 0);
   }
 
 
@@ -1073,7 +1102,9 @@ struct StateKernelWS {
       __syncthreads();
 
       // 3. O = gamma QS + P U, gated, stored.
-      char *yb = static_cast<char *>(x.y) + static_cast<size_t>(chunk) * C * x.H_v * D * ey;
+      const __amdgpu_buffer_rsrc_t ry =
+          buf_rsrc(static_cast<char *>(x.y) + static_cast<size_t>(chunk) * C * x.H_v * D * ey, kAllBytes);
+      const uint32_t yoff = x.o_zy * ey + 16 * m * ystride;
       f32x4 out[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
@@ -1100,11 +1131,11 @@ struct StateKernelWS {
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * m + 4 * gq + r;
           if (!kLast || t < n_valid) {
-            char *dst = yb + (x.o_zy + 16 * n) * ey + (16 * m + r) * ystride;
+            const uint32_t so = 16 * n * ey + r * ystride;
             if constexpr (DTY == 0)
-              *reinterpret_cast<float *>(dst) = out[n][r];
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out[n][r]), ry, yoff, so, 0);
             else
-              *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16_bits(out[n][r]);
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(out[n][r]), ry, yoff, so, 0);
           }
         }
       __syncthreads();
