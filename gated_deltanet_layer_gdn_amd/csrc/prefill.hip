@@ -946,9 +946,20 @@ struct StateKernelWS {
       __syncthreads();
 
       // 2. U = Tm R for the owned tile, and its decayed copy for the update.
-      //    First the owned K tile into the token-major copy, as held (read in
+      //    The R operands are read first, every K step whether this tile
+      //    needs it or not, so that they go out together ahead of the LDS
+      //    stores below instead of one round trip per step behind them.
+      //    Then the owned K tile into the token-major copy, as held (read in
       //    phase 3; phase 1 already carries the state-operand reads), and the
       //    next chunk's K in flight.
+      u16x8 rh[KSC][NB], rl[KSC][NB];
+#pragma unroll
+      for (int kk = 0; kk < KSC; ++kk)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          rh[kk][n] = pair(sm.Rh, kk, n, lane);
+          rl[kk][n] = pair(sm.Rl, kk, n, lane);
+        }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int off = kq_piece(t_own, 4 * s + x.gq);
@@ -962,7 +973,7 @@ struct StateKernelWS {
 #pragma unroll
         for (int kk = 0; kk < KSC; ++kk)
           if (kk <= m / 2) {
-            acc = mfma_split2(o.tm[kk], pair(sm.Rh, kk, n, lane), pair(sm.Rl, kk, n, lane), acc);
+            acc = mfma_split2(o.tm[kk], rh[kk][n], rl[kk][n], acc);
           }
         // DU first: the split overwrites what it splits.
         const float4 dl = quad4(o.g.dl);
