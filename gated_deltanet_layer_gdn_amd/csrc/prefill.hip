@@ -571,7 +571,9 @@ __global__ __launch_bounds__((StateShape<D, C>::NWV * 64)) void state_kernel(
 // chain waves' A operand registers, stored as held) through transposing
 // loads; V is SiLU(conv x) of the block's v channels, from x tiles the output
 // waves stage; the low halves of q, k and P arrive as scaled e4m3 bytes and
-// are widened to bf16 in registers.
+// are widened to bf16 in registers.  Column c of the two 16-column tiles
+// (n = 0, 1) is the block's state row 2c + n, so each lane's two channels
+// sit side by side in x, z and y: one 4- or 8-byte access serves both.
 template <int DTZ, int DTY>
 struct StateKernelWS {
   static constexpr int D = 128, C = 64, NT = 4, NB = 2, ROWS = 32, NDT = 2, KSC = 2, Cp = 64;
@@ -757,6 +759,35 @@ struct StateKernelWS {
     }
   }
 
+  // V of the owned tile for both of the lane's channels (2c and 2c + 1: tile
+  // columns n = 0, 1 hold the block's even and odd rows), D-register order:
+  // tokens 16 m + 4 g + r, r = 0..3 (tile rows 16 m + 4 g + r .. + 3).
+  static __device__ __forceinline__ void v_tile2(const Smem &sm, int buf, int m, int gq, int c,
+                                                 const float (&w)[NB][4], float4 (&v)[NB]) {
+    const int t0 = 16 * m + 4 * gq;
+    float xs[NB][7];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      if constexpr (DTZ == 0) {
+        const uint2 p = *reinterpret_cast<const uint2 *>(&sm.XT[buf][t0 + i][2 * c]);
+        xs[0][i] = __uint_as_float(p.x);
+        xs[1][i] = __uint_as_float(p.y);
+      } else {
+        const uint32_t p = *reinterpret_cast<const uint32_t *>(&sm.XT[buf][t0 + i][2 * c]);
+        xs[0][i] = __uint_as_float(p << 16);
+        xs[1][i] = __uint_as_float(p & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const float *q = xs[n];
+      v[n].x = siluf_(conv4(w[n][0], w[n][1], w[n][2], w[n][3], q[0], q[1], q[2], q[3]));
+      v[n].y = siluf_(conv4(w[n][0], w[n][1], w[n][2], w[n][3], q[1], q[2], q[3], q[4]));
+      v[n].z = siluf_(conv4(w[n][0], w[n][1], w[n][2], w[n][3], q[2], q[3], q[4], q[5]));
+      v[n].w = siluf_(conv4(w[n][0], w[n][1], w[n][2], w[n][3], q[3], q[4], q[5], q[6]));
+    }
+  }
+
   // V of the owned tile, D-register order: lane (c, g) gets channel row
   // 16 n + c for tokens 16 m + 4 g + r, r = 0..3 (tile rows 16 m + 4 g + r .. + 3).
   static __device__ __forceinline__ float4 v_tile(const Smem &sm, int buf, int m, int gq, int row,
@@ -884,7 +915,7 @@ struct StateKernelWS {
     for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const float4 v = *reinterpret_cast<const float4 *>(Sh + 16 * n * D + 32 * w + 16 * dt + 4 * x.gq);
+        const float4 v = *reinterpret_cast<const float4 *>(Sh + n * D + 32 * w + 16 * dt + 4 * x.gq);
         st[n][dt] = f32x4{v.x, v.y, v.z, v.w};
       }
 #pragma unroll
@@ -894,7 +925,7 @@ struct StateKernelWS {
 #pragma unroll
     for (int n = 0; n < NB; ++n)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) wv[n][k] = load_elem<DTZ>(x.w, (16 * n + (lane & 15)) * 4 + k);
+      for (int k = 0; k < 4; ++k) wv[n][k] = load_elem<DTZ>(x.w, (2 * (lane & 15) + n) * 4 + k);
     ChainOps o;
     float4 vc[NB];  // V of the current chunk, from the staged x tile
     o.g = load_gates(x, 0);
@@ -908,8 +939,7 @@ struct StateKernelWS {
     for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) st[n][dt] *= o.g.glast;
-#pragma unroll
-    for (int n = 0; n < NB; ++n) vc[n] = v_tile(sm, 0, m, x.gq, 16 * n + (lane & 15), wv[n]);
+    v_tile2(sm, 0, m, x.gq, lane & 15, wv, vc);
     // The owned token's row of the token-major K copy.
     const int t_own = 16 * m + (lane & 15);
 
@@ -986,8 +1016,7 @@ struct StateKernelWS {
 
       // 3. S^T <- gamma_last S^T + K^T DU over the owned d_k slice, and V of
       //    the next chunk from its x tile (staged in phase 2).
-#pragma unroll
-      for (int n = 0; n < NB; ++n) vc[n] = v_tile(sm, next & 1, m, x.gq, 16 * n + (lane & 15), wv[n]);
+      v_tile2(sm, next & 1, m, x.gq, lane & 15, wv, vc);
       u16x8 th[KSC][NDT], tl[KSC][NDT];
 #pragma unroll
       for (int kk = 0; kk < KSC; ++kk)
@@ -1028,7 +1057,7 @@ struct StateKernelWS {
     for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        *reinterpret_cast<float4 *>(Sh + 16 * n * D + 32 * w + 16 * dt + 4 * x.gq) =
+        *reinterpret_cast<float4 *>(Sh + n * D + 32 * w + 16 * dt + 4 * x.gq) =
             make_float4(st[n][dt][0], st[n][dt][1], st[n][dt][2], st[n][dt][3]);
   }
 
@@ -1090,17 +1119,21 @@ struct StateKernelWS {
         asm volatile("" ::: "memory");
         const char *zt = reinterpret_cast<const char *>(sm.z[m]);
 #pragma unroll
-        for (int n = 0; n < NB; ++n)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int off = ((4 * gq + r) * ROWS + 16 * n + c) * EZ;
-            float zz;
-            if constexpr (DTZ == 0)
-              zz = *reinterpret_cast<const float *>(zt + off);
-            else
-              zz = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(zt + off));
-            sg[n][r] = sigmoidf_(zz);
+        for (int r = 0; r < 4; ++r) {
+          const int off = ((4 * gq + r) * ROWS + 2 * c) * EZ;  // channels 2c, 2c + 1
+          float z0, z1;
+          if constexpr (DTZ == 0) {
+            const uint2 p = *reinterpret_cast<const uint2 *>(zt + off);
+            z0 = __uint_as_float(p.x);
+            z1 = __uint_as_float(p.y);
+          } else {
+            const uint32_t p = *reinterpret_cast<const uint32_t *>(zt + off);
+            z0 = __uint_as_float(p << 16);
+            z1 = __uint_as_float(p & 0xffff0000u);
           }
+          sg[0][r] = sigmoidf_(z0);
+          sg[1][r] = sigmoidf_(z1);
+        }
         asm volatile("" ::: "memory");
       }
       if (!kLast) {
@@ -1136,19 +1169,23 @@ struct StateKernelWS {
         load_gam(x, next, o);
       }
       const int n_valid = valid_of(x, chunk);
+      // Channels 2c and 2c + 1 side by side: one store per token.
 #pragma unroll
-      for (int n = 0; n < NB; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * m + 4 * gq + r;
-          if (!kLast || t < n_valid) {
-            const uint32_t so = 16 * n * ey + r * ystride;
-            if constexpr (DTY == 0)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out[n][r]), ry, yoff, so, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(out[n][r]), ry, yoff, so, 0);
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * m + 4 * gq + r;
+        if (!kLast || t < n_valid) {
+          const uint32_t so = r * ystride;
+          if constexpr (DTY == 0) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = {__float_as_uint(out[0][r]), __float_as_uint(out[1][r])};
+            __builtin_amdgcn_raw_buffer_store_b64(v, ry, yoff, so, 0);
+          } else {
+            const uint32_t v = static_cast<uint32_t>(f32_to_bf16_bits(out[0][r])) |
+                               (static_cast<uint32_t>(f32_to_bf16_bits(out[1][r])) << 16);
+            __builtin_amdgcn_raw_buffer_store_b32(v, ry, yoff, so, 0);
           }
         }
+      }
       __syncthreads();
     };
     // The first chunk runs ahead of the loop so that the loop is entered with
@@ -1228,10 +1265,10 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   x.gq = gq;
   x.o_tok = ((16 * x.m + c) * 32 + 8 * gq) * 2;
   x.o_mat = ((16 * x.m + c) * Cp + 8 * gq) * 2;
-  x.o_zy = 4 * gq * g.H_v * D + c;
+  x.o_zy = 4 * gq * g.H_v * D + 2 * c;  // tile columns n = 0, 1 are rows 2c, 2c + 1
   x.o_gate = (16 * x.m + 4 * gq + (lane & 3)) * 4;
 
-  float *Sh = S + ((static_cast<size_t>(b) * g.H_v + h) * D + ROWS * rb + c) * D;
+  float *Sh = S + ((static_cast<size_t>(b) * g.H_v + h) * D + ROWS * rb + 2 * c) * D;
   if (is_chain)
     K::chain(x, sm, Sh, wave);
   else
