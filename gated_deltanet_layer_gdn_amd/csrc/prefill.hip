@@ -788,21 +788,6 @@ struct StateKernelWS {
     }
   }
 
-  // V of the owned tile, D-register order: lane (c, g) gets channel row
-  // 16 n + c for tokens 16 m + 4 g + r, r = 0..3 (tile rows 16 m + 4 g + r .. + 3).
-  static __device__ __forceinline__ float4 v_tile(const Smem &sm, int buf, int m, int gq, int row,
-                                                  const float (&w)[4]) {
-    const int t0 = 16 * m + 4 * gq;
-    float xs[7];
-#pragma unroll
-    for (int i = 0; i < 7; ++i) xs[i] = xval(sm.XT[buf][t0 + i][row]);
-    float4 v;
-    v.x = siluf_(conv4(w[0], w[1], w[2], w[3], xs[0], xs[1], xs[2], xs[3]));
-    v.y = siluf_(conv4(w[0], w[1], w[2], w[3], xs[1], xs[2], xs[3], xs[4]));
-    v.z = siluf_(conv4(w[0], w[1], w[2], w[3], xs[2], xs[3], xs[4], xs[5]));
-    v.w = siluf_(conv4(w[0], w[1], w[2], w[3], xs[3], xs[4], xs[5], xs[6]));
-    return v;
-  }
 
 
   // Element offset in a token row of KQ of the 16-byte piece `piece` (0..15,
@@ -908,7 +893,6 @@ struct StateKernelWS {
   static __device__ void chain(const Ctx &x, Smem &sm, float *Sh, int w) {
     const int lane = x.lane, m = x.m;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const Split4 none = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
     // State slice d_k = 32w..32w+31 of the block's rows, as S^T tiles.
     f32x4 st[NB][NDT];
 #pragma unroll
@@ -1052,7 +1036,6 @@ struct StateKernelWS {
       o.g = gn;
       __syncthreads();
     }
-    (void)none;
 #pragma unroll
     for (int n = 0; n < NB; ++n)
 #pragma unroll
