@@ -56,8 +56,8 @@ def test_prefill_t4096():
     check_layer("prefill T=4096 C=64", gpu_prefill(wl.geom, I, 64), oracle_run(wl.geom, I))
 
 
-@pytest.mark.parametrize("T,chunk", [(1, 64), (2, 16), (3, 32), (77, 64), (200, 128), (130, 16),
-                                     (781, 64), (1000, 64)])
+@pytest.mark.parametrize("T,chunk", [(1, 64), (2, 16), (3, 32), (77, 64), (128, 64), (150, 64),
+                                     (192, 64), (200, 128), (130, 16), (781, 64), (1000, 64)])
 def test_prefill_ragged_small(T, chunk):
     geom = Geometry(B=2, T=T, H_k=4, H_v=12, d_k=128, d_v=128, zero_state=False)
     I = make_inputs(geom, seed=100 + T)
