@@ -202,7 +202,7 @@ bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *w) {
   w->Tm = take(mat);
   w->P_hi = take(mat);
   w->P_lo = take(split ? mat / 2 : mat);  // e4m3 low halves for the split-role pass
-  w->gates = take(static_cast<size_t>(g.B) * g.H_v * w->NC * 3 * C * 4);
+  w->gates = take(static_cast<size_t>(g.B) * g.H_v * w->NC * 4 * C * 4);
   w->total = off;
   return true;
 }

@@ -33,7 +33,11 @@ struct Geom {
 //   T = (I + A)^{-1}  [B][H_v][NC][C][Cp]      bf16, columns permuted
 //   P = tril(D) * QK^T [B][H_v][NC][C][Cp]     bf16 hi and lo, columns permuted
 //   gates             [B][H_v][NC][3][C]       fp32: gamma_t = exp(G_t),
-//                                               exp(G_last - G_t), beta_t
+//                                               exp(G_last - G_t), beta_t;
+//                     [B][H_v][NC][C][4]       for d = 128, chunk 64: per token
+//                                               gamma_t, exp(G_last - G_t), beta_t,
+//                                               gamma_last (room for 4C per chunk
+//                                               is reserved either way)
 struct PrefillWs {
   int64_t T, T_pad;
   int C, Cp, Dp, NC;

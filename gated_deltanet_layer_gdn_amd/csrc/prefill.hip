@@ -833,14 +833,13 @@ struct StateKernelWS {
   // One dword per lane: sixteen lanes share each group's four values, so
   // the loads return a quarter of what per-lane float4 loads would.
   static __device__ __forceinline__ Gates load_gates(const Ctx &x, int chunk) {
-    const __amdgpu_buffer_rsrc_t r = buf_rsrc(x.gates + static_cast<size_t>(chunk) * 3 * C, kAllBytes);
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(x.gates + static_cast<size_t>(chunk) * 4 * C, kAllBytes);
+    const float4 v = bld<float4>(r, 4 * x.o_gate, 0);
     Gates o;
-    o.gam = bld<float>(r, x.o_gate, 0);
-    o.dl = bld<float>(r, x.o_gate, C * 4);
-    o.bt = bld<float>(r, x.o_gate, 2 * C * 4);
-    uint32_t z0 = 0;
-    asm volatile("" : "+v"(z0));  // a vector offset, so the load stays a vector one
-    o.glast = bld<float>(r, z0, (C - 1) * 4);
+    o.gam = v.x;
+    o.dl = v.y;
+    o.bt = v.z;
+    o.glast = v.w;
     return o;
   }
 
@@ -885,7 +884,7 @@ struct StateKernelWS {
   }
 
   static __device__ __forceinline__ void load_gam(const Ctx &x, int chunk, OutOps &o) {
-    o.gam = bld<float>(buf_rsrc(x.gates + static_cast<size_t>(chunk) * 3 * C, kAllBytes), x.o_gate, 0);
+    o.gam = bld<float>(buf_rsrc(x.gates + static_cast<size_t>(chunk) * 4 * C, kAllBytes), 4 * x.o_gate, 0);
   }
 
 
@@ -1236,7 +1235,7 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   x.Tm = reinterpret_cast<const uint16_t *>(ws + L.Tm) + mat;
   x.Ph = reinterpret_cast<const uint16_t *>(ws + L.P_hi) + mat;
   x.Pl8 = reinterpret_cast<const uint8_t *>(ws + L.P_lo) + mat;
-  x.gates = reinterpret_cast<const float *>(ws + L.gates) + (static_cast<size_t>(b) * g.H_v + h) * L.NC * 3 * C;
+  x.gates = reinterpret_cast<const float *>(ws + L.gates) + (static_cast<size_t>(b) * g.H_v + h) * L.NC * 4 * C;
   const size_t zy = (static_cast<size_t>(b) * L.T * g.H_v + h) * D + ROWS * rb;
   x.z = static_cast<const char *>(z) + zy * K::EZ;
   x.y = static_cast<char *>(y) + zy * (DTY == 0 ? 4 : 2);

@@ -206,12 +206,23 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
 
     // Gate factors of this chunk for the state pass.
     {
-      float *gt = reinterpret_cast<float *>(ws + L.gates) +
-                  ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * 3 * C;
-      for (int t = threadIdx.x; t < C; t += blockDim.x) {
-        gt[t] = __expf(Gs[t]);
-        gt[C + t] = __expf(Gs[C - 1] - Gs[t]);
-        gt[2 * C + t] = Bs[t];
+      if constexpr (D == 128 && C == 64) {
+        // Interleaved per token for the split-role state pass: one 16-byte
+        // load gives a token's gamma, decay to the chunk end, beta and the
+        // chunk's gamma_last.
+        float4 *gt = reinterpret_cast<float4 *>(ws + L.gates) +
+                     ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C;
+        const float glast = __expf(Gs[C - 1]);
+        for (int t = threadIdx.x; t < C; t += blockDim.x)
+          gt[t] = make_float4(__expf(Gs[t]), __expf(Gs[C - 1] - Gs[t]), Bs[t], glast);
+      } else {
+        float *gt = reinterpret_cast<float *>(ws + L.gates) +
+                    ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * 3 * C;
+        for (int t = threadIdx.x; t < C; t += blockDim.x) {
+          gt[t] = __expf(Gs[t]);
+          gt[C + t] = __expf(Gs[C - 1] - Gs[t]);
+          gt[2 * C + t] = Bs[t];
+        }
       }
     }
 
