@@ -36,8 +36,8 @@ ROTATE_BYTES = 512 << 20   # rotated state sets per decode timing
 # file the bench reports the traffic as null until the counters are taken again.
 MEASURED_TRAFFIC = {
     "prefill_state": {"source": "gated_deltanet_layer_gdn_amd/csrc/prefill.hip",
-        "sha256": "12df5f6ea5a0c1c89550a6ee9cb152f44516536d032a91484622aa7cfbdf6d41",
-        "read_bytes": 219727495, "write_bytes": 103845888},
+        "sha256": "fcb6d01f013a420f6469e1f8b7e9865efa454914a00e265fdc97ff181d46978b",
+        "read_bytes": 220512960, "write_bytes": 103845888},
     "decode_b64": {"source": "gated_deltanet_layer_gdn_amd/csrc/decode.hip",
         "sha256": "1cb61099c38a89d236d4e790f0ce552d7b02c440f98cb1d160d6dfff6482c483",
         "read_bytes": 207301072, "write_bytes": 202916593},
