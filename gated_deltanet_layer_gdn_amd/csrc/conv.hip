@@ -19,6 +19,7 @@ namespace gdn {
 
 constexpr int kConvThreads = 128;  // channels per block
 constexpr int kConvTT = 32;        // tokens per block
+constexpr int kConvQKTT = 16;      // tokens per block of the q/k prefill conv
 
 // kOutPrefillQK: the prefill layout for the q and k channels only, without
 // the dim-major k copy (so without the LDS staging buffer, which would cap
@@ -126,6 +127,40 @@ __device__ __forceinline__ void head_scale_128x32(float (&ss)[32], float eps, fl
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int i = 0; i < kConvTT; ++i) ss[i] = bc[w][i];
+}
+
+// The same factors for 16 tokens: 8 + 4 + 2 + 1 exchanges leave lane l with
+// token l / 4, and two more DPP additions (partners l ^ 2, then l ^ 1) finish
+// the lane sums.  Every token's sum runs through the same pairing tree, so a
+// token's factor does not depend on its place in the tile.
+__device__ __forceinline__ void head_scale_128x16(float (&ss)[16], float eps, float sc,
+                                                  float (*red)[16], float (*bc)[16]) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss[i]),
+                                                    __float_as_uint(ss[i + 8]), false, false);
+    ss[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss[i]),
+                                                    __float_as_uint(ss[i + 4]), false, false);
+    ss[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  tr_step<4, 0x140, 8>(ss, lane);
+  tr_step<2, 0x141, 4>(ss, lane);
+  float s = ss[0] + dpp_f<0x4E>(ss[0]);
+  s += dpp_f<0xB1>(s);
+  const int t = lane >> 2;
+  if ((lane & 3) == 0) red[w][t] = s;
+  __syncthreads();
+  const float f = __builtin_amdgcn_rsqf(red[0][t] + red[1][t] + eps) * sc;
+  if ((lane & 3) == 0) bc[w][t] = f;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ss[i] = bc[w][i];
 }
 
 // One thread per channel and kConvTT tokens: the tile's inputs (plus the three
@@ -334,16 +369,18 @@ __global__ __launch_bounds__(kConvThreads, (MODE == kOutPrefillQK && D == 128 ? 
 }
 
 // Prefill conv of the q and k channels at d = 128, one head per block, for
-// NTL consecutive 32-token tiles: the next tile's inputs are loaded while the
-// current tile is computed and stored, so the loads, arithmetic and stores of
-// different tiles overlap inside every wave (with one tile per block all
-// waves run the three phases in lockstep).  Same arithmetic and outputs as
-// conv_kernel's prefill layout.
+// NTL consecutive 16-token tiles: with NTL > 1 the next tile's inputs are
+// loaded while the current tile is computed and stored.  One short tile per
+// block (twice conv_kernel's block count) measured faster than both: the
+// blocks on a CU drift apart, so one block's loads overlap another's
+// arithmetic and stores.  Same conv and output layout as conv_kernel's
+// prefill layout; the head sums add in another order.
 template <int DT, int NTL>
 __global__ __launch_bounds__(kConvThreads) void conv_qk_kernel(Geom g, ConvArgs a) {
-  constexpr int TT = kConvTT, D = 128;
-  __shared__ float red[2][kConvTT];
-  __shared__ float bc[2][kConvTT];
+  constexpr int TT = kConvQKTT, D = 128;
+  static_assert(kConvThreads == 128 && TT == 16, "store pieces sized for 128 threads x 16 tokens");
+  __shared__ float red[2][TT];
+  __shared__ float bc[2][TT];
   const PrefillWs &L = a.L;
   // One grid dimension over (tile group, head), head fastest: the blocks in
   // flight together read whole token rows of x (each block 256 bytes of a row).
@@ -413,7 +450,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_qk_kernel(Geom g, ConvArgs 
       val[t] = siluf_(conv4(w0, w1, w2, w3, xa[t], xa[t + 1], xa[t + 2], xa[t + 3]));
       ss[t] = val[t] * val[t];
     }
-    head_scale_128x32(ss, g.eps, sc, red, bc);
+    head_scale_128x16(ss, g.eps, sc, red, bc);
 #pragma unroll
     for (int t = 0; t < TT; ++t) val[t] *= ss[t];
     if (t0 + TT > a.T) {
@@ -421,10 +458,10 @@ __global__ __launch_bounds__(kConvThreads) void conv_qk_kernel(Geom g, ConvArgs 
       for (int t = 0; t < TT; ++t)
         if (t0 + t >= a.T) val[t] = 0.f;  // padding tokens of the prefill layout
     }
-    // The head's token-major output for the tile is four 2 KB runs of hi
-    // (bf16) and four 1 KB runs of lo (e4m3), one per 32-channel slice:
-    // gather them in LDS, then write 16-byte pieces (six store instructions
-    // per thread instead of 64).
+    // The head's token-major output for the tile is four 1 KB runs of hi
+    // (bf16) and four 512-byte runs of lo (e4m3), one per 32-channel slice:
+    // gather them in LDS, then write 16-byte pieces (three store
+    // instructions per thread instead of 32).
 #pragma unroll
     for (int t = 0; t < TT; t += 2) {
       uint32_t h2;
@@ -437,16 +474,15 @@ __global__ __launch_bounds__(kConvThreads) void conv_qk_kernel(Geom g, ConvArgs 
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int piece = threadIdx.x + kConvThreads * u;  // 16-byte piece of the 8 KB of hi
-      const int sl = piece >> 7, tok = (piece >> 2) & 31, part = piece & 3;
+    for (int u = 0; u < 2; ++u) {
+      const int piece = threadIdx.x + kConvThreads * u;  // 16-byte piece of the 4 KB of hi
+      const int sl = piece >> 6, tok = (piece >> 2) & 15, part = piece & 3;
       uint16_t *dst = phi + ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 8 * part);
       *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stage_hi[sl][tok][8 * part]);
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int piece = threadIdx.x + kConvThreads * u;  // 16-byte piece of the 4 KB of lo
-      const int sl = piece >> 6, tok = (piece >> 1) & 31, part = piece & 1;
+    {
+      const int piece = threadIdx.x;  // 16-byte piece of the 2 KB of lo
+      const int sl = piece >> 5, tok = (piece >> 1) & 15, part = piece & 1;
       uint8_t *dst = plo + ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 16 * part);
       *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stage_lo[sl][tok][16 * part]);
     }
@@ -616,7 +652,7 @@ hipError_t launch_conv_prefill(const Geom &g, const PrefillWs &L, const void *x,
   if (a.write_v) return launch_conv<kOutPrefill, kConvTT>(g, a, s);
   // q and k only (the split-role state pass computes v): d = 128.
   constexpr int NTL = 1;
-  const int64_t tiles = a.T_iter / kConvTT;
+  const int64_t tiles = a.T_iter / kConvQKTT;  // T_pad is a multiple of the 64-token chunk
   dim3 grid(static_cast<unsigned>(2 * g.H_k * ((tiles + NTL - 1) / NTL)), 1, g.B);
   if (g.in_dt == 0)
     hipLaunchKernelGGL((conv_qk_kernel<0, NTL>), grid, dim3(kConvThreads), 0, s, g, a);
