@@ -333,10 +333,23 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
     // e4m3 bytes (|P| <= |q_scale|, so q's scale), at the same element index.
     constexpr bool kLo8 = D == 128 && C == 64;
     uint8_t *Pl8 = reinterpret_cast<uint8_t *>(ws + L.P_lo) + mat;
-    constexpr int ITEMS = C * (Cp / 32) * 4;
+    // The split-role pass reads K step 1 only for rows 32..63 (a row's
+    // product stops at its own 32-column step), so there the pieces of K
+    // step 1 for rows 0..31, all zero, are not stored: 384 items, K step 0 of
+    // every row first.
+    constexpr int ITEMS = kLo8 ? 384 : C * (Cp / 32) * 4;
     for (int it = threadIdx.x; it < ITEMS; it += 256) {
-      const int t = it / (Cp / 8), rem = it % (Cp / 8);
-      const int kk = rem >> 2, q = rem & 3;
+      int t, kk, q;
+      if constexpr (kLo8) {
+        kk = it >> 8;
+        t = 32 * kk + ((it & 255) >> 2);
+        q = it & 3;
+      } else {
+        t = it / (Cp / 8);
+        const int rem = it % (Cp / 8);
+        kk = rem >> 2;
+        q = rem & 3;
+      }
       u16x8 tv8;
       float pv[8];
 #pragma unroll
