@@ -1151,7 +1151,11 @@ struct StateKernelWS {
         load_gam(x, next, o);
       }
       const int n_valid = valid_of(x, chunk);
-      // Channels 2c and 2c + 1 side by side: one store per token.
+      // Channels 2c and 2c + 1 side by side: one store per token.  y is
+      // written once and not read here again: nontemporal stores (cache
+      // policy bit 1) keep it from evicting the operands the blocks share
+      // from L2 (measured: about 4 us faster at T = 4096).
+      constexpr int kYNt = 2;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * m + 4 * gq + r;
@@ -1160,11 +1164,11 @@ struct StateKernelWS {
           if constexpr (DTY == 0) {
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             const u32x2 v = {__float_as_uint(out[0][r]), __float_as_uint(out[1][r])};
-            __builtin_amdgcn_raw_buffer_store_b64(v, ry, yoff, so, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(v, ry, yoff, so, kYNt);
           } else {
             const uint32_t v = static_cast<uint32_t>(f32_to_bf16_bits(out[0][r])) |
                                (static_cast<uint32_t>(f32_to_bf16_bits(out[1][r])) << 16);
-            __builtin_amdgcn_raw_buffer_store_b32(v, ry, yoff, so, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(v, ry, yoff, so, kYNt);
           }
         }
       }
