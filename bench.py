@@ -36,14 +36,14 @@ ROTATE_BYTES = 512 << 20   # rotated state sets per decode timing
 # file the bench reports the traffic as null until the counters are taken again.
 MEASURED_TRAFFIC = {
     "prefill_state": {"source": "gated_deltanet_layer_gdn_amd/csrc/prefill.hip",
-        "sha256": "fcb6d01f013a420f6469e1f8b7e9865efa454914a00e265fdc97ff181d46978b",
-        "read_bytes": 220512960, "write_bytes": 103845888},
+        "sha256": "4278b816ea36e932c8d53f44403afc5035bc16db3a9146f2d24a512898987fe7",
+        "read_bytes": 220512756, "write_bytes": 103845888},
     "decode_b64": {"source": "gated_deltanet_layer_gdn_amd/csrc/decode.hip",
-        "sha256": "1cb61099c38a89d236d4e790f0ce552d7b02c440f98cb1d160d6dfff6482c483",
-        "read_bytes": 207301072, "write_bytes": 202916593},
+        "sha256": "258817b890ec79a39c4c41e16865b1cc76871c0ba79ded590950542eab7be4b3",
+        "read_bytes": 207297221, "write_bytes": 202929184},
     "decode_b1": {"source": "gated_deltanet_layer_gdn_amd/csrc/decode.hip",
-        "sha256": "1cb61099c38a89d236d4e790f0ce552d7b02c440f98cb1d160d6dfff6482c483",
-        "read_bytes": 3376048, "write_bytes": 3170304},
+        "sha256": "258817b890ec79a39c4c41e16865b1cc76871c0ba79ded590950542eab7be4b3",
+        "read_bytes": 3376045, "write_bytes": 3170304},
 }
 
 
