@@ -37,13 +37,13 @@ ROTATE_BYTES = 512 << 20   # rotated state sets per decode timing
 MEASURED_TRAFFIC = {
     "prefill_state": {"source": "gated_deltanet_layer_gdn_amd/csrc/prefill.hip",
         "sha256": "4278b816ea36e932c8d53f44403afc5035bc16db3a9146f2d24a512898987fe7",
-        "read_bytes": 220512756, "write_bytes": 103845888},
+        "read_bytes": 220512960, "write_bytes": 103845888},
     "decode_b64": {"source": "gated_deltanet_layer_gdn_amd/csrc/decode.hip",
-        "sha256": "258817b890ec79a39c4c41e16865b1cc76871c0ba79ded590950542eab7be4b3",
-        "read_bytes": 207297221, "write_bytes": 202929184},
+        "sha256": "51950c41a5f5bf594acc405e8e0ba297df929a0dc536f20ede747bc9aa40e674",
+        "read_bytes": 213097863, "write_bytes": 202900176},
     "decode_b1": {"source": "gated_deltanet_layer_gdn_amd/csrc/decode.hip",
-        "sha256": "258817b890ec79a39c4c41e16865b1cc76871c0ba79ded590950542eab7be4b3",
-        "read_bytes": 3376045, "write_bytes": 3170304},
+        "sha256": "51950c41a5f5bf594acc405e8e0ba297df929a0dc536f20ede747bc9aa40e674",
+        "read_bytes": 3376042, "write_bytes": 3170304},
 }
 
 
