@@ -370,11 +370,12 @@ __global__ __launch_bounds__(kConvThreads, (MODE == kOutPrefillQK && D == 128 ? 
 
 // Prefill conv of the q and k channels at d = 128, one head per block, for
 // NTL consecutive 16-token tiles: with NTL > 1 the next tile's inputs are
-// loaded while the current tile is computed and stored.  One short tile per
-// block (twice conv_kernel's block count) measured faster than both: the
-// blocks on a CU drift apart, so one block's loads overlap another's
-// arithmetic and stores.  Same conv and output layout as conv_kernel's
-// prefill layout; the head sums add in another order.
+// loaded while the current tile is computed and stored.  One 16-token tile
+// per block (NTL = 1, twice conv_kernel's block count) measured faster than
+// 32-token tiles and than several tiles per block: the blocks on a CU drift
+// apart, so one block's loads overlap another's arithmetic and stores.  Same
+// conv and output layout as conv_kernel's prefill layout; the head sums add
+// in another order.
 template <int DT, int NTL>
 __global__ __launch_bounds__(kConvThreads) void conv_qk_kernel(Geom g, ConvArgs a) {
   constexpr int TT = kConvQKTT, D = 128;
