@@ -35,9 +35,14 @@
  *  - the readout uses the updated state; y = o * sigmoid(z).
  *
  * Arithmetic: every value is widened to double on load and all arithmetic is
- * double.  parity unpinned: none of the pages prints a worked example or a
- * test vector, so no stored value comes from them; the test suite pins this
- * code to closed forms, library routines and brute-force products instead.
+ * double.  None of the pages prints a worked example or a test vector, so
+ * no stored value comes from them.  Every function here is pinned instead by
+ * the CPU test suite: the conv against numpy.convolve and identity/shift
+ * taps, the history roll against the last rows, the norm against
+ * numpy.linalg.norm and the epsilon placement, the recurrence against closed
+ * forms (beta = 0 with a = 1 keeps the state, one-hot and orthonormal keys
+ * overwrite, full decay forgets, the per-step retrieval identity) and dense
+ * brute-force products, the layer against its composed stages.
  */
 #include <math.h>
 #include <pthread.h>
