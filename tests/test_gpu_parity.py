@@ -64,6 +64,18 @@ def test_prefill_ragged_small(T, chunk):
     check_layer(f"ragged T={T} C={chunk}", gpu_prefill(geom, I, chunk), oracle_run(geom, I))
 
 
+@pytest.mark.parametrize("H_k,H_v,B", [(1, 1, 1), (2, 4, 1), (3, 3, 2), (1, 5, 1)])
+def test_prefill_head_groupings(H_k, H_v, B):
+    # d = 128, chunk 64 (the split-role passes) with 1, 2 and 5 value heads
+    # per key head, including state-pass grids (4 blocks per value head) that
+    # are not a multiple of 8 blocks; the same tokens through decode steps.
+    geom = Geometry(B=B, T=150, H_k=H_k, H_v=H_v, d_k=128, d_v=128, zero_state=False)
+    I = make_inputs(geom, seed=500 + 10 * H_k + H_v)
+    ref = oracle_run(geom, I)
+    check_layer(f"heads {H_k}/{H_v} B={B} T=150 C=64", gpu_prefill(geom, I, 64), ref)
+    check_layer(f"heads {H_k}/{H_v} B={B} 150 decode steps", gpu_decode_seq(geom, I), ref)
+
+
 @pytest.mark.parametrize("q_scale", [128 ** -0.5, 3.7, -0.5, 1.5e21])
 def test_prefill_q_scale(q_scale):
     # d = 128, chunk 64 keeps the low halves of q and P as e4m3 bytes scaled by
