@@ -76,6 +76,18 @@ def test_prefill_head_groupings(H_k, H_v, B):
     check_layer(f"heads {H_k}/{H_v} B={B} 150 decode steps", gpu_decode_seq(geom, I), ref)
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_prefill_fp32_inputs(chunk):
+    # x, z, the conv weights and history in fp32 at d = 128 (every other
+    # d = 128 case feeds bf16): prefill, then the same tokens as decode steps.
+    geom = Geometry(B=1, T=150, H_k=2, H_v=6, d_k=128, d_v=128, dtype="f32", zero_state=False)
+    I = make_inputs(geom, seed=77)
+    ref = oracle_run(geom, I)
+    check_layer(f"fp32 inputs T=150 C={chunk}", gpu_prefill(geom, I, chunk), ref)
+    if chunk == 64:
+        check_layer("fp32 inputs 150 decode steps", gpu_decode_seq(geom, I), ref)
+
+
 @pytest.mark.parametrize("q_scale", [128 ** -0.5, 3.7, -0.5, 1.5e21])
 def test_prefill_q_scale(q_scale):
     # d = 128, chunk 64 keeps the low halves of q and P as e4m3 bytes scaled by
