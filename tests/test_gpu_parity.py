@@ -88,6 +88,29 @@ def test_prefill_fp32_inputs(chunk):
         check_layer("fp32 inputs 150 decode steps", gpu_decode_seq(geom, I), ref)
 
 
+def test_full_decay_and_zero_input():
+    # Degenerate inputs at d = 128, chunk 64 and as decode steps: a = e^-30
+    # (the state forgets almost everything each token; chunk decays underflow
+    # to zero), then x and the history all zero (q, k and v vanish: the state
+    # only decays and y is exactly zero).
+    geom = Geometry(B=1, T=150, H_k=2, H_v=6, d_k=128, d_v=128, zero_state=False)
+    I = make_inputs(geom, seed=91)
+    I["g"][:] = -30.0
+    ref = oracle_run(geom, I)
+    check_layer("full decay T=150 C=64", gpu_prefill(geom, I, 64), ref)
+    check_layer("full decay 150 decode steps", gpu_decode_seq(geom, I), ref)
+    I0 = make_inputs(geom, seed=92)
+    I0["x"][:] = 0
+    I0["hist"][:] = 0
+    I0["g"] *= 0.05
+    _, S_ref, h_ref = oracle_run(geom, I0)
+    for name, (y, S, h) in (("prefill", gpu_prefill(geom, I0, 64)), ("decode", gpu_decode_seq(geom, I0))):
+        eS = rel_l2(S, S_ref)
+        print(f"[parity] zero input {name}: max|y|={np.abs(y).max():.1e} rel_l2 S={eS:.3e}", flush=True)
+        assert not np.any(y) and eS <= TOL
+        np.testing.assert_array_equal(h, h_ref)
+
+
 @pytest.mark.parametrize("q_scale", [128 ** -0.5, 3.7, -0.5, 1.5e21])
 def test_prefill_q_scale(q_scale):
     # d = 128, chunk 64 keeps the low halves of q and P as e4m3 bytes scaled by
