@@ -122,7 +122,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus "
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus "
               f"{args.gpus}", file=sys.stderr)
         sys.exit(2)
 
