@@ -1,23 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the GDN layer hot path on one MI355X.
 
-One step = one call of gdn_prefill_chunked over the prefill workload
-(B=1, T=4096 tokens, 16 key / 48 value heads, d_k = d_v = 128, chunk 64,
-bf16 inputs, fp32 recurrent state, fp32 y): conv + SiLU + L2 norm, the
-chunk-local prep, the conv history roll and the state pass with the fused
-sigmoid gate.  Inputs are synthetic (gdn_inputs, seed 2) and resident in HBM
-before the timed region.  The same run also times single-token decode at
-B=1 and B=64 (each step on a different state set, rotated so the states do
-not stay in the 256 MB Infinity Cache) and the fp64 CPU oracle on the host.
+Headline step: one call of gdn_prefill_chunked over the long-context prefill
+workload (B=1, T=65536 tokens, 16 key / 48 value heads, d_k = d_v = 128,
+chunk 64, bf16 inputs, fp32 recurrent state, fp32 y), starting from the zero
+initial state: conv + SiLU + L2 norm, the chunk-local prep, the conv history
+roll and the state pass with the fused sigmoid gate.  The step includes
+putting the zero initial state back (a 3 MB device copy), so every timed call
+does the same work.  Inputs are synthetic (gdn_inputs, seed 4) and resident
+in HBM before the timed region.
+
+The same run reports, each as its own leg: the same workload at chunk 128,
+the T=4096 prefill workload, single-token decode at B=1 and B=64 (captured
+HIP graphs, each step on a different state set, rotated so that the states
+do not stay in the 256 MB Infinity Cache), cold-cache repetitions of every
+prefill leg (a 512 MiB device write between repetitions), and the fp64 CPU
+oracle on the host's cores.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -28,22 +37,19 @@ METRIC = "GDN prefill tokens/s + decode steps/s (1 GPU), % of MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 ROTATE_BYTES = 512 << 20   # rotated state sets per decode timing
+COLD_BYTES = 512 << 20     # device write between cold repetitions
+CSRC = os.path.join(ROOT, "gated_deltanet_layer_gdn_amd", "csrc")
 
-# HBM bytes per launch of the roofline kernels, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE runs scaled by the same counters on a 1 GiB device copy (the
-# summaries under profiles/ give the commands and figures).  Each entry holds
-# for the kernel source with the given SHA-256 only; after any change to that
-# file the bench reports the traffic as null until the counters are taken again.
+# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs (one
+# counter per run), scaled by what the same counters read on a 1 GiB device
+# copy (reads x2, writes x1; the summaries under profiles/ give the commands
+# and the raw figures).  They hold for the kernel sources whose combined
+# SHA-256 is recorded with them; after any change under csrc/ the bench
+# reports the traffic as null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    "prefill_state": {"source": "gated_deltanet_layer_gdn_amd/csrc/prefill.hip",
-        "sha256": "4278b816ea36e932c8d53f44403afc5035bc16db3a9146f2d24a512898987fe7",
-        "read_bytes": 220512960, "write_bytes": 103845888},
-    "decode_b64": {"source": "gated_deltanet_layer_gdn_amd/csrc/decode.hip",
-        "sha256": "51950c41a5f5bf594acc405e8e0ba297df929a0dc536f20ede747bc9aa40e674",
-        "read_bytes": 213097863, "write_bytes": 202900176},
-    "decode_b1": {"source": "gated_deltanet_layer_gdn_amd/csrc/decode.hip",
-        "sha256": "51950c41a5f5bf594acc405e8e0ba297df929a0dc536f20ede747bc9aa40e674",
-        "read_bytes": 3376042, "write_bytes": 3170304},
+    "csrc_sha256": None,
+    # leg -> {kernel: (read_bytes, write_bytes)}
+    "legs": {},
 }
 
 
@@ -51,46 +57,50 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(key):
-    """Measured HBM bytes per launch (read + write), or None if the kernel
-    source changed since the counters were taken."""
-    import hashlib
-    e = MEASURED_TRAFFIC.get(key)
-    if not e or e["sha256"] is None:
+def csrc_sha256() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(leg):
+    """Measured HBM bytes per call of a leg (read + write over its kernels),
+    or None if the sources changed since the counters were taken."""
+    e = MEASURED_TRAFFIC["legs"].get(leg)
+    if not e or MEASURED_TRAFFIC["csrc_sha256"] != csrc_sha256():
         return None
-    with open(os.path.join(ROOT, e["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != e["sha256"]:
-            return None
-    return e["read_bytes"] + e["write_bytes"]
+    return int(sum(r + w for r, w in e.values()))
 
 
 def prefill_flops_per_token(H_k, H_v, d_k, d_v, C):
-    """Algorithmic flops of the whole chunked prefill per token (triangular
-    products at triangular size, K K^T and Q K^T once per key head)."""
+    """Algorithmic flops of the whole chunked prefill per token: per value head
+    C^2/3 (the triangular inverse), (C-1)(d_k+d_v) (the triangular products of
+    the WY factors), 6 d_k d_v (K S^T, Q S^T and the state update),
+    (C+1) d_v (P U and the gate); per key head 2 C d_k (K K^T, Q K^T)."""
     return (H_v * (C * C / 3 + (C - 1) * (d_k + d_v) + 6 * d_k * d_v + (C + 1) * d_v)
             + H_k * (2 * C * d_k))
 
 
+def prefill_bytes_per_token(C_ch, H_v, d_v, in_bytes, out_bytes):
+    """Algorithmic HBM bytes per token of the whole prefill: x and z read
+    once, g and beta read once, y written once (the state in and out is
+    added per call)."""
+    return C_ch * in_bytes + H_v * d_v * in_bytes + 2 * H_v * 4 + H_v * d_v * out_bytes
+
+
 def state_pass_flops_per_token(H_v, d_k, d_v, C):
-    """Algorithmic flops of the state-pass kernel per token: K S^T, Q S^T and
-    the rank-C state update (2 d_k d_v each) plus (I+A)^{-1} R and P U
+    """Algorithmic flops of the state-pass kernel alone per token: K S^T, Q S^T
+    and the rank-C state update (2 d_k d_v each) plus (I+A)^{-1} R and P U
     (triangular, C d_v each)."""
     return H_v * (6 * d_k * d_v + 2 * C * d_v)
 
 
 def state_pass_bytes_per_token(H_v, d_v, in_bytes, out_bytes):
-    """Algorithmic HBM bytes per token of the state-pass kernel: the v
-    channels of x and z read once, g and beta read once, y written once (the
-    state in and out is added per launch).  The chunk-local intermediates it
-    also reads (q, k, (I+A)^{-1}, P, gate table) are this design's, not the
-    method's, and are not counted."""
+    """Algorithmic HBM bytes per token of the state-pass kernel alone: the v
+    channels of x and z, g and beta, y (the state in and out per call)."""
     return H_v * d_v * in_bytes + H_v * d_v * in_bytes + 2 * H_v * 4 + H_v * d_v * out_bytes
-
-
-def prefill_bytes_per_token(C_ch, H_v, d_v, in_bytes, out_bytes):
-    """Algorithmic HBM bytes per token of a fully fused prefill: x and z read
-    once, g and beta read once, y written once."""
-    return C_ch * in_bytes + H_v * d_v * in_bytes + 2 * H_v * 4 + H_v * d_v * out_bytes
 
 
 def decode_kernel_bytes_per_seq(H_v, d_k, d_v, in_bytes, out_bytes):
@@ -106,15 +116,35 @@ def decode_step_bytes_per_seq(C_ch, H_v, d_k, d_v, in_bytes, out_bytes):
             + 2 * 3 * C_ch * in_bytes + C_ch * in_bytes)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def fractions(F, Bytes, t_s):
+    mf = F / (t_s * PEAK_BF16_TFLOPS * 1e12)
+    hf = Bytes / (t_s * PEAK_HBM_GBS * 1e9)
+    return {"mfma": round(mf, 4), "hbm": round(hf, 4), "roofline": round(max(mf, hf), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--chunk", type=int, default=64, help="chunk size of the headline leg")
+    ap.add_argument("--cold-reps", type=int, default=10)
     ap.add_argument("--decode-rounds", type=int, default=5,
                     help="graph replays per decode timing (each replays R rotated steps)")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--legs", default="all",
+                    help="comma list of: long64, long128, t4096, decode_b1, decode_b64, cpu "
+                         "(default all); the headline leg always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run --steps plain device copies of MIB MiB (for scaling the HBM "
@@ -149,88 +179,142 @@ def main():
                           "copies": args.steps}), flush=True)
         return
 
+    legs = set(args.legs.split(",")) if args.legs != "all" else {
+        "long64", "long128", "t4096", "decode_b1", "decode_b64", "cpu"}
+    if args.no_cpu_baseline:
+        legs.discard("cpu")
+    head_leg = "long64" if args.chunk == 64 else "long128"
+    if args.chunk not in (64, 128):
+        raise SystemExit("--chunk must be 64 or 128 (the long-context workload's chunk sizes)")
+    legs.add(head_leg)
+
     def dev(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    # ------------------------------------------------------------ prefill
-    wl, I = workload_inputs(2)
-    G = wl.geom
-    C = args.chunk
-    d = gdn.Dims(B=G.B, H_k=G.H_k, H_v=G.H_v, d_k=G.d_k, d_v=G.d_v, W=G.W, in_dtype=gdn.BF16,
-                 out_dtype=gdn.F32)
-    D = {k: dev(v) for k, v in I.items()}
-    y = torch.empty((G.B, G.T, G.H_v, G.d_v), dtype=torch.float32, device="cuda")
-    ws = torch.empty(gdn.prefill_workspace_bytes(d, G.T, C), dtype=torch.uint8, device="cuda")
-    log(f"[bench] prefill workload: {wl.name}, chunk {C}, workspace {ws.numel() / 2**20:.1f} MiB")
+    cold_buf = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device="cuda")
 
-    def prefill(kernel_ms=None):
-        gdn.prefill_chunked(d, D["x"], D["z"], D["g"], D["beta"], D["w"], D["hist"], D["S"],
-                            chunk=C, y=y, ws=ws, kernel_ms=kernel_ms)
+    def prefill_leg(wl, I, C, steps, warmup):
+        """Warm back-to-back steps (the contract's K timed steps), per-kernel
+        durations from the library's HIP events, and cold repetitions."""
+        G = wl.geom
+        d = gdn.Dims(B=G.B, H_k=G.H_k, H_v=G.H_v, d_k=G.d_k, d_v=G.d_v, W=G.W,
+                     in_dtype=gdn.BF16, out_dtype=gdn.F32)
+        D = {k: dev(v) for k, v in I.items()}
+        S0, h0 = D["S"].clone(), D["hist"].clone()
+        y = torch.empty((G.B, G.T, G.H_v, G.d_v), dtype=torch.float32, device="cuda")
+        ws = torch.empty(gdn.prefill_workspace_bytes(d, G.T, C), dtype=torch.uint8, device="cuda")
+        log(f"[bench] prefill {wl.name}, chunk {C}, workspace {ws.numel() / 2**20:.1f} MiB")
 
-    for _ in range(args.warmup):
-        prefill()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(args.steps):
-        prefill()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    tok_s = G.B * G.T / (ms_step * 1e-3)
-    log(f"[bench] prefill: {ms_step * 1e3:.1f} us/step, {tok_s:.4g} tokens/s")
+        def step(kernel_ms=None):
+            D["S"].copy_(S0)
+            D["hist"].copy_(h0)
+            gdn.prefill_chunked(d, D["x"], D["z"], D["g"], D["beta"], D["w"], D["hist"], D["S"],
+                                chunk=C, y=y, ws=ws, kernel_ms=kernel_ms)
 
-    names = ["conv", "prep", "state"]
-    per = {n: [] for n in names}
-    for _ in range(args.steps):
-        km = []
-        prefill(kernel_ms=km)
-        for n, v in zip(names, km):
-            per[n].append(v)
-    kern_ms = {n: float(np.mean(v)) for n, v in per.items()}
-    log("[bench] prefill kernels (us): " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in kern_ms.items()))
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        names = ["conv", "prep", "state"]
+        per = {n: [] for n in names}
+        for _ in range(max(steps, 5)):
+            km = []
+            step(kernel_ms=km)
+            for n, v in zip(names, km):
+                per[n].append(v)
+        kern = {n: float(np.mean(v)) for n, v in per.items()}
+        cold = []
+        for r in range(args.cold_reps):
+            D["S"].copy_(S0)
+            D["hist"].copy_(h0)
+            cold_buf.fill_(float(r))
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record()
+            gdn.prefill_chunked(d, D["x"], D["z"], D["g"], D["beta"], D["w"], D["hist"], D["S"],
+                                chunk=C, y=y, ws=ws)
+            c1.record()
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1))
+        ntok = G.B * G.T
+        F = prefill_flops_per_token(G.H_k, G.H_v, G.d_k, G.d_v, C) * ntok
+        state_bytes = G.B * G.H_v * G.d_v * G.d_k * 4
+        Bytes = prefill_bytes_per_token(G.C_ch, G.H_v, G.d_v, 2, 4) * ntok + 2 * state_bytes
+        t_kern = sum(kern.values()) * 1e-3
+        ach = Bytes / t_kern / 1e9
+        F_st = state_pass_flops_per_token(G.H_v, G.d_k, G.d_v, C) * ntok
+        B_st = state_pass_bytes_per_token(G.H_v, G.d_v, 2, 4) * ntok + 2 * state_bytes
+        t_st = kern["state"] * 1e-3
+        res = {
+            "workload": f"GDN prefill B={G.B} T={G.T} H_k={G.H_k} H_v={G.H_v} d_k=d_v={G.d_k} "
+                        f"chunk={C}, bf16 in, fp32 state, fp32 y, zero initial state",
+            "tokens_per_s": round(ntok / (ms * 1e-3), 1),
+            "us_per_step": round(ms * 1e3, 2),
+            "cold": {"reps": len(cold), "median_us": round(float(np.median(cold)) * 1e3, 2),
+                     "min_us": round(float(np.min(cold)) * 1e3, 2),
+                     "tokens_per_s_median": round(ntok / (float(np.median(cold)) * 1e-3), 1),
+                     "protocol": f"{COLD_BYTES >> 20} MiB device write before each call"},
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+            "step_fractions": fractions(F, Bytes, ms * 1e-3),
+            "roofline": {
+                "bound": "hbm" if Bytes * PEAK_BF16_TFLOPS * 1e12 > F * PEAK_HBM_GBS * 1e9
+                else "mfma",
+                "kernel": "gdn_prefill_chunked: conv_qk_kernel + prep_kernel + state_kernel_ws"
+                          if C == 64 else
+                          "gdn_prefill_chunked: conv_kernel + prep_kernel + state_kernel",
+                "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": None,
+                "alg_bytes_per_call": int(Bytes), "alg_flops_per_call": int(F),
+                "arithmetic_intensity": round(F / Bytes, 1),
+                "mfma_frac": round(F / t_kern / (PEAK_BF16_TFLOPS * 1e12), 4),
+                "avg_call_us": round(t_kern * 1e6, 2),
+            },
+            "state_pass": {
+                "kernel": "state_kernel_ws" if C == 64 else "state_kernel",
+                "alg_bytes": int(B_st), "alg_flops": int(F_st),
+                "hbm_frac": round(B_st / t_st / (PEAK_HBM_GBS * 1e9), 4),
+                "mfma_frac": round(F_st / t_st / (PEAK_BF16_TFLOPS * 1e12), 4),
+                "avg_launch_us": round(kern["state"] * 1e3, 2),
+            },
+        }
+        log(f"[bench] prefill T={G.T} C={C}: {ms * 1e3:.1f} us/step warm, cold median "
+            f"{res['cold']['median_us']:.1f} us; kernels (us) " +
+            ", ".join(f"{n} {v * 1e3:.1f}" for n, v in kern.items()) +
+            f"; whole-call {ach:.0f} GB/s = {ach / PEAK_HBM_GBS:.3f} of HBM peak")
+        del D, y, ws, S0, h0
+        torch.cuda.empty_cache()
+        return res
 
-    F_step = prefill_flops_per_token(G.H_k, G.H_v, G.d_k, G.d_v, C) * G.B * G.T
-    B_step = prefill_bytes_per_token(G.C_ch, G.H_v, G.d_v, 2, 4) * G.B * G.T + 2 * (
-        G.B * G.H_v * G.d_v * G.d_k * 4)
-    t_s = ms_step * 1e-3
-    step_frac = {
-        "mfma": F_step / (t_s * PEAK_BF16_TFLOPS * 1e12),
-        "hbm": B_step / (t_s * PEAK_HBM_GBS * 1e9),
-    }
-    step_frac["roofline"] = max(step_frac["mfma"], step_frac["hbm"])
-    # Dominant kernel: the state pass.  Its binding roofline is the larger of
-    # its MFMA time and its HBM time at the published peaks; with an
-    # arithmetic intensity below the ridge (2500 TFLOP/s / 8 TB/s = 312.5
-    # flop/B) that is HBM.
-    F_state = state_pass_flops_per_token(G.H_v, G.d_k, G.d_v, C) * G.B * G.T
-    B_state = state_pass_bytes_per_token(G.H_v, G.d_v, 2, 4) * G.B * G.T + 2 * (
-        G.B * G.H_v * G.d_v * G.d_k * 4)
-    t_state = kern_ms["state"] * 1e-3
-    mfma_frac = F_state / (t_state * PEAK_BF16_TFLOPS * 1e12)
-    hbm_frac = B_state / (t_state * PEAK_HBM_GBS * 1e9)
-    if hbm_frac >= mfma_frac:
-        achieved = B_state / t_state / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        achieved = F_state / t_state / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roofline.update({"traffic": measured_traffic("prefill_state"),
-                     "kernel": "state_kernel_ws (state pass + gate)",
-                     "bytes_per_launch": B_state, "flops_per_launch": F_state,
-                     "arithmetic_intensity": round(F_state / B_state, 1),
-                     "mfma_frac": round(mfma_frac, 4), "hbm_frac": round(hbm_frac, 4),
-                     "avg_launch_us": round(kern_ms["state"] * 1e3, 2)})
+    out_legs = {}
+    wl4 = I4 = None
+    if legs & {"long64", "long128", "cpu"}:
+        t = time.perf_counter()
+        wl4, I4 = workload_inputs(4)
+        log(f"[bench] long-context inputs drawn in {time.perf_counter() - t:.1f} s")
+    for leg, C in (("long64", 64), ("long128", 128)):
+        if leg in legs:
+            out_legs[leg] = prefill_leg(wl4, I4, C, args.steps, args.warmup)
+    if "t4096" in legs:
+        wl2, I2 = workload_inputs(2)
+        out_legs["t4096"] = prefill_leg(wl2, I2, 64, args.steps, args.warmup)
+        del I2
+    for leg, res in out_legs.items():
+        res["roofline"]["traffic"] = measured_traffic(leg)
 
     # ------------------------------------------------------------ decode
     decode = {}
     copy_gbs = None
-    if not args.no_decode:
+    if legs & {"decode_b1", "decode_b64"}:
         # Attainable streaming rate on this GPU: a 1 GiB device-to-device copy.
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -246,111 +330,131 @@ def main():
         copy_gbs = 2 * (1 << 30) / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9
         del src, dst
         log(f"[bench] device copy 1 GiB: {copy_gbs:.0f} GB/s (read + write)")
-        for idx, key in ((1, "b1"), (3, "b64")):
-            wl_d, Id = workload_inputs(idx)
-            Gd = wl_d.geom
-            dd = gdn.Dims(B=Gd.B, H_k=Gd.H_k, H_v=Gd.H_v, d_k=Gd.d_k, d_v=Gd.d_v, W=Gd.W,
-                          in_dtype=gdn.BF16, out_dtype=gdn.F32)
-            state_bytes = Id["S"].nbytes
-            R = max(2, math.ceil(ROTATE_BYTES / state_bytes))
-            Dd = {k: dev(v) for k, v in Id.items()}
-            Ss = [Dd["S"].clone() for _ in range(R)]
-            Hs = [Dd["hist"].clone() for _ in range(R)]
-            yd = torch.empty((Gd.B, Gd.H_v, Gd.d_v), dtype=torch.float32, device="cuda")
-            wsd = torch.empty(gdn.decode_workspace_bytes(dd), dtype=torch.uint8, device="cuda")
-            x1 = Dd["x"].reshape(Gd.B, Gd.C_ch)
-            z1 = Dd["z"].reshape(Gd.B, Gd.H_v, Gd.d_v)
-            g1 = Dd["g"].reshape(Gd.B, Gd.H_v)
-            b1 = Dd["beta"].reshape(Gd.B, Gd.H_v)
+    for idx, key in ((1, "b1"), (3, "b64")):
+        if "decode_" + key not in legs:
+            continue
+        wl_d, Id = workload_inputs(idx)
+        Gd = wl_d.geom
+        dd = gdn.Dims(B=Gd.B, H_k=Gd.H_k, H_v=Gd.H_v, d_k=Gd.d_k, d_v=Gd.d_v, W=Gd.W,
+                      in_dtype=gdn.BF16, out_dtype=gdn.F32)
+        state_bytes = Id["S"].nbytes
+        R = max(2, math.ceil(ROTATE_BYTES / state_bytes))
+        Dd = {k: dev(v) for k, v in Id.items()}
+        Ss = [Dd["S"].clone() for _ in range(R)]
+        Hs = [Dd["hist"].clone() for _ in range(R)]
+        yd = torch.empty((Gd.B, Gd.H_v, Gd.d_v), dtype=torch.float32, device="cuda")
+        wsd = torch.empty(gdn.decode_workspace_bytes(dd), dtype=torch.uint8, device="cuda")
+        x1 = Dd["x"].reshape(Gd.B, Gd.C_ch)
+        z1 = Dd["z"].reshape(Gd.B, Gd.H_v, Gd.d_v)
+        g1 = Dd["g"].reshape(Gd.B, Gd.H_v)
+        b1 = Dd["beta"].reshape(Gd.B, Gd.H_v)
 
-            def step(r, kernel_ms=None):
-                gdn.decode_step(dd, x1, z1, g1, b1, Dd["w"], Hs[r], Ss[r], y=yd, ws=wsd,
-                                kernel_ms=kernel_ms)
+        def dstep(r, kernel_ms=None):
+            gdn.decode_step(dd, x1, z1, g1, b1, Dd["w"], Hs[r], Ss[r], y=yd, ws=wsd,
+                            kernel_ms=kernel_ms)
 
-            for r in range(R):  # warm-up, and the graph's first capture is clean
-                step(r)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for r in range(R):
-                    step(r)
-            graph.replay()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(args.decode_rounds):
-                graph.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            ms_dec = e0.elapsed_time(e1) / (args.decode_rounds * R)
-            # eager (one Python call per step) for reference
-            e0.record()
+        for r in range(R):  # warm-up, and the graph's first capture is clean
+            dstep(r)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
             for r in range(R):
-                step(r)
-            e1.record()
-            torch.cuda.synchronize()
-            ms_eager = e0.elapsed_time(e1) / R
-            kms = {"conv": [], "state": []}
-            for i in range(max(4 * R, 12)):
-                km = []
-                step(i % R, kernel_ms=km)
-                kms["conv"].append(km[0])
-                kms["state"].append(km[1])
-            k_state = float(np.mean(kms["state"]))
-            kb = decode_kernel_bytes_per_seq(Gd.H_v, Gd.d_k, Gd.d_v, 2, 4) * Gd.B
-            sb = decode_step_bytes_per_seq(Gd.C_ch, Gd.H_v, Gd.d_k, Gd.d_v, 2, 4) * Gd.B
-            ach = kb / (k_state * 1e-3) / 1e9
-            decode[key] = {
-                "workload": wl_d.name, "steps_per_s": round(1e3 / ms_dec, 1),
-                "seq_steps_per_s": round(Gd.B * 1e3 / ms_dec, 1), "us_per_step": round(ms_dec * 1e3, 3),
-                "us_per_step_eager": round(ms_eager * 1e3, 3), "rotated_state_sets": R,
-                "step_hbm_frac": round(sb / (ms_dec * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
-                "kernels_us": {"conv": round(float(np.mean(kms["conv"])) * 1e3, 3),
-                               "state": round(k_state * 1e3, 3)},
-                "roofline": {"bound": "hbm", "kernel": "decode_kernel (state stream + gate)",
-                             "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": round(ach / PEAK_HBM_GBS, 4),
-                             "traffic": measured_traffic("decode_" + key),
-                             "bytes_per_launch": kb,
-                             "attainable_copy_GBs": round(copy_gbs, 1),
-                             "frac_of_copy": round(ach / copy_gbs, 4)},
-            }
-            log(f"[bench] decode {key}: {ms_dec * 1e3:.2f} us/step (graph), {ms_eager * 1e3:.2f} "
-                f"eager; state kernel {k_state * 1e3:.2f} us = {ach:.0f} GB/s")
-            del Ss, Hs, Dd
+                dstep(r)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.decode_rounds):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_dec = e0.elapsed_time(e1) / (args.decode_rounds * R)
+        e0.record()
+        for r in range(R):
+            dstep(r)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_eager = e0.elapsed_time(e1) / R
+        kms = []
+        for i in range(max(4 * R, 12)):
+            km = []
+            dstep(i % R, kernel_ms=km)
+            kms.append(km)
+        kmean = [float(np.mean([k[j] for k in kms])) for j in range(len(kms[0]))]
+        k_state = kmean[-1]
+        kb = decode_kernel_bytes_per_seq(Gd.H_v, Gd.d_k, Gd.d_v, 2, 4) * Gd.B
+        sb = decode_step_bytes_per_seq(Gd.C_ch, Gd.H_v, Gd.d_k, Gd.d_v, 2, 4) * Gd.B
+        ach = kb / (k_state * 1e-3) / 1e9
+        decode[key] = {
+            "workload": wl_d.name, "steps_per_s": round(1e3 / ms_dec, 1),
+            "seq_steps_per_s": round(Gd.B * 1e3 / ms_dec, 1), "us_per_step": round(ms_dec * 1e3, 3),
+            "us_per_step_eager": round(ms_eager * 1e3, 3), "rotated_state_sets": R,
+            "step_hbm_frac": round(sb / (ms_dec * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+            "step_alg_bytes": int(sb),
+            "kernels_us": [round(v * 1e3, 3) for v in kmean],
+            "roofline": {"bound": "hbm", "kernel": "decode state stream + gate",
+                         "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("decode_" + key),
+                         "alg_bytes_per_launch": int(kb),
+                         "attainable_copy_GBs": round(copy_gbs, 1),
+                         "frac_of_copy": round(ach / copy_gbs, 4)},
+        }
+        log(f"[bench] decode {key}: {ms_dec * 1e3:.2f} us/step (graph), {ms_eager * 1e3:.2f} "
+            f"eager; state kernel {k_state * 1e3:.2f} us = {ach:.0f} GB/s")
+        del Ss, Hs, Dd
 
     # ------------------------------------------------------------ CPU oracle
     cpu = None
-    if not args.no_cpu_baseline:
+    if "cpu" in legs:
         import oracle
+        G4 = wl4.geom
         nth = oracle.default_threads()
-        passes = 3
-        t = time.perf_counter()
-        for _ in range(passes):
-            oracle.layer(I["x"], I["z"], I["g"], I["beta"], I["w"], I["hist"], I["S"], H_k=G.H_k,
-                         H_v=G.H_v, d_k=G.d_k, d_v=G.d_v, eps=d.l2_eps, nthreads=nth)
-        dt = time.perf_counter() - t
-        cpu = {"value": round(passes * G.B * G.T / dt, 1), "unit": "tokens/s", "cores": nth,
-               "kind": "oracle",
-               "sample": f"the whole prefill workload (B=1, T={G.T}, all {G.H_v} value heads) "
-                         f"through the fp64 oracle {passes} times, {dt:.2f} s wall on {nth} "
-                         f"threads"}
-        log(f"[bench] cpu oracle: {cpu['value']:.1f} tokens/s on {nth} threads ({passes} passes, {dt:.2f} s)")
+        try:
+            host_cpus = len(os.sched_getaffinity(0))
+        except AttributeError:  # pragma: no cover
+            host_cpus = os.cpu_count()
 
+        def run(T_s, heads, nthreads):
+            sl = {k: np.ascontiguousarray(I4[k][:, :T_s]) for k in ("x", "z", "g", "beta")}
+            t = time.perf_counter()
+            oracle.layer(sl["x"], sl["z"], sl["g"], sl["beta"], I4["w"], I4["hist"], I4["S"],
+                         H_k=G4.H_k, H_v=G4.H_v, d_k=G4.d_k, d_v=G4.d_v, eps=1e-6,
+                         heads=heads, nthreads=nthreads)
+            return time.perf_counter() - t
+
+        T_mt = 16384
+        dt = run(T_mt, None, nth)
+        T_1, h_1 = 2048, 8
+        dt1 = run(T_1, [(0, h) for h in range(h_1)], 1)
+        rate1 = T_1 * h_1 / G4.H_v / dt1
+        cpu = {"value": round(T_mt / dt, 1), "unit": "tokens/s", "cores": nth, "kind": "oracle",
+               "sample": f"the first {T_mt} tokens of the long-context workload, all {G4.H_v} "
+                         f"value heads, through the fp64 oracle: {dt:.2f} s wall on {nth} threads",
+               "cpu_model": cpu_model(), "host_cpus": host_cpus,
+               "one_thread_tokens_per_s": round(rate1, 1),
+               "one_thread_sample": f"{T_1} tokens x {h_1} of {G4.H_v} value heads on 1 thread "
+                                    f"({dt1:.2f} s), scaled to whole-layer tokens"}
+        log(f"[bench] cpu oracle: {cpu['value']:.1f} tokens/s on {nth} threads, "
+            f"{rate1:.1f} on 1 thread ({cpu['cpu_model']})")
+
+    H = out_legs[head_leg]
+    G4 = wl4.geom
     out = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "metric": METRIC, "value": H["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(H["us_per_step"] / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "precision": "bf16 MFMA on hi/lo split operands, fp32 accumulation, fp32 state and y",
+        "precision": "bf16 MFMA (fp32 accumulation) on split operands x = hi + lo: hi bf16, lo "
+                     "bf16 or, for q, k and P on the d=128 chunk-64 path, scaled e4m3 bytes "
+                     "(about 13 significant bits in all); (I+A)^-1 plain bf16; fp32 state, "
+                     "fp32 y",
         "data": "synthetic",
-        "config": {"workload": f"GDN prefill B={G.B} T={G.T} H_k={G.H_k} H_v={G.H_v} "
-                               f"d_k=d_v={G.d_k} chunk={C}, bf16 in, fp32 state, fp32 y",
-                   "B": G.B, "T": G.T, "H_k": G.H_k, "H_v": G.H_v, "d_k": G.d_k, "d_v": G.d_v,
-                   "chunk": C},
-        "roofline": roofline,
-        "step_fractions": {k: round(v, 4) for k, v in step_frac.items()},
-        "prefill_kernels_us": {k: round(v * 1e3, 2) for k, v in kern_ms.items()},
+        "config": {"workload": H["workload"], "B": G4.B, "T": G4.T, "H_k": G4.H_k,
+                   "H_v": G4.H_v, "d_k": G4.d_k, "d_v": G4.d_v, "chunk": args.chunk},
+        "roofline": H["roofline"],
+        "step_fractions": H["step_fractions"],
+        "prefill": out_legs,
         "decode": decode,
         "cpu_baseline": cpu,
     }

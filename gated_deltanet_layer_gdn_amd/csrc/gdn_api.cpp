@@ -21,7 +21,11 @@ namespace {
 
 thread_local std::string g_last_hip_error;
 
-constexpr int64_t kMaxTokens = int64_t(1) << 28;  // keeps every per-call index in range
+// Largest T per call.  The split-role state pass addresses the four 32-wide
+// d_k slices of q and k as one buffer base plus a 32-bit scalar offset of up
+// to 3 * T_pad * 64 bytes; 2^24 tokens keep that below 2^32 (the first T to
+// wrap would be about 22.4M).  Every other per-call index is 64-bit.
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
 constexpr int kMaxBatch = 65535;                  // grid z / y limits
 
 int set_hip_error(hipError_t e, const char *where) {

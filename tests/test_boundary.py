@@ -79,8 +79,8 @@ def test_size_queries(lib, dims):
     w = [lib.gdn_prefill_workspace_bytes(b, T, 64) for T in (1, 64, 65, 1000)]
     assert all(x > 0 for x in w) and w == sorted(w)
     assert lib.gdn_prefill_workspace_bytes(b, 0, 64) == 0
-    assert lib.gdn_prefill_workspace_bytes(b, 1 << 28, 64) > 0  # the largest T accepted
-    assert lib.gdn_prefill_workspace_bytes(b, (1 << 28) + 1, 64) == 0
+    assert lib.gdn_prefill_workspace_bytes(b, 1 << 24, 64) > 0  # the largest T accepted
+    assert lib.gdn_prefill_workspace_bytes(b, (1 << 24) + 1, 64) == 0
     assert lib.gdn_prefill_workspace_bytes(b, 64, 48) == 0
     for C in (16, 32, 64, 128):
         assert lib.gdn_prefill_workspace_bytes(b, 100, C) > 0
@@ -148,7 +148,7 @@ def test_prefill_rejects_and_leaves_buffers_untouched(lib, dims):
     for over, want in cases:
         assert prefill_call(lib, d, T, C, b, **over) == want, over
     assert prefill_call(lib, d, 0, C, b) == INVALID
-    assert prefill_call(lib, d, (1 << 28) + 1, C, b) == INVALID  # past the largest T
+    assert prefill_call(lib, d, (1 << 24) + 1, C, b) == INVALID  # past the largest T
     assert prefill_call(lib, d, T, 48, b) == UNSUPPORTED
     assert prefill_call(lib, d, T, 8, b) == UNSUPPORTED
     for field, val, want in [("abi", 2, UNSUPPORTED), ("d_k", 64, UNSUPPORTED),

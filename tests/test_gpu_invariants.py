@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 
 from gdn_inputs import Geometry, make_inputs, workload_inputs
-from gdn_testlib import (TOL, dev_inputs, dims_of, from_dev, gpu_decode_seq, gpu_prefill,
-                         oracle_run, rel_l2)
+from gdn_testlib import (TOL, check_errors, dev_inputs, dims_of, from_dev, gpu_decode_seq,
+                         gpu_prefill, oracle_run, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,9 +44,7 @@ def test_prefill_equals_decode_steps_t4096():
     wl, I = workload_inputs(2)
     yp, Sp, hp = gpu_prefill(wl.geom, I, 64)
     yd, Sd, hd = gpu_decode_seq(wl.geom, I)
-    ey, eS = rel_l2(yp, yd), rel_l2(Sp, Sd)
-    print(f"[invariant] prefill vs 4096 decode steps: y={ey:.3e} S={eS:.3e}", flush=True)
-    assert ey <= TOL and eS <= TOL
+    check_errors("prefill vs 4096 decode steps", yp, yd, Sp, Sd)
     np.testing.assert_array_equal(hp, hd)
 
 
@@ -55,9 +53,7 @@ def test_chunk_sizes_agree():
     ref = oracle_run(geom, I)
     outs = {C: gpu_prefill(geom, I, C) for C in (16, 32, 64, 128)}
     for C, (y, S, h) in outs.items():
-        ey, eS = rel_l2(y, ref[0]), rel_l2(S, ref[1])
-        print(f"[invariant] chunk {C}: vs oracle y={ey:.3e} S={eS:.3e}", flush=True)
-        assert ey <= TOL and eS <= TOL
+        check_errors(f"chunk {C} vs oracle", y, ref[0], S, ref[1])
         np.testing.assert_array_equal(h, ref[2])
     for C in (16, 32, 128):
         assert rel_l2(outs[C][0], outs[64][0]) <= TOL
@@ -147,11 +143,9 @@ def test_bf16_output():
     d = dims_of(geom, out_dtype=gdn.BF16)
     y, S, _ = gpu_prefill(geom, I, 64, dims=d)
     y_ref_bf16 = bf16_bits_to_f32(f64_to_bf16_bits(y_ref)).astype(np.float64)
-    ey = rel_l2(y, y_ref_bf16)
-    print(f"[invariant] bf16 y vs bf16-rounded oracle: {ey:.3e}", flush=True)
-    assert ey <= TOL and rel_l2(S, S_ref) <= TOL
+    check_errors("bf16 y vs bf16-rounded oracle", y, y_ref_bf16, S, S_ref)
     yd, Sd, _ = gpu_decode_seq(geom, I, dims=d)
-    assert rel_l2(yd, y_ref_bf16) <= TOL
+    check_errors("bf16 y, decode steps, vs bf16-rounded oracle", yd, y_ref_bf16, Sd, S_ref)
 
 
 def test_decode_graph_replay_matches_eager():
@@ -186,29 +180,26 @@ def test_decode_graph_replay_matches_eager():
 
 # ----------------------------------------------------------------- long context (T = 65536)
 
-LONG_HEADS = [(0, 0), (0, 25), (0, 47)]
-
-
 @pytest.fixture(scope="module")
 def long_ctx():
+    # Every value head of the long-context workload against one full oracle
+    # run (the oracle has no chunk size, so one run serves both chunk sizes).
     wl, I = workload_inputs(4)
     print(f"[invariant] long-context inputs ready: {wl.name}", flush=True)
-    ref = oracle_run(wl.geom, I, heads=LONG_HEADS)
+    ref = oracle_run(wl.geom, I)
+    print("[invariant] long-context oracle done", flush=True)
     return wl.geom, I, ref
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("chunk", [64, 128])
-def test_long_context_sampled_heads_and_resume(long_ctx, chunk):
+def test_long_context_all_heads_and_resume(long_ctx, chunk):
     import torch
 
     geom, I, (yr, Sr, hr) = long_ctx
     y, S, h = gpu_prefill(geom, I, chunk)
-    for b, hh in LONG_HEADS:
-        ey, eS = rel_l2(y[b, :, hh], yr[b, :, hh]), rel_l2(S[b, hh], Sr[b, hh])
-        print(f"[parity] T=65536 C={chunk} head {hh}: y={ey:.3e} S={eS:.3e}", flush=True)
-        assert ey <= TOL and eS <= TOL
+    check_errors(f"T=65536 C={chunk}, all {geom.H_v} heads", y, yr, S, Sr)
     np.testing.assert_array_equal(h, hr)
-    assert np.isfinite(y).all() and np.isfinite(S).all()
     # checkpoint at token 32768 (through a saved blob), resume, compare bit for bit
     import gated_deltanet_layer_gdn_amd as gdn
 

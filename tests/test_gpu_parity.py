@@ -1,28 +1,23 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
-same seeded inputs.  Bar: relative L2 <= 2e-3 on y and on the final state;
-conv history bit-exact."""
+same seeded inputs.  Bar: relative L2 <= 2e-3 on y and on the final state,
+over the whole tensor and for every value head, every row within 1e-2 of
+its scale (see gdn_testlib.ROW_TOL); conv history bit-exact."""
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
 from gdn_inputs import Geometry, make_inputs, workload_inputs
-from gdn_testlib import (EPS, TOL, dev_inputs, dims_of, from_dev, gpu_decode_seq, gpu_prefill,
-                         oracle_run, rel_l2)
+from gdn_testlib import (EPS, ROW_TOL, TOL, check_errors, dev_inputs, dims_of, from_dev,
+                         gpu_decode_seq, gpu_prefill, oracle_run, rel_l2, s_errors)
 
 pytestmark = pytest.mark.gpu
-
-
-def report(name, ey, eS):
-    print(f"[parity] {name}: rel_l2 y={ey:.3e} S={eS:.3e}", flush=True)
 
 
 def check_layer(name, got, ref, tol=TOL):
     y, S, h = got
     yr, Sr, hr = ref
-    ey, eS = rel_l2(y, yr), rel_l2(S, Sr)
-    report(name, ey, eS)
-    assert ey <= tol and eS <= tol, (ey, eS)
+    check_errors(name, y, yr, S, Sr, tol=tol)
     np.testing.assert_array_equal(h, hr)
 
 
@@ -56,8 +51,9 @@ def test_prefill_t4096():
     check_layer("prefill T=4096 C=64", gpu_prefill(wl.geom, I, 64), oracle_run(wl.geom, I))
 
 
-@pytest.mark.parametrize("T,chunk", [(1, 64), (2, 16), (3, 32), (77, 64), (128, 64), (150, 64),
-                                     (192, 64), (200, 128), (130, 16), (781, 64), (1000, 64)])
+@pytest.mark.parametrize("T,chunk", [(1, 64), (2, 64), (3, 64), (2, 16), (3, 32), (77, 64),
+                                     (128, 64), (150, 64), (192, 64), (2, 128), (129, 128),
+                                     (200, 128), (130, 16), (781, 64), (1000, 64)])
 def test_prefill_ragged_small(T, chunk):
     geom = Geometry(B=2, T=T, H_k=4, H_v=12, d_k=128, d_v=128, zero_state=False)
     I = make_inputs(geom, seed=100 + T)
@@ -105,9 +101,11 @@ def test_full_decay_and_zero_input():
     I0["g"] *= 0.05
     _, S_ref, h_ref = oracle_run(geom, I0)
     for name, (y, S, h) in (("prefill", gpu_prefill(geom, I0, 64)), ("decode", gpu_decode_seq(geom, I0))):
+        hs, rs = s_errors(S, S_ref)
         eS = rel_l2(S, S_ref)
-        print(f"[parity] zero input {name}: max|y|={np.abs(y).max():.1e} rel_l2 S={eS:.3e}", flush=True)
-        assert not np.any(y) and eS <= TOL
+        print(f"[parity] zero input {name}: max|y|={np.abs(y).max():.1e} rel_l2 S={eS:.3e} "
+              f"worst head {hs.max():.3e} worst row {rs.max():.3e}", flush=True)
+        assert not np.any(y) and eS <= TOL and hs.max() <= TOL and rs.max() <= ROW_TOL
         np.testing.assert_array_equal(h, h_ref)
 
 
@@ -128,6 +126,22 @@ def test_prefill_weak_decay(chunk):
     geom = Geometry(B=1, T=512, H_k=2, H_v=6, d_k=128, d_v=128, g_scale=0.02)
     I = make_inputs(geom, seed=7)
     check_layer(f"weak decay C={chunk}", gpu_prefill(geom, I, chunk), oracle_run(geom, I))
+
+
+@pytest.fixture(scope="module")
+def long_weak_decay():
+    # The state's memory spans thousands of tokens (mean decay per token
+    # e^-0.014), so rounding carried through the state accumulates over the
+    # longest chain: T = 8192 is 128 chunks of 64 and 64 of 128.
+    geom = Geometry(B=1, T=8192, H_k=4, H_v=12, d_k=128, d_v=128, g_scale=0.02)
+    I = make_inputs(geom, seed=17)
+    return geom, I, oracle_run(geom, I)
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_prefill_long_weak_decay(long_weak_decay, chunk):
+    geom, I, ref = long_weak_decay
+    check_layer(f"weak decay T=8192 C={chunk}", gpu_prefill(geom, I, chunk), ref)
 
 
 def test_conv1d_standalone():
