@@ -21,7 +21,8 @@ from . import _lib
 from ._lib import BF16, F32, GdnError
 
 __all__ = [
-    "Dims", "GdnError", "conv1d", "prefill_chunked", "decode_step", "state_save",
+    "Dims", "GdnError", "conv1d", "prefill_chunked", "decode_step", "decode_step_noalloc",
+    "state_save",
     "state_restore", "state_check", "prefill_workspace_bytes", "decode_workspace_bytes",
     "rec_state_bytes", "conv_state_bytes", "state_blob_bytes", "F32", "BF16",
 ]
@@ -191,6 +192,28 @@ def decode_step(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, y=None, w
         rc = L.gdn_decode_step_timed(ctypes.byref(d.c()), *args, *tail, ms)
         kernel_ms.extend(float(v) for v in ms)
     _lib.check(rc, "gdn_decode_step")
+    return y
+
+
+def decode_step_noalloc(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, y):
+    """decode_step through the entry point that allocates nothing: the caller
+    passes every buffer including y (shaped like z), and the library uses its
+    fixed per-GPU scratch as the workspace."""
+    torch = _torch()
+    L = _lib.load()
+    dt = _dt(d.in_dtype)
+    args = [
+        _need(x.reshape(d.B, d.C_ch), "x", (d.B, d.C_ch), dt),
+        _need(z.reshape(d.B, d.H_v, d.d_v), "z", (d.B, d.H_v, d.d_v), dt),
+        _need(g.reshape(d.B, d.H_v), "g", (d.B, d.H_v), torch.float32),
+        _need(beta.reshape(d.B, d.H_v), "beta", (d.B, d.H_v), torch.float32),
+        _need(conv_w, "conv_w", (d.C_ch, d.W), dt),
+        _need(conv_state, "conv_state", (d.B, d.W - 1, d.C_ch), dt),
+        _need(rec_state, "rec_state", (d.B, d.H_v, d.d_v, d.d_k), torch.float32),
+        _need(y.reshape(d.B, d.H_v, d.d_v), "y", (d.B, d.H_v, d.d_v), _dt(d.out_dtype)),
+    ]
+    _lib.check(L.gdn_decode_step_noalloc(ctypes.byref(d.c()), *args, _stream()),
+               "gdn_decode_step_noalloc")
     return y
 
 

@@ -17,7 +17,7 @@ STATUS = {
     0: "GDN_OK", -1: "GDN_ERR_INVALID_ARG", -2: "GDN_ERR_UNSUPPORTED", -3: "GDN_ERR_ALIGNMENT",
     -4: "GDN_ERR_ALIAS", -5: "GDN_ERR_WORKSPACE", -6: "GDN_ERR_BLOB_MAGIC",
     -7: "GDN_ERR_BLOB_VERSION", -8: "GDN_ERR_BLOB_SHAPE", -9: "GDN_ERR_BLOB_SIZE",
-    -10: "GDN_ERR_BLOB_CHECKSUM", -11: "GDN_ERR_HIP",
+    -10: "GDN_ERR_BLOB_CHECKSUM", -11: "GDN_ERR_HIP", -12: "GDN_ERR_TOO_LARGE",
 }
 F32, BF16 = 0, 1
 ABI_VERSION = 1
@@ -27,7 +27,7 @@ EXPORTS = (
     "gdn_conv_state_bytes", "gdn_state_blob_bytes", "gdn_prefill_workspace_bytes",
     "gdn_decode_workspace_bytes", "gdn_conv1d", "gdn_prefill_chunked", "gdn_decode_step",
     "gdn_state_save", "gdn_state_restore", "gdn_state_check", "gdn_prefill_chunked_timed",
-    "gdn_decode_step_timed",
+    "gdn_decode_step_timed", "gdn_decode_step_noalloc",
 )
 
 
@@ -83,6 +83,8 @@ def load():
     L.gdn_prefill_chunked_timed.argtypes = L.gdn_prefill_chunked.argtypes + [vp]
     L.gdn_decode_step_timed.restype = ctypes.c_int
     L.gdn_decode_step_timed.argtypes = L.gdn_decode_step.argtypes + [vp]
+    L.gdn_decode_step_noalloc.restype = ctypes.c_int
+    L.gdn_decode_step_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_state_save.restype = ctypes.c_int
     L.gdn_state_save.argtypes = [dp, vp, vp, vp, sz, vp]
     L.gdn_state_restore.restype = ctypes.c_int

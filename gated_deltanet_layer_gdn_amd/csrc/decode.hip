@@ -20,6 +20,8 @@
 // nontemporal stores, these small blocks (12,288 at B = 64) stream faster
 // than one block per (sequence, head) walking four such groups (67.7-68.4
 // vs 75.4-75.6 us at B = 64, measured side by side).
+#include <mutex>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -166,6 +168,45 @@ hipError_t launch_decode(const Geom &g, const float *qkv, const void *z, const f
   }
 #undef GDN_DEC
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fixed scratch
+// The decode workspace of gdn_decode_step_noalloc lives in this array: one
+// copy per GPU, loaded with the code object, kept until the process ends.
+// Host code never passes the array's name to a kernel (on the host it only
+// stands for the symbol); it passes the device address that
+// hipGetSymbolAddress returns for the GPU the call runs on, fetched once per
+// GPU with that GPU current.
+namespace {
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxGpus = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxGpus] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t s, void **out) {
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxGpus) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace gdn

@@ -237,6 +237,7 @@ const char *gdn_status_str(int s) {
     case GDN_ERR_BLOB_SIZE: return "state blob: size mismatch";
     case GDN_ERR_BLOB_CHECKSUM: return "state blob: checksum mismatch";
     case GDN_ERR_HIP: return "HIP runtime error";
+    case GDN_ERR_TOO_LARGE: return "request exceeds the fixed scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -345,10 +346,12 @@ int gdn_prefill_chunked_timed(const gdn_dims *dims, int64_t T, int32_t chunk, co
                       ws_bytes, stream, kernel_ms);
 }
 
+// validate_only: run every check on the arguments except those of `ws`
+// (which may be null then) and return without any HIP call.
 static int decode_impl(const gdn_dims *dims, const void *x, const void *z, const float *gl,
                     const float *beta, const void *conv_w, void *conv_state,
                     float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream,
-                    float *kernel_ms) {
+                    float *kernel_ms, bool validate_only = false) {
   Geom g;
   int rc = check_dims(dims, &g);
   if (rc) return rc;
@@ -364,7 +367,8 @@ static int decode_impl(const gdn_dims *dims, const void *x, const void *z, const
                      {rec_state, rec_state_bytes(g), 16},
                      {y, B * g.H_v * g.D * eo, eo},
                      {ws, need, 16}};
-  if ((rc = check_buffers(in, 5, out, 4))) return rc;
+  if ((rc = check_buffers(in, 5, out, validate_only ? 3 : 4))) return rc;
+  if (validate_only) return GDN_OK;
   if (ws_bytes < need) return GDN_ERR_WORKSPACE;
   if (injected_launch_failure()) return GDN_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -384,6 +388,29 @@ int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, const fl
                     float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream) {
   return decode_impl(dims, x, z, gl, beta, conv_w, conv_state, rec_state, y, ws, ws_bytes,
                      stream, nullptr);
+}
+
+int gdn_decode_step_noalloc(const gdn_dims *dims, const void *x, const void *z, const float *gl,
+                            const float *beta, const void *conv_w, void *conv_state,
+                            float *rec_state, void *y, void *stream) {
+  Geom g;
+  int rc = check_dims(dims, &g);
+  if (rc) return rc;
+  const size_t need = decode_ws_bytes(g);
+  if (need > kNoAllocScratchBytes) return GDN_ERR_TOO_LARGE;
+  // Every other check (pointers, alignment, aliasing) runs in decode_impl
+  // before the first launch; the scratch itself is checked against the
+  // buffers there as the workspace.  Validate first, so an invalid call
+  // makes no HIP call at all.
+  rc = decode_impl(dims, x, z, gl, beta, conv_w, conv_state, rec_state, y, nullptr, need,
+                   stream, nullptr, /*validate_only=*/true);
+  if (rc) return rc;
+  if (injected_launch_failure()) return GDN_ERR_HIP;
+  void *ws = nullptr;
+  const hipError_t e = noalloc_scratch(static_cast<hipStream_t>(stream), &ws);
+  if (e != hipSuccess) return set_hip_error(e, "gdn_decode_step_noalloc");
+  return decode_impl(dims, x, z, gl, beta, conv_w, conv_state, rec_state, y, ws, need, stream,
+                     nullptr);
 }
 
 int gdn_decode_step_timed(const gdn_dims *dims, const void *x, const void *z, const float *gl,

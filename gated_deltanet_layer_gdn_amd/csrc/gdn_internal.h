@@ -57,6 +57,12 @@ __host__ __device__ inline bool prefill_split_roles(const Geom &g, const Prefill
 }
 size_t decode_ws_bytes(const Geom &g);
 
+// Size of the fixed device array that serves as the decode workspace of
+// gdn_decode_step_noalloc, and its device address on the GPU of stream `s`
+// (looked up once per GPU).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(hipStream_t s, void **ptr);
+
 // Kernel launchers (enqueue only; return the launch status).
 hipError_t launch_conv_plain(const Geom &g, int64_t T, const void *x, const void *w,
                              void *hist, float *out, hipStream_t s);

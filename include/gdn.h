@@ -83,6 +83,7 @@ extern "C" {
 #define GDN_ERR_BLOB_SIZE (-9)     /* state blob: buffer size mismatch       */
 #define GDN_ERR_BLOB_CHECKSUM (-10) /* state blob: header or payload corrupt */
 #define GDN_ERR_HIP (-11)          /* HIP runtime error; see gdn_last_hip_error */
+#define GDN_ERR_TOO_LARGE (-12)    /* beyond the fixed scratch of gdn_decode_step_noalloc */
 
 /* Element types. */
 #define GDN_F32 0
@@ -153,6 +154,24 @@ GDN_API int gdn_prefill_chunked(const gdn_dims *dims, int64_t T, int32_t chunk, 
 GDN_API int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, const float *g,
                     const float *beta, const void *conv_w, void *conv_state,
                     float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream);
+
+/* gdn_decode_step without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (minus ws and ws_bytes) and the same results, bit for bit, as
+ * gdn_decode_step; it runs the same kernels with the decode workspace placed
+ * in a fixed 16 MiB device array that the library holds on each GPU it runs
+ * on until the process ends.  Calls whose gdn_decode_workspace_bytes(dims)
+ * exceeds 16 MiB (about B = 409 at C_ch = 10240) are rejected with
+ * GDN_ERR_TOO_LARGE before anything is enqueued.  The first call on a GPU
+ * looks the array's device address up (no allocation, no stream work).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and give wrong results;
+ * calls in one stream order are safe.  Nothing in the array needs to start
+ * at zero: each call writes what it reads. */
+GDN_API int gdn_decode_step_noalloc(const gdn_dims *dims, const void *x, const void *z,
+                                    const float *g, const float *beta, const void *conv_w,
+                                    void *conv_state, float *rec_state, void *y, void *stream);
 
 /* Measurement variants ("Add a performance-parity Qwen3.8-27B Q4 and Q8 text
  * backend on Metal", section Measurements and gates, asks for the conv, the

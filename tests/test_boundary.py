@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 
 OK, INVALID, UNSUPPORTED, ALIGN, ALIAS, WORKSPACE = 0, -1, -2, -3, -4, -5
-B_MAGIC, B_VERSION, B_SHAPE, B_SIZE, B_CHECKSUM, HIP = -6, -7, -8, -9, -10, -11
+B_MAGIC, B_VERSION, B_SHAPE, B_SIZE, B_CHECKSUM, HIP, TOO_LARGE = -6, -7, -8, -9, -10, -11, -12
 
 
 @pytest.fixture(scope="module")
@@ -58,7 +58,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.gdn_abi_version() == 1
-    for code in range(-11, 1):
+    for code in range(-12, 1):
         s = lib.gdn_status_str(code).decode()
         assert s and s != "unknown status"
     assert lib.gdn_status_str(-99).decode() == "unknown status"
@@ -183,6 +183,27 @@ def test_decode_and_conv_reject_and_leave_buffers_untouched(lib, dims):
     assert conv(1, out=b.p("x")) == ALIAS
     assert conv(1, hist=b.p("w")) == ALIAS
     assert b.unchanged()
+
+
+def test_decode_noalloc_validates_before_any_hip_call(lib, dims):
+    # The entry point that allocates nothing: the same argument checks as
+    # gdn_decode_step (there is no workspace argument), and sizes beyond its
+    # fixed 16 MiB scratch are refused before anything else.
+    d = dims
+    b = Bufs(d, 1, 0)
+    call = lambda **o: lib.gdn_decode_step_noalloc(
+        ctypes.byref(d), o.get("x", b.p("x")), b.p("z"), b.p("g"), b.p("beta"), b.p("w"),
+        o.get("hist", b.p("hist")), o.get("S", b.p("S")), o.get("y", b.p("y")), None)
+    assert call(x=None) == INVALID
+    assert call(S=b.p("S", 4)) == ALIGN
+    assert call(y=b.p("z")) == ALIAS
+    assert b.unchanged()
+    from gated_deltanet_layer_gdn_amd import _lib
+
+    big = _lib.GdnDims(_lib.ABI_VERSION, 500, 16, 48, 128, 128, 4, 1, 0, 1e-6, 1.0)
+    assert lib.gdn_decode_workspace_bytes(ctypes.byref(big)) > 16 << 20
+    assert lib.gdn_decode_step_noalloc(ctypes.byref(big), *[None] * 8, None) == TOO_LARGE
+    assert "fixed scratch" in lib.gdn_status_str(TOO_LARGE).decode()
 
 
 def test_injected_launch_failure_leaves_buffers_untouched(lib, dims, monkeypatch):
