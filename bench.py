@@ -383,8 +383,8 @@ def main():
             kms.append(km)
         kmean = [float(np.mean([k[j] for k in kms])) for j in range(len(kms[0]))]
         k_state = kmean[-1]
-        kb = decode_kernel_bytes_per_seq(Gd.H_v, Gd.d_k, Gd.d_v, 2, 4) * Gd.B
         sb = decode_step_bytes_per_seq(Gd.C_ch, Gd.H_v, Gd.d_k, Gd.d_v, 2, 4) * Gd.B
+        kb = decode_kernel_bytes_per_seq(Gd.H_v, Gd.d_k, Gd.d_v, 2, 4) * Gd.B
         ach = kb / (k_state * 1e-3) / 1e9
         decode[key] = {
             "workload": wl_d.name, "steps_per_s": round(1e3 / ms_dec, 1),
@@ -392,8 +392,9 @@ def main():
             "us_per_step_eager": round(ms_eager * 1e3, 3), "rotated_state_sets": R,
             "step_hbm_frac": round(sb / (ms_dec * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
             "step_alg_bytes": int(sb),
-            "kernels_us": [round(v * 1e3, 3) for v in kmean],
-            "roofline": {"bound": "hbm", "kernel": "decode state stream + gate",
+            "kernels_us": {"conv_step": round(kmean[0] * 1e3, 3),
+                           "state": round(kmean[1] * 1e3, 3)},
+            "roofline": {"bound": "hbm", "kernel": "decode_kernel (state stream + gate)",
                          "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(ach / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("decode_" + key),

@@ -22,7 +22,7 @@ from ._lib import BF16, F32, GdnError
 
 __all__ = [
     "Dims", "GdnError", "conv1d", "prefill_chunked", "decode_step", "decode_step_noalloc",
-    "state_save",
+    "decode_multi", "prefill_varlen", "prefill_varlen_workspace_bytes", "state_save",
     "state_restore", "state_check", "prefill_workspace_bytes", "decode_workspace_bytes",
     "rec_state_bytes", "conv_state_bytes", "state_blob_bytes", "F32", "BF16",
 ]
@@ -99,6 +99,7 @@ def decode_workspace_bytes(d: Dims) -> int:
 
 
 def _workspace(nbytes: int, ref, ws):
+    """A new workspace when ``ws`` is None, else ``ws`` after a size check."""
     torch = _torch()
     if ws is None:
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=ref.device)
@@ -192,6 +193,87 @@ def decode_step(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, y=None, w
         rc = L.gdn_decode_step_timed(ctypes.byref(d.c()), *args, *tail, ms)
         kernel_ms.extend(float(v) for v in ms)
     _lib.check(rc, "gdn_decode_step")
+    return y
+
+
+def decode_multi(d: Dims, x, z, g, beta, conv_w, conv_pool, rec_pool, in_slots, out_slots=None,
+                 y=None, ws=None):
+    """T (1..4) tokens per sequence from slot-indexed states: x [B,T,C_ch],
+    z [B,T,H_v,d_v], g/beta [B,T,H_v]; conv_pool [n_slots,W-1,C_ch], rec_pool
+    [n_slots,H_v,d_v,d_k]; in_slots int32 [B] and out_slots int32 [B,T] (or
+    None) on the device.  Returns y [B,T,H_v,d_v]."""
+    torch = _torch()
+    L = _lib.load()
+    T = x.shape[1]
+    n_slots = rec_pool.shape[0]
+    dt = _dt(d.in_dtype)
+    args = [
+        _need(x, "x", (d.B, T, d.C_ch), dt),
+        _need(z, "z", (d.B, T, d.H_v, d.d_v), dt),
+        _need(g, "g", (d.B, T, d.H_v), torch.float32),
+        _need(beta, "beta", (d.B, T, d.H_v), torch.float32),
+        _need(conv_w, "conv_w", (d.C_ch, d.W), dt),
+        _need(conv_pool, "conv_pool", (n_slots, d.W - 1, d.C_ch), dt),
+        _need(rec_pool, "rec_pool", (n_slots, d.H_v, d.d_v, d.d_k), torch.float32),
+    ]
+    pin = _need(in_slots, "in_slots", (d.B,), torch.int32)
+    pout = (ctypes.c_void_p(None) if out_slots is None
+            else _need(out_slots, "out_slots", (d.B, T), torch.int32))
+    if y is None:
+        y = torch.empty((d.B, T, d.H_v, d.d_v), dtype=_dt(d.out_dtype), device=x.device)
+    py = _need(y, "y", (d.B, T, d.H_v, d.d_v), _dt(d.out_dtype))
+    need = T * L.gdn_decode_workspace_bytes(ctypes.byref(d.c()))
+    ws = _workspace(need, x, ws)
+    rc = L.gdn_decode_multi(ctypes.byref(d.c()), T, *args[:5], args[5], args[6], n_slots, pin,
+                            pout, py, ctypes.c_void_p(ws.data_ptr()),
+                            ws.numel() * ws.element_size(), _stream())
+    _lib.check(rc, "gdn_decode_multi")
+    return y
+
+
+def _cu_array(cu_seqlens):
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    return cu, cu.ctypes.data_as(ctypes.c_void_p)
+
+
+def prefill_varlen_workspace_bytes(d: Dims, cu_seqlens, chunk: int) -> int:
+    cu, pcu = _cu_array(cu_seqlens)
+    return _lib.load().gdn_prefill_varlen_workspace_bytes(ctypes.byref(d.c()), pcu, chunk)
+
+
+def prefill_varlen(d: Dims, cu_seqlens, x, z, g, beta, conv_w, conv_pool, rec_pool, slots,
+                   chunk: int = 64, y=None, ws=None):
+    """Packed variable-length prefill of d.B sequences: cu_seqlens (host,
+    B+1 offsets), x [T_total,C_ch], z [T_total,H_v,d_v], g/beta [T_total,H_v];
+    slots (host, B) index conv_pool / rec_pool.  Returns y [T_total,H_v,d_v]."""
+    torch = _torch()
+    L = _lib.load()
+    cu, pcu = _cu_array(cu_seqlens)
+    sl = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+    T_total = x.shape[0]
+    n_slots = rec_pool.shape[0]
+    dt = _dt(d.in_dtype)
+    args = [
+        _need(x, "x", (T_total, d.C_ch), dt),
+        _need(z, "z", (T_total, d.H_v, d.d_v), dt),
+        _need(g, "g", (T_total, d.H_v), torch.float32),
+        _need(beta, "beta", (T_total, d.H_v), torch.float32),
+        _need(conv_w, "conv_w", (d.C_ch, d.W), dt),
+        _need(conv_pool, "conv_pool", (n_slots, d.W - 1, d.C_ch), dt),
+        _need(rec_pool, "rec_pool", (n_slots, d.H_v, d.d_v, d.d_k), torch.float32),
+    ]
+    if y is None:
+        y = torch.empty((T_total, d.H_v, d.d_v), dtype=_dt(d.out_dtype), device=x.device)
+    py = _need(y, "y", (T_total, d.H_v, d.d_v), _dt(d.out_dtype))
+    need = L.gdn_prefill_varlen_workspace_bytes(ctypes.byref(d.c()), pcu, chunk)
+    if need == 0:
+        raise GdnError(-1, "gdn_prefill_varlen", "invalid sequence table or chunk")
+    ws = _workspace(need, x, ws)
+    rc = L.gdn_prefill_varlen(ctypes.byref(d.c()), pcu, chunk, *args, n_slots,
+                              sl.ctypes.data_as(ctypes.c_void_p), py,
+                              ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                              _stream())
+    _lib.check(rc, "gdn_prefill_varlen")
     return y
 
 

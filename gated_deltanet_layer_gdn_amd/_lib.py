@@ -27,7 +27,8 @@ EXPORTS = (
     "gdn_conv_state_bytes", "gdn_state_blob_bytes", "gdn_prefill_workspace_bytes",
     "gdn_decode_workspace_bytes", "gdn_conv1d", "gdn_prefill_chunked", "gdn_decode_step",
     "gdn_state_save", "gdn_state_restore", "gdn_state_check", "gdn_prefill_chunked_timed",
-    "gdn_decode_step_timed", "gdn_decode_step_noalloc",
+    "gdn_decode_step_timed", "gdn_decode_step_noalloc", "gdn_decode_multi",
+    "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_bytes",
 )
 
 
@@ -83,6 +84,13 @@ def load():
     L.gdn_prefill_chunked_timed.argtypes = L.gdn_prefill_chunked.argtypes + [vp]
     L.gdn_decode_step_timed.restype = ctypes.c_int
     L.gdn_decode_step_timed.argtypes = L.gdn_decode_step.argtypes + [vp]
+    L.gdn_decode_multi.restype = ctypes.c_int
+    L.gdn_decode_multi.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.gdn_prefill_varlen_workspace_bytes.restype = sz
+    L.gdn_prefill_varlen_workspace_bytes.argtypes = [dp, vp, i32]
+    L.gdn_prefill_varlen.restype = ctypes.c_int
+    L.gdn_prefill_varlen.argtypes = [dp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz,
+                                     vp]
     L.gdn_decode_step_noalloc.restype = ctypes.c_int
     L.gdn_decode_step_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_state_save.restype = ctypes.c_int

@@ -514,14 +514,21 @@ __global__ __launch_bounds__(256) void roll_kernel(int C_ch, int64_t T, const E 
   for (int r = 0; r < 3; ++r) hist[(static_cast<size_t>(b) * 3 + r) * C_ch + ch] = v[r];
 }
 
-// One token per sequence (decode step): one thread owns one channel for BB
+// Decode step of TT tokens per sequence: one thread owns one channel for BB
 // sequences, so a block does BB rows of work and the per-head sums of all BB
-// rows share one LDS exchange.  The history roll (rows 1, 2 and the new
-// token become rows 0..2) stays with the thread that read those rows.
-template <int DT, int D, int BB>
+// rows and TT tokens share one LDS exchange.  The history is read from the
+// sequence's in slot and the history after token t (the last three raw
+// inputs up to t) is stored to its out slot for t, by the thread that read
+// the channel, after it has read it; a sequence whose in slot lies outside
+// [0, n_slots) is skipped (slot rules as in decode.hip).
+// out: [B][TT][C_ch] fp32, read by the state-stream kernel.
+template <int DT, int D, int BB, int TT>
 __global__ __launch_bounds__(kConvThreads) void conv_step_kernel(Geom g, const void *x,
                                                                  const void *w, void *hist,
-                                                                 float *out) {
+                                                                 float *out, const int32_t *in_slots,
+                                                                 const int32_t *out_slots,
+                                                                 int n_slots) {
+  static_assert(BB * TT <= kConvTT, "one LDS exchange for all rows and tokens");
   __shared__ float red[2][kConvTT];
   const int ch = blockIdx.x * kConvThreads + threadIdx.x;
   const int b0 = blockIdx.y * BB;
@@ -537,56 +544,88 @@ __global__ __launch_bounds__(kConvThreads) void conv_step_kernel(Geom g, const v
   const float w1 = load_elem<DT>(w, static_cast<size_t>(chc) * 4 + 1);
   const float w2 = load_elem<DT>(w, static_cast<size_t>(chc) * 4 + 2);
   const float w3 = load_elem<DT>(w, static_cast<size_t>(chc) * 4 + 3);
-  float xv[BB][4], val[BB], ss[BB];
+  float xv[BB][3 + TT], val[BB * TT], ss[BB * TT];
+  int sin[BB];
 #pragma unroll
   for (int r = 0; r < BB; ++r) {
     const int b = b0 + r < g.B ? b0 + r : g.B - 1;  // rows past B re-read the last one
+    const int sl = in_slots ? in_slots[b] : b;
+    sin[r] = (b0 + r < g.B && sl >= 0 && sl < n_slots) ? sl : -1;
+    const int src = sin[r] >= 0 ? sin[r] : 0;  // padding rows read slot 0, use nothing
 #pragma unroll
-    for (int k = 0; k < 3; ++k) xv[r][k] = load_elem<DT>(hist, (static_cast<size_t>(b) * 3 + k) * C + chc);
-    xv[r][3] = load_elem<DT>(x, static_cast<size_t>(b) * C + chc);
-    val[r] = siluf_(conv4(w0, w1, w2, w3, xv[r][0], xv[r][1], xv[r][2], xv[r][3]));
-    ss[r] = val[r] * val[r];
+    for (int k = 0; k < 3; ++k) xv[r][k] = load_elem<DT>(hist, (static_cast<size_t>(src) * 3 + k) * C + chc);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+      xv[r][3 + t] = load_elem<DT>(x, (static_cast<size_t>(b) * TT + t) * C + chc);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      val[r * TT + t] = siluf_(conv4(w0, w1, w2, w3, xv[r][t], xv[r][t + 1], xv[r][t + 2], xv[r][t + 3]));
+      ss[r * TT + t] = val[r * TT + t] * val[r * TT + t];
+    }
   }
   if (qk_block) {
-    head_sums<D, BB>(ss, red);
+    head_sums<D, BB * TT>(ss, red);
     if (is_q || is_k) {
       const float sc = is_q ? g.q_scale : 1.0f;
 #pragma unroll
-      for (int r = 0; r < BB; ++r) val[r] *= __builtin_amdgcn_rsqf(ss[r] + g.eps) * sc;
+      for (int k = 0; k < BB * TT; ++k) val[k] *= __builtin_amdgcn_rsqf(ss[k] + g.eps) * sc;
     }
   }
   if (!active) return;
 #pragma unroll
   for (int r = 0; r < BB; ++r) {
     const int b = b0 + r;
-    if (b < g.B) {
-      out[static_cast<size_t>(b) * C + ch] = val[r];
+    if (sin[r] < 0) continue;
 #pragma unroll
-      for (int k = 0; k < 3; ++k) store_elem<DT>(hist, (static_cast<size_t>(b) * 3 + k) * C + ch, xv[r][k + 1]);
+    for (int t = 0; t < TT; ++t) {
+      out[(static_cast<size_t>(b) * TT + t) * C + ch] = val[r * TT + t];
+      const int o = out_slots ? out_slots[static_cast<size_t>(b) * TT + t]
+                              : (t == TT - 1 ? sin[r] : -1);
+      if (o >= 0 && o < n_slots) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+          store_elem<DT>(hist, (static_cast<size_t>(o) * 3 + k) * C + ch, xv[r][t + 1 + k]);
+      }
     }
   }
 }
 
-template <int D, int BB>
+template <int D, int BB, int TT>
 static hipError_t launch_conv_step_t(const Geom &g, const void *x, const void *w, void *hist,
-                                     float *out, hipStream_t s) {
+                                     float *out, const int32_t *in_slots,
+                                     const int32_t *out_slots, int n_slots, hipStream_t s) {
   dim3 grid((g.C_ch + kConvThreads - 1) / kConvThreads, (g.B + BB - 1) / BB);
   if (g.in_dt == 0)
-    hipLaunchKernelGGL((conv_step_kernel<0, D, BB>), grid, dim3(kConvThreads), 0, s, g, x, w, hist, out);
+    hipLaunchKernelGGL((conv_step_kernel<0, D, BB, TT>), grid, dim3(kConvThreads), 0, s, g, x, w, hist, out, in_slots, out_slots, n_slots);
   else
-    hipLaunchKernelGGL((conv_step_kernel<1, D, BB>), grid, dim3(kConvThreads), 0, s, g, x, w, hist, out);
+    hipLaunchKernelGGL((conv_step_kernel<1, D, BB, TT>), grid, dim3(kConvThreads), 0, s, g, x, w, hist, out, in_slots, out_slots, n_slots);
   return hipGetLastError();
 }
 
-static hipError_t launch_conv_step(const Geom &g, const void *x, const void *w, void *hist,
-                                   float *out, hipStream_t s) {
+template <int TT>
+static hipError_t launch_conv_step_tt(const Geom &g, const void *x, const void *w, void *hist,
+                                      float *out, const int32_t *in_slots,
+                                      const int32_t *out_slots, int n_slots, hipStream_t s) {
   // d = 128: two sequences per block (B = 64: 2,560 blocks) measured faster
   // than eight (640 blocks: too few waves in flight for the short loads).
   if (g.D == 128)
-    return g.B >= 8 ? launch_conv_step_t<128, 2>(g, x, w, hist, out, s)
-                    : launch_conv_step_t<128, 1>(g, x, w, hist, out, s);
-  return g.B >= 8 ? launch_conv_step_t<16, 8>(g, x, w, hist, out, s)
-                  : launch_conv_step_t<16, 1>(g, x, w, hist, out, s);
+    return g.B >= 8 ? launch_conv_step_t<128, 2, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s)
+                    : launch_conv_step_t<128, 1, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
+  return g.B >= 8 && TT == 1
+             ? launch_conv_step_t<16, 8, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s)
+             : launch_conv_step_t<16, 1, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
+}
+
+hipError_t launch_conv_step(const Geom &g, int T, const void *x, const void *w, void *hist,
+                            float *out, const int32_t *in_slots, const int32_t *out_slots,
+                            int n_slots, hipStream_t s) {
+  switch (T) {
+    case 1: return launch_conv_step_tt<1>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
+    case 2: return launch_conv_step_tt<2>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
+    case 3: return launch_conv_step_tt<3>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
+    case 4: return launch_conv_step_tt<4>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int MODE, int TT>
@@ -633,7 +672,7 @@ hipError_t launch_conv_plain(const Geom &g, int64_t T, const void *x, const void
   a.T = T;
   a.T_iter = T;
   a.fuse_roll = T <= kConvTT;
-  if (T == 1) return launch_conv_step(g, x, w, hist, out, s);
+  if (T == 1) return launch_conv_step(g, 1, x, w, hist, out, nullptr, nullptr, g.B, s);
   hipError_t e = launch_conv<kOutPlain, kConvTT>(g, a, s);
   if (e != hipSuccess || a.fuse_roll) return e;
   return launch_conv_roll(g, T, x, hist, s);

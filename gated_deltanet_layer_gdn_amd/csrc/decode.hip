@@ -20,6 +20,15 @@
 // nontemporal stores, these small blocks (12,288 at B = 64) stream faster
 // than one block per (sequence, head) walking four such groups (67.7-68.4
 // vs 75.4-75.6 us at B = 64, measured side by side).
+//
+// Several tokens per sequence (gdn_decode_multi): the rows stay in registers
+// across the TT tokens, so the state is read once for all of them; the rows
+// after token t are stored to the slot chosen for t, if any.  The conv step
+// (conv.hip) runs as its own launch before this one: it owns the conv
+// history roll, which the blocks here could not do without knowing that
+// every other block of the key head has read the history (a device-wide
+// counter for that cost about 4 us per step at B = 1 on MI355X, more than
+// the second launch).
 #include <mutex>
 
 #include "gdn_device.h"
@@ -40,51 +49,78 @@ __device__ __forceinline__ void store_stream(float4 *p, float4 v) {
   __builtin_nontemporal_store(r, reinterpret_cast<f4v *>(p));
 }
 
-template <int D>
+template <int D, int NPL_>
 struct DecodeShape {
-  static constexpr int NPL = (D >= 128) ? 16 : 4;  // floats per lane per row
-  static constexpr int LPR = D / NPL;              // lanes per row
-  static constexpr int RPW = kWave / LPR;          // rows per wave per pass
-  static constexpr int RPB = 4 * RPW;              // rows per block per pass
+  static constexpr int NPL = NPL_;         // floats per lane per row
+  static constexpr int LPR = D / NPL;      // lanes per row
+  static constexpr int RPW = kWave / LPR;  // rows per wave
+  static constexpr int RPB = 4 * RPW;      // rows per block
 };
 
-template <int D, int DTZ, int DTY, int PASSES>
+// Slots (gdn_decode_multi): sequence b reads its state from slot
+// in_slots[b] (b itself when in_slots is null) and stores the state after
+// token t to slot out_slots[b * TT + t] (when out_slots is null: the in slot
+// after the last token, nothing before).  An in slot outside [0, n_slots)
+// makes b a padding row: zero y, nothing read or stored; an out slot outside
+// that range is not stored.  A block only stores rows it has already read,
+// so a sequence may name its in slot as an out slot.
+struct SlotArgs {
+  const int32_t *in_slots, *out_slots;
+  int n_slots;
+};
+
+__device__ __forceinline__ int in_slot(const SlotArgs &sa, int b) {
+  const int s = sa.in_slots ? sa.in_slots[b] : b;
+  return (s >= 0 && s < sa.n_slots) ? s : -1;
+}
+
+template <int TT>
+__device__ __forceinline__ int out_slot(const SlotArgs &sa, int b, int t, int sin) {
+  const int o = sa.out_slots ? sa.out_slots[static_cast<size_t>(b) * TT + t]
+                             : (t == TT - 1 ? sin : -1);
+  return (o >= 0 && o < sa.n_slots) ? o : -1;
+}
+
+// qkv: [B][TT][C_ch] fp32 from the conv step (q scaled and normalised, k
+// normalised, v).  z, y: [B][TT][H_v][D]; gl, beta: [B][TT][H_v].
+template <int D, int NPL, int DTZ, int DTY, int TT>
 __global__ __launch_bounds__(256) void decode_kernel(Geom g, const float *__restrict__ qkv,
                                                      const void *__restrict__ z,
                                                      const float *__restrict__ gl,
                                                      const float *__restrict__ beta,
                                                      float *__restrict__ S, void *__restrict__ y,
-                                                     int64_t total_rows) {
-  using Sh = DecodeShape<D>;
-  constexpr int NPL = Sh::NPL, LPR = Sh::LPR, NV = NPL / 4;
+                                                     SlotArgs sa, int64_t total_rows) {
+  using Sh = DecodeShape<D, NPL>;
+  constexpr int LPR = Sh::LPR, NV = NPL / 4;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int j = lane % LPR;  // column slot of this lane
-  const int64_t base_row = static_cast<int64_t>(blockIdx.x) * (PASSES * Sh::RPB);
-
-  float4 s[PASSES][NV];
-  int64_t rows[PASSES];
+  const int64_t R = static_cast<int64_t>(blockIdx.x) * Sh::RPB + wave * Sh::RPW + lane / LPR;
+  if (R >= total_rows) return;  // whole row groups only: shuffles stay within live lanes
+  // (b, h, i) of this row.
+  const int i = static_cast<int>(R % D);
+  const int64_t bh = R / D;
+  const int h = static_cast<int>(bh % g.H_v);
+  const int b = static_cast<int>(bh / g.H_v);
+  const int kh = h / g.G;
+  const size_t bt0 = static_cast<size_t>(b) * TT;
+  const int sin = in_slot(sa, b);
+  if (sin < 0) {  // padding row
+    if (j == 0)
+      for (int t = 0; t < TT; ++t) store_elem<DTY>(y, ((bt0 + t) * g.H_v + h) * D + i, 0.f);
+    return;
+  }
+  const size_t row_off = (static_cast<size_t>(h) * D + i) * D;
+  const size_t pool_stride = static_cast<size_t>(g.H_v) * D * D;
+  float4 s[NV];
+  {
+    const float4 *src = reinterpret_cast<const float4 *>(S + sin * pool_stride + row_off);
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    rows[p] = base_row + p * Sh::RPB + wave * Sh::RPW + lane / LPR;
-    if (rows[p] < total_rows) {
-      const float4 *src = reinterpret_cast<const float4 *>(S + rows[p] * D);
-#pragma unroll
-      for (int m = 0; m < NV; ++m) s[p][m] = load_stream(src + j + LPR * m);
-    }
+    for (int m = 0; m < NV; ++m) s[m] = load_stream(src + j + LPR * m);
   }
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int64_t R = rows[p];
-    const bool live = R < total_rows;
-    // (b, h, i) of this row; rows of dead lanes alias row 0 for the loads.
-    const int64_t Rc = live ? R : 0;
-    const int i = static_cast<int>(Rc % D);
-    const int64_t bh = Rc / D;
-    const int h = static_cast<int>(bh % g.H_v);
-    const int b = static_cast<int>(bh / g.H_v);
-    const int kh = h / g.G;
-    const float *qrow = qkv + static_cast<size_t>(b) * g.C_ch + kh * D;
+  for (int t = 0; t < TT; ++t) {
+    const float *qrow = qkv + (bt0 + t) * g.C_ch + kh * D;
     const float *krow = qrow + g.H_k * D;
     float4 kv[NV], qv[NV];
 #pragma unroll
@@ -95,15 +131,14 @@ __global__ __launch_bounds__(256) void decode_kernel(Geom g, const float *__rest
     float pk = 0.f, pq = 0.f, kq = 0.f;
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
-      const float4 sv = live ? s[p][m] : make_float4(0.f, 0.f, 0.f, 0.f);
-      pk = __builtin_fmaf(sv.x, kv[m].x, pk);
-      pk = __builtin_fmaf(sv.y, kv[m].y, pk);
-      pk = __builtin_fmaf(sv.z, kv[m].z, pk);
-      pk = __builtin_fmaf(sv.w, kv[m].w, pk);
-      pq = __builtin_fmaf(sv.x, qv[m].x, pq);
-      pq = __builtin_fmaf(sv.y, qv[m].y, pq);
-      pq = __builtin_fmaf(sv.z, qv[m].z, pq);
-      pq = __builtin_fmaf(sv.w, qv[m].w, pq);
+      pk = __builtin_fmaf(s[m].x, kv[m].x, pk);
+      pk = __builtin_fmaf(s[m].y, kv[m].y, pk);
+      pk = __builtin_fmaf(s[m].z, kv[m].z, pk);
+      pk = __builtin_fmaf(s[m].w, kv[m].w, pk);
+      pq = __builtin_fmaf(s[m].x, qv[m].x, pq);
+      pq = __builtin_fmaf(s[m].y, qv[m].y, pq);
+      pq = __builtin_fmaf(s[m].z, qv[m].z, pq);
+      pq = __builtin_fmaf(s[m].w, qv[m].w, pq);
       kq = __builtin_fmaf(kv[m].x, qv[m].x, kq);
       kq = __builtin_fmaf(kv[m].y, qv[m].y, kq);
       kq = __builtin_fmaf(kv[m].z, qv[m].z, kq);
@@ -115,58 +150,69 @@ __global__ __launch_bounds__(256) void decode_kernel(Geom g, const float *__rest
       pq += __shfl_xor(pq, msk, kWave);
       kq += __shfl_xor(kq, msk, kWave);
     }
-    const size_t gh = static_cast<size_t>(b) * g.H_v + h;
+    const size_t gh = (bt0 + t) * g.H_v + h;
     const float a = __expf(gl[gh]);
     const float bt = beta[gh];
-    const float vi = qkv[static_cast<size_t>(b) * g.C_ch + 2 * g.H_k * D + h * D + i];
+    const float vi = qkv[(bt0 + t) * g.C_ch + 2 * g.H_k * D + h * D + i];
     const float u = bt * (vi - a * pk);
     const float o = a * pq + u * kq;
-    if (live) {
-      float4 *dst = reinterpret_cast<float4 *>(S + R * D);
 #pragma unroll
-      for (int m = 0; m < NV; ++m) {
-        float4 n;
-        n.x = __builtin_fmaf(u, kv[m].x, a * s[p][m].x);
-        n.y = __builtin_fmaf(u, kv[m].y, a * s[p][m].y);
-        n.z = __builtin_fmaf(u, kv[m].z, a * s[p][m].z);
-        n.w = __builtin_fmaf(u, kv[m].w, a * s[p][m].w);
-        store_stream(dst + j + LPR * m, n);
-      }
-      if (j == 0) {
-        const size_t yi = gh * D + i;
-        store_elem<DTY>(y, yi, o * sigmoidf_(load_elem<DTZ>(z, yi)));
-      }
+    for (int m = 0; m < NV; ++m) {
+      s[m].x = __builtin_fmaf(u, kv[m].x, a * s[m].x);
+      s[m].y = __builtin_fmaf(u, kv[m].y, a * s[m].y);
+      s[m].z = __builtin_fmaf(u, kv[m].z, a * s[m].z);
+      s[m].w = __builtin_fmaf(u, kv[m].w, a * s[m].w);
+    }
+    const int so = out_slot<TT>(sa, b, t, sin);
+    if (so >= 0) {
+      float4 *dst = reinterpret_cast<float4 *>(S + so * pool_stride + row_off);
+#pragma unroll
+      for (int m = 0; m < NV; ++m) store_stream(dst + j + LPR * m, s[m]);
+    }
+    if (j == 0) {
+      const size_t yi = gh * D + i;
+      store_elem<DTY>(y, yi, o * sigmoidf_(load_elem<DTZ>(z, yi)));
     }
   }
 }
 
-template <int D, int DTZ, int DTY>
-static void launch_decode_t(const Geom &g, dim3 grid, const float *qkv, const void *z,
-                            const float *gl, const float *beta, float *S, void *y, int64_t rows,
+template <int D, int NPL, int TT>
+static void launch_decode_t(const Geom &g, const float *qkv, const void *z, const float *gl,
+                            const float *beta, float *S, void *y, const SlotArgs &sa,
                             hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<D, DTZ, DTY, 1>), grid, dim3(256), 0, s, g, qkv, z, gl,
-                     beta, S, y, rows);
+  const int64_t rows = static_cast<int64_t>(g.B) * g.H_v * D;
+  const dim3 grid(static_cast<unsigned>((rows + DecodeShape<D, NPL>::RPB - 1) /
+                                        DecodeShape<D, NPL>::RPB));
+  const int key = (g.in_dt << 1) | g.out_dt;
+  switch (key) {
+    case 0: hipLaunchKernelGGL((decode_kernel<D, NPL, 0, 0, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<D, NPL, 0, 1, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, NPL, 1, 0, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows); break;
+    default: hipLaunchKernelGGL((decode_kernel<D, NPL, 1, 1, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows); break;
+  }
 }
 
-hipError_t launch_decode(const Geom &g, const float *qkv, const void *z, const float *gl,
-                         const float *beta, float *S, void *y, hipStream_t s) {
-  const int64_t rows = static_cast<int64_t>(g.B) * g.H_v * g.D;
-  const int rpb = (g.D == 128) ? DecodeShape<128>::RPB : DecodeShape<16>::RPB;
-  dim3 grid(static_cast<unsigned>((rows + rpb - 1) / rpb));
-  const int key = (g.in_dt << 1) | g.out_dt;
-#define GDN_DEC(Dv)                                                               \
-  switch (key) {                                                                  \
-    case 0: launch_decode_t<Dv, 0, 0>(g, grid, qkv, z, gl, beta, S, y, rows, s); break; \
-    case 1: launch_decode_t<Dv, 0, 1>(g, grid, qkv, z, gl, beta, S, y, rows, s); break; \
-    case 2: launch_decode_t<Dv, 1, 0>(g, grid, qkv, z, gl, beta, S, y, rows, s); break; \
-    default: launch_decode_t<Dv, 1, 1>(g, grid, qkv, z, gl, beta, S, y, rows, s); break; \
+template <int TT>
+static void launch_decode_tt(const Geom &g, const float *qkv, const void *z, const float *gl,
+                             const float *beta, float *S, void *y, const SlotArgs &sa,
+                             hipStream_t s) {
+  if (g.D == 128)  // 8 lanes x 16 floats per row, 32 rows per block
+    launch_decode_t<128, 16, TT>(g, qkv, z, gl, beta, S, y, sa, s);
+  else
+    launch_decode_t<16, 4, TT>(g, qkv, z, gl, beta, S, y, sa, s);
+}
+
+hipError_t launch_decode(const Geom &g, int T, const float *qkv, const void *z, const float *gl,
+                         const float *beta, float *S, void *y, int n_slots,
+                         const int32_t *in_slots, const int32_t *out_slots, hipStream_t s) {
+  const SlotArgs sa{in_slots, out_slots, n_slots};
+  switch (T) {
+    case 1: launch_decode_tt<1>(g, qkv, z, gl, beta, S, y, sa, s); break;
+    case 2: launch_decode_tt<2>(g, qkv, z, gl, beta, S, y, sa, s); break;
+    case 3: launch_decode_tt<3>(g, qkv, z, gl, beta, S, y, sa, s); break;
+    case 4: launch_decode_tt<4>(g, qkv, z, gl, beta, S, y, sa, s); break;
+    default: return hipErrorInvalidValue;
   }
-  if (g.D == 128) {
-    GDN_DEC(128)
-  } else {
-    GDN_DEC(16)
-  }
-#undef GDN_DEC
   return hipGetLastError();
 }
 

@@ -211,8 +211,10 @@ bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *w) {
   return true;
 }
 
-size_t decode_ws_bytes(const Geom &g) {
-  return round_up(static_cast<size_t>(g.B) * g.C_ch * 4, 256);
+// Decode workspace: the fp32 [B][T][C_ch] output of the conv step (q
+// scaled and normalised, k normalised, v), read by the state stream.
+size_t decode_ws_bytes(const Geom &g, int T) {
+  return round_up(static_cast<size_t>(g.B) * T * g.C_ch * 4, 256);
 }
 
 }  // namespace gdn
@@ -269,7 +271,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int64_t T, int32_t chun
 
 size_t gdn_decode_workspace_bytes(const gdn_dims *dims) {
   Geom g;
-  return check_dims(dims, &g) == GDN_OK ? decode_ws_bytes(g) : 0;
+  return check_dims(dims, &g) == GDN_OK ? decode_ws_bytes(g, 1) : 0;
 }
 
 int gdn_conv1d(const gdn_dims *dims, int64_t T, const void *x, const void *conv_w,
@@ -288,6 +290,22 @@ int gdn_conv1d(const gdn_dims *dims, int64_t T, const void *x, const void *conv_
   hipError_t e = launch_conv_plain(g, T, x, conv_w, conv_state, qkv_out,
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_conv1d");
+}
+
+// The three launches of one prefill call (conv, prep with the q/k history
+// roll, state pass with the v history roll and the gate).
+static hipError_t enqueue_prefill(const Geom &g, const PrefillWs &L, const void *x, const void *z,
+                                  const float *gl, const float *beta, const void *conv_w,
+                                  void *conv_state, float *rec_state, void *y, char *w,
+                                  hipStream_t s, LaunchTimer *tm) {
+  hipError_t e = tm->mark(s);
+  if (e == hipSuccess) e = launch_conv_prefill(g, L, x, conv_w, conv_state, w, s);
+  if (e == hipSuccess) e = tm->mark(s);
+  if (e == hipSuccess) e = launch_prefill_prep(g, L, gl, beta, w, x, conv_state, s);
+  if (e == hipSuccess) e = tm->mark(s);
+  if (e == hipSuccess) e = launch_prefill_state(g, L, z, rec_state, y, w, x, conv_w, conv_state, s);
+  if (e == hipSuccess) e = tm->mark(s);
+  return e;
 }
 
 static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const void *x,
@@ -316,15 +334,9 @@ static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const vo
   if (ws_bytes < L.total) return GDN_ERR_WORKSPACE;
   if (injected_launch_failure()) return GDN_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char *w = static_cast<char *>(ws);
   LaunchTimer tm(kernel_ms);
-  hipError_t e = tm.mark(s);
-  if (e == hipSuccess) e = launch_conv_prefill(g, L, x, conv_w, conv_state, w, s);
-  if (e == hipSuccess) e = tm.mark(s);
-  if (e == hipSuccess) e = launch_prefill_prep(g, L, gl, beta, w, x, conv_state, s);
-  if (e == hipSuccess) e = tm.mark(s);
-  if (e == hipSuccess) e = launch_prefill_state(g, L, z, rec_state, y, w, x, conv_w, conv_state, s);
-  if (e == hipSuccess) e = tm.mark(s);
+  hipError_t e = enqueue_prefill(g, L, x, z, gl, beta, conv_w, conv_state, rec_state, y,
+                                 static_cast<char *>(ws), s, &tm);
   if (e == hipSuccess) e = tm.elapsed();
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_prefill_chunked");
 }
@@ -346,41 +358,74 @@ int gdn_prefill_chunked_timed(const gdn_dims *dims, int64_t T, int32_t chunk, co
                       ws_bytes, stream, kernel_ms);
 }
 
-// validate_only: run every check on the arguments except those of `ws`
-// (which may be null then) and return without any HIP call.
-static int decode_impl(const gdn_dims *dims, const void *x, const void *z, const float *gl,
-                    const float *beta, const void *conv_w, void *conv_state,
-                    float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream,
-                    float *kernel_ms, bool validate_only = false) {
+// One decode call of T tokens per sequence on slot-indexed states (the plain
+// decode step is T = 1 with the states as a pool of B slots, sequence b in
+// slot b).  validate_only: run every check except those of `ws` (which may be
+// null then) and return without any HIP call.
+struct DecodeArgs {
+  int T;
+  const void *x, *z;
+  const float *gl, *beta;
+  const void *conv_w;
+  void *conv_pool;
+  float *rec_pool;
+  int n_slots;
+  const int32_t *in_slots, *out_slots;  // device arrays or null
+  void *y, *ws;
+  size_t ws_bytes;
+  void *stream;
+  float *kernel_ms;  // timed variant: [0] conv step, [1] state stream
+};
+
+static int decode_run(const gdn_dims *dims, const DecodeArgs &a, const char *where,
+                      bool validate_only = false) {
   Geom g;
   int rc = check_dims(dims, &g);
   if (rc) return rc;
+  if (a.T < 1 || a.T > kMaxMultiTokens || a.n_slots < 1) return GDN_ERR_INVALID_ARG;
   const size_t es = esize(g.in_dt), eo = esize(g.out_dt);
-  const size_t B = static_cast<size_t>(g.B);
-  const size_t need = decode_ws_bytes(g);
-  const Buf in[] = {{x, B * g.C_ch * es, es},
-                    {z, B * g.H_v * g.D * es, es},
-                    {gl, B * g.H_v * 4, 4},
-                    {beta, B * g.H_v * 4, 4},
-                    {conv_w, static_cast<size_t>(g.C_ch) * g.W * es, es}};
-  const Buf out[] = {{conv_state, conv_state_bytes(g), es},
-                     {rec_state, rec_state_bytes(g), 16},
-                     {y, B * g.H_v * g.D * eo, eo},
-                     {ws, need, 16}};
-  if ((rc = check_buffers(in, 5, out, validate_only ? 3 : 4))) return rc;
+  const size_t bt = static_cast<size_t>(g.B) * a.T;
+  const size_t ns = static_cast<size_t>(a.n_slots);
+  const size_t need = decode_ws_bytes(g, a.T);
+  Buf in[7] = {{a.x, bt * g.C_ch * es, es},
+               {a.z, bt * g.H_v * g.D * es, es},
+               {a.gl, bt * g.H_v * 4, 4},
+               {a.beta, bt * g.H_v * 4, 4},
+               {a.conv_w, static_cast<size_t>(g.C_ch) * g.W * es, es}};
+  int n_in = 5;
+  if (a.in_slots) in[n_in++] = {a.in_slots, static_cast<size_t>(g.B) * 4, 4};
+  if (a.out_slots) in[n_in++] = {a.out_slots, bt * 4, 4};
+  const Buf out[] = {{a.conv_pool, ns * (g.W - 1) * g.C_ch * es, es},
+                     {a.rec_pool, ns * g.H_v * g.D * g.D * 4, 16},
+                     {a.y, bt * g.H_v * g.D * eo, eo},
+                     {a.ws, need, 16}};
+  if ((rc = check_buffers(in, n_in, out, validate_only ? 3 : 4))) return rc;
   if (validate_only) return GDN_OK;
-  if (ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (a.ws_bytes < need) return GDN_ERR_WORKSPACE;
   if (injected_launch_failure()) return GDN_ERR_HIP;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float *qkv = static_cast<float *>(ws);
-  LaunchTimer tm(kernel_ms);
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+  LaunchTimer tm(a.kernel_ms);
+  float *qkv = static_cast<float *>(a.ws);
   hipError_t e = tm.mark(s);
-  if (e == hipSuccess) e = launch_conv_plain(g, 1, x, conv_w, conv_state, qkv, s);
+  if (e == hipSuccess)
+    e = launch_conv_step(g, a.T, a.x, a.conv_w, a.conv_pool, qkv, a.in_slots, a.out_slots,
+                         a.n_slots, s);
   if (e == hipSuccess) e = tm.mark(s);
-  if (e == hipSuccess) e = launch_decode(g, qkv, z, gl, beta, rec_state, y, s);
+  if (e == hipSuccess)
+    e = launch_decode(g, a.T, qkv, a.z, a.gl, a.beta, a.rec_pool, a.y, a.n_slots, a.in_slots,
+                      a.out_slots, s);
   if (e == hipSuccess) e = tm.mark(s);
   if (e == hipSuccess) e = tm.elapsed();
-  return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_decode_step");
+  return e == hipSuccess ? GDN_OK : set_hip_error(e, where);
+}
+
+static int decode_impl(const gdn_dims *dims, const void *x, const void *z, const float *gl,
+                       const float *beta, const void *conv_w, void *conv_state,
+                       float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream,
+                       float *kernel_ms, bool validate_only = false) {
+  const DecodeArgs a{1, x, z, gl, beta, conv_w, conv_state, rec_state, dims ? dims->B : 0,
+                     nullptr, nullptr, y, ws, ws_bytes, stream, kernel_ms};
+  return decode_run(dims, a, "gdn_decode_step", validate_only);
 }
 
 int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, const float *gl,
@@ -396,7 +441,7 @@ int gdn_decode_step_noalloc(const gdn_dims *dims, const void *x, const void *z, 
   Geom g;
   int rc = check_dims(dims, &g);
   if (rc) return rc;
-  const size_t need = decode_ws_bytes(g);
+  const size_t need = decode_ws_bytes(g, 1);
   if (need > kNoAllocScratchBytes) return GDN_ERR_TOO_LARGE;
   // Every other check (pointers, alignment, aliasing) runs in decode_impl
   // before the first launch; the scratch itself is checked against the
@@ -420,6 +465,112 @@ int gdn_decode_step_timed(const gdn_dims *dims, const void *x, const void *z, co
   if (!kernel_ms) return GDN_ERR_INVALID_ARG;
   return decode_impl(dims, x, z, gl, beta, conv_w, conv_state, rec_state, y, ws, ws_bytes,
                      stream, kernel_ms);
+}
+
+int gdn_decode_multi(const gdn_dims *dims, int32_t T, const void *x, const void *z,
+                     const float *gl, const float *beta, const void *conv_w, void *conv_pool,
+                     float *rec_pool, int32_t n_slots, const int32_t *in_slots,
+                     const int32_t *out_slots, void *y, void *ws, size_t ws_bytes,
+                     void *stream) {
+  if (!in_slots) return GDN_ERR_INVALID_ARG;
+  const DecodeArgs a{T, x, z, gl, beta, conv_w, conv_pool, rec_pool, n_slots, in_slots,
+                     out_slots, y, ws, ws_bytes, stream, nullptr};
+  return decode_run(dims, a, "gdn_decode_multi");
+}
+
+// Packed variable-length prefill: host-side sequence table, validated in
+// full before anything is enqueued; then each non-empty sequence runs the
+// chunked prefill on its own rows and its own slot, in stream order, all
+// sharing one workspace.
+static int varlen_check(const Geom &g, const int64_t *cu, int32_t chunk, size_t *ws_need,
+                        int64_t *T_total) {
+  if (!cu) return GDN_ERR_INVALID_ARG;
+  if (cu[0] != 0) return GDN_ERR_INVALID_ARG;
+  size_t need = 0;
+  for (int n = 0; n < g.B; ++n) {
+    const int64_t len = cu[n + 1] - cu[n];
+    if (len < 0 || len > kMaxTokens) return GDN_ERR_INVALID_ARG;
+    if (len == 0) continue;
+    Geom g1 = g;
+    g1.B = 1;
+    PrefillWs L;
+    if (!prefill_ws_layout(g1, len, chunk, &L)) return GDN_ERR_UNSUPPORTED;
+    need = std::max(need, L.total);
+  }
+  if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128) return GDN_ERR_UNSUPPORTED;
+  if (cu[g.B] > (int64_t(1) << 40)) return GDN_ERR_INVALID_ARG;
+  *ws_need = std::max<size_t>(need, 256);
+  *T_total = cu[g.B];
+  return GDN_OK;
+}
+
+size_t gdn_prefill_varlen_workspace_bytes(const gdn_dims *dims, const int64_t *cu_seqlens,
+                                          int32_t chunk) {
+  Geom g;
+  size_t need = 0;
+  int64_t T_total = 0;
+  if (check_dims(dims, &g) != GDN_OK || varlen_check(g, cu_seqlens, chunk, &need, &T_total))
+    return 0;
+  return need;
+}
+
+int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, int32_t chunk,
+                       const void *x, const void *z, const float *gl, const float *beta,
+                       const void *conv_w, void *conv_pool, float *rec_pool, int32_t n_slots,
+                       const int32_t *slots, void *y, void *ws, size_t ws_bytes, void *stream) {
+  Geom g;
+  int rc = check_dims(dims, &g);
+  if (rc) return rc;
+  size_t need = 0;
+  int64_t T_total = 0;
+  if ((rc = varlen_check(g, cu_seqlens, chunk, &need, &T_total))) return rc;
+  if (!slots || n_slots < 1) return GDN_ERR_INVALID_ARG;
+  for (int n = 0; n < g.B; ++n) {
+    if (slots[n] < 0 || slots[n] >= n_slots) return GDN_ERR_INVALID_ARG;
+    for (int m = 0; m < n; ++m)
+      if (slots[m] == slots[n]) return GDN_ERR_INVALID_ARG;  // two sequences, one state
+  }
+  const size_t es = esize(g.in_dt), eo = esize(g.out_dt);
+  const size_t tt = static_cast<size_t>(T_total), ns = static_cast<size_t>(n_slots);
+  const size_t conv_slot = static_cast<size_t>(g.W - 1) * g.C_ch * es;
+  const size_t rec_slot = static_cast<size_t>(g.H_v) * g.D * g.D * 4;
+  const Buf in[] = {{x, tt * g.C_ch * es, 16},
+                    {z, tt * g.H_v * g.D * es, 16},
+                    {gl, tt * g.H_v * 4, 4},
+                    {beta, tt * g.H_v * 4, 4},
+                    {conv_w, static_cast<size_t>(g.C_ch) * g.W * es, es}};
+  const Buf out[] = {{conv_pool, ns * conv_slot, 16},
+                     {rec_pool, ns * rec_slot, 16},
+                     {y, tt * g.H_v * g.D * eo, eo},
+                     {ws, need, 16}};
+  // Inputs and outputs may be empty (all sequences of length 0): then only
+  // the state pools and the workspace are checked.
+  if (T_total == 0) {
+    if ((rc = check_buffers(nullptr, 0, out, 2))) return rc;
+  } else if ((rc = check_buffers(in, 5, out, 4))) {
+    return rc;
+  }
+  if (T_total > 0 && ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (injected_launch_failure()) return GDN_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LaunchTimer tm(nullptr);
+  Geom g1 = g;
+  g1.B = 1;
+  for (int n = 0; n < g.B; ++n) {
+    const int64_t t0 = cu_seqlens[n], len = cu_seqlens[n + 1] - t0;
+    if (len == 0) continue;
+    PrefillWs L;
+    prefill_ws_layout(g1, len, chunk, &L);
+    const size_t tok = static_cast<size_t>(t0);
+    const hipError_t e = enqueue_prefill(
+        g1, L, static_cast<const char *>(x) + tok * g.C_ch * es,
+        static_cast<const char *>(z) + tok * g.H_v * g.D * es, gl + tok * g.H_v,
+        beta + tok * g.H_v, conv_w, static_cast<char *>(conv_pool) + slots[n] * conv_slot,
+        rec_pool + static_cast<size_t>(slots[n]) * (rec_slot / 4),
+        static_cast<char *>(y) + tok * g.H_v * g.D * eo, static_cast<char *>(ws), s, &tm);
+    if (e != hipSuccess) return set_hip_error(e, "gdn_prefill_varlen");
+  }
+  return GDN_OK;
 }
 
 int gdn_state_check(const gdn_dims *dims, const void *blob, size_t blob_bytes) {

@@ -55,7 +55,7 @@ bool prefill_ws_layout(const Geom &g, int64_t T, int C, PrefillWs *ws);
 __host__ __device__ inline bool prefill_split_roles(const Geom &g, const PrefillWs &L) {
   return g.D == 128 && L.C == 64;
 }
-size_t decode_ws_bytes(const Geom &g);
+size_t decode_ws_bytes(const Geom &g, int T);
 
 // Size of the fixed device array that serves as the decode workspace of
 // gdn_decode_step_noalloc, and its device address on the GPU of stream `s`
@@ -70,8 +70,17 @@ hipError_t launch_conv_prefill(const Geom &g, const PrefillWs &L, const void *x,
                                const void *w, const void *hist, char *ws, hipStream_t s);
 hipError_t launch_conv_roll(const Geom &g, int64_t T, const void *x, void *hist,
                             hipStream_t s);
-hipError_t launch_decode(const Geom &g, const float *qkv, const void *z, const float *gl,
-                         const float *beta, float *S, void *y, hipStream_t s);
+// Decode of T = 1..kMaxMultiTokens tokens per sequence in two launches: the
+// conv step writes qkv [B][T][C_ch] fp32 and rolls the histories into their
+// out slots; the state stream then reads qkv.  in_slots / out_slots may be
+// null (sequence b in slot b, state after the last token back into it).
+constexpr int kMaxMultiTokens = 4;
+hipError_t launch_conv_step(const Geom &g, int T, const void *x, const void *w, void *hist,
+                            float *out, const int32_t *in_slots, const int32_t *out_slots,
+                            int n_slots, hipStream_t s);
+hipError_t launch_decode(const Geom &g, int T, const float *qkv, const void *z, const float *gl,
+                         const float *beta, float *S, void *y, int n_slots,
+                         const int32_t *in_slots, const int32_t *out_slots, hipStream_t s);
 // Also rolls the conv history (x, hist) after the sequence.
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
                                const float *beta, char *ws, const void *x, void *hist,

@@ -149,11 +149,71 @@ GDN_API int gdn_prefill_chunked(const gdn_dims *dims, int64_t T, int32_t chunk, 
 
 /* The same function as gdn_prefill_chunked at T = 1, tuned for one token per
  * sequence: every recurrent state is streamed from HBM once and written back
- * once.  Shapes as above with T = 1.  `ws`: at least
- * gdn_decode_workspace_bytes(dims) bytes. */
+ * once ("Add a performance-parity Qwen3.8-27B Q4 and Q8 text backend on
+ * Metal", section Scope: separately tuned single-step decode behind the same
+ * semantic interface as prefill).  Shapes as above with T = 1.  `ws`: at
+ * least gdn_decode_workspace_bytes(dims) bytes (contents ignored). */
 GDN_API int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, const float *g,
                     const float *beta, const void *conv_w, void *conv_state,
                     float *rec_state, void *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Slot-indexed decode of T = 1..4 tokens per sequence, with the state after
+ * each token kept in a slot of its own, d = 128 only (sources: "Add Qwen3.8
+ * MTP and multimodal inference on Metal without regressing text", section
+ * Correctness gates: MTP candidate verification, cache updates and
+ * rollback; the model card "Qwen3.8-27B FP8 + native MTP + multimodal Core
+ * AI", section What is fused: a three-token target prefill; "Implement the
+ * Qwen3.8 Flash Next Rust and Metal text core", implementation comment:
+ * resident-state swaps).  Two launches, like gdn_decode_step: the conv step
+ * for all T tokens, then one pass over the states that keeps them in
+ * registers across the T tokens.  dims->B rows (sequences);
+ *   x [B][T][C_ch], z [B][T][H_v][d_v], g, beta [B][T][H_v], y [B][T][H_v][d_v]
+ *   as for prefill; conv_w as above;
+ *   conv_pool [n_slots][W-1][C_ch] in_dtype and rec_pool
+ *   [n_slots][H_v][d_v][d_k] fp32: a pool of conv histories and recurrent
+ *   states, addressed by slot;
+ *   in_slots [B] int32, device memory: the slot each sequence starts from;
+ *   out_slots [B][T] int32, device memory, or NULL: the slot that receives
+ *   the state (history and recurrent state) after token t of sequence b;
+ *   NULL means the in slot after the last token and nothing before it.
+ * The step equals T single-token decode steps; an MTP verifier passes
+ * distinct out slots per token and afterwards keeps the slot of the last
+ * accepted token (rollback without any copy).  A sequence whose in slot lies
+ * outside [0, n_slots) is a padding row: its y rows are written as zero and
+ * nothing else is touched; out slots outside that range are not stored.
+ * Slot values live on the device and are not validated on the host.  One
+ * sequence may use its in slot as an out slot; different sequences must not
+ * share any slot (they would race).  `ws`: at least
+ * T * gdn_decode_workspace_bytes(dims) bytes (contents ignored).  Errors:
+ * GDN_ERR_INVALID_ARG for T outside 1..4, n_slots < 1 or a null in_slots. */
+GDN_API int gdn_decode_multi(const gdn_dims *dims, int32_t T, const void *x, const void *z,
+                             const float *g, const float *beta, const void *conv_w,
+                             void *conv_pool, float *rec_pool, int32_t n_slots,
+                             const int32_t *in_slots, const int32_t *out_slots, void *y,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Packed variable-length prefill ("Implement the Qwen3.8 Flash Next Rust and
+ * Metal text core", section Implementation: prefill/small-batch
+ * infrastructure).  dims->B sequences, packed back to back:
+ *   cu_seqlens [B+1] int64, HOST memory: sequence n owns token rows
+ *   cu_seqlens[n] .. cu_seqlens[n+1]-1 (cu_seqlens[0] = 0, non-decreasing;
+ *   a sequence may be empty; each at most 2^24 tokens);
+ *   x [T_total][C_ch], z [T_total][H_v][d_v], g, beta [T_total][H_v],
+ *   y [T_total][H_v][d_v] with T_total = cu_seqlens[B];
+ *   conv_pool, rec_pool: state pools as for gdn_decode_multi (16-byte
+ *   aligned); slots [B] int32, HOST memory: the slot of each sequence, in
+ *   [0, n_slots) and pairwise distinct (checked; GDN_ERR_INVALID_ARG).
+ * Each sequence gets exactly what gdn_prefill_chunked gives it alone, and its
+ * slot holds its states afterwards; other slots are not touched.  `ws`: at
+ * least gdn_prefill_varlen_workspace_bytes(dims, cu_seqlens, chunk) bytes
+ * (the largest single-sequence prefill workspace; contents ignored). */
+GDN_API size_t gdn_prefill_varlen_workspace_bytes(const gdn_dims *dims,
+                                                  const int64_t *cu_seqlens, int32_t chunk);
+GDN_API int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, int32_t chunk,
+                               const void *x, const void *z, const float *g, const float *beta,
+                               const void *conv_w, void *conv_pool, float *rec_pool,
+                               int32_t n_slots, const int32_t *slots, void *y, void *ws,
+                               size_t ws_bytes, void *stream);
 
 /* gdn_decode_step without a workspace argument and without any allocation,
  * for callers that cannot allocate device memory: code under HIP graph
@@ -162,7 +222,7 @@ GDN_API int gdn_decode_step(const gdn_dims *dims, const void *x, const void *z, 
  * gdn_decode_step; it runs the same kernels with the decode workspace placed
  * in a fixed 16 MiB device array that the library holds on each GPU it runs
  * on until the process ends.  Calls whose gdn_decode_workspace_bytes(dims)
- * exceeds 16 MiB (about B = 409 at C_ch = 10240) are rejected with
+ * exceeds 16 MiB (B above 409 at C_ch = 10240) are rejected with
  * GDN_ERR_TOO_LARGE before anything is enqueued.  The first call on a GPU
  * looks the array's device address up (no allocation, no stream work).
  * Every call on one GPU shares that GPU's array: calls that overlap in time

@@ -173,3 +173,81 @@ def layer(x, z, g, beta, w, hist, S0, *, H_k: int, H_v: int, d_k: int, d_v: int,
                              _ptr(tasks), n, nth)
     assert rc == 0, rc
     return y, S, conv_history_next(x, hist)
+
+
+# ---------------------------------------------------------------------------
+# Serving-shaped calls, composed from `layer` (each sequence is one plain
+# layer call on its own tokens and its own state; nothing else is computed).
+# Sources: "Add Qwen3.8 MTP and multimodal inference on Metal without
+# regressing text", section Correctness gates (MTP candidate generation,
+# verification, cache updates, rollback); the model card "Qwen3.8-27B FP8 +
+# native MTP + multimodal Core AI", section What is fused (a three-token
+# target prefill); "Implement the Qwen3.8 Flash Next Rust and Metal text
+# core", section Implementation (prefill/small-batch infrastructure) and its
+# implementation comment (resident-state swaps).
+
+def layer_varlen(x, z, g, beta, w, hist_pool, S_pool, cu_seqlens, slots, *, H_k: int, H_v: int,
+                 d_k: int, d_v: int, eps: float, q_scale: float = 1.0, nthreads=None):
+    """Packed variable-length prefill.
+
+    x [T_total, C_ch], z [T_total, H_v, d_v], g/beta [T_total, H_v]: the
+    sequences' tokens back to back; sequence n owns rows cu_seqlens[n] ..
+    cu_seqlens[n+1]-1 and the states in slot slots[n] of hist_pool
+    [n_slots, W-1, C_ch] and S_pool [n_slots, H_v, d_v, d_k].
+    Returns (y float64 [T_total, H_v, d_v], S_pool float64, hist_pool): the
+    slots of the sequences hold their states after their tokens, every other
+    slot is returned unchanged (a sequence of length 0 leaves its slot as is).
+    """
+    cu = [int(c) for c in cu_seqlens]
+    T_total = x.shape[0]
+    assert cu[0] == 0 and cu[-1] == T_total and len(slots) == len(cu) - 1
+    y = np.full((T_total, H_v, d_v), np.nan)
+    S_out = np.array(S_pool, np.float64, copy=True)
+    h_out = np.array(hist_pool, copy=True)
+    for n, s in enumerate(slots):
+        a, b = cu[n], cu[n + 1]
+        if b == a:
+            continue
+        yn, Sn, hn = layer(x[None, a:b], z[None, a:b], g[None, a:b], beta[None, a:b], w,
+                           hist_pool[None, s], S_pool[None, s], H_k=H_k, H_v=H_v, d_k=d_k,
+                           d_v=d_v, eps=eps, q_scale=q_scale, nthreads=nthreads)
+        y[a:b] = yn[0]
+        S_out[s] = Sn[0]
+        h_out[s] = hn[0]
+    return y, S_out, h_out
+
+
+def decode_multi(x, z, g, beta, w, hist_pool, S_pool, in_slots, out_slots, *, H_k: int,
+                 H_v: int, d_k: int, d_v: int, eps: float, q_scale: float = 1.0):
+    """T tokens per sequence from slot-indexed states, with the state after
+    every token stored to a slot of its own (MTP verify and rollback keep
+    the per-token states and pick one).
+
+    x [B, T, C_ch], z [B, T, H_v, d_v], g/beta [B, T, H_v]; in_slots [B]:
+    the slot each sequence starts from; out_slots [B, T]: the slot that
+    receives the state after token t (or None: the in slot after the last
+    token, nothing for earlier tokens).  A sequence whose in slot lies outside
+    [0, n_slots) is a padding row (y zero, nothing stored); an out slot
+    outside that range is not stored.  The state after token t is the plain
+    layer over tokens 0..t from the in slot's state.
+    Returns (y float64 [B, T, H_v, d_v], S_pool float64, hist_pool).
+    """
+    B, T = x.shape[0], x.shape[1]
+    n_slots = S_pool.shape[0]
+    y = np.zeros((B, T, H_v, d_v))
+    S_out = np.array(S_pool, np.float64, copy=True)
+    h_out = np.array(hist_pool, copy=True)
+    for b in range(B):
+        s = int(in_slots[b])
+        if not 0 <= s < n_slots:
+            continue
+        for t in range(T):
+            o = (s if t == T - 1 else -1) if out_slots is None else int(out_slots[b][t])
+            yt, St, ht = layer(x[b:b + 1, :t + 1], z[b:b + 1, :t + 1], g[b:b + 1, :t + 1],
+                               beta[b:b + 1, :t + 1], w, hist_pool[None, s], S_pool[None, s],
+                               H_k=H_k, H_v=H_v, d_k=d_k, d_v=d_v, eps=eps, q_scale=q_scale)
+            y[b, t] = yt[0, t]
+            if 0 <= o < n_slots:
+                S_out[o] = St[0]
+                h_out[o] = ht[0]
+    return y, S_out, h_out

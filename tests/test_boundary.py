@@ -206,6 +206,64 @@ def test_decode_noalloc_validates_before_any_hip_call(lib, dims):
     assert "fixed scratch" in lib.gdn_status_str(TOO_LARGE).decode()
 
 
+def test_decode_multi_rejects_and_leaves_buffers_untouched(lib, dims):
+    # Slot-indexed multi-token decode: every argument check runs on the host
+    # before any HIP call (the slot values themselves live on the device).
+    d = dims
+    d.d_k = d.d_v = 128
+    T = 3
+    need = T * lib.gdn_decode_workspace_bytes(ctypes.byref(d))
+    b = Bufs(d, T, need)
+    slots = np.zeros(d.B * T + 64, np.int32)
+    sp = lambda off=0: ctypes.c_void_p(slots.ctypes.data + off)
+    pool_S = b.p("S")  # B = 2 slots' worth; n_slots = 2 below unless changed
+
+    def call(**o):
+        return lib.gdn_decode_multi(
+            ctypes.byref(d), o.get("T", T), b.p("x"), b.p("z"), b.p("g"), b.p("beta"), b.p("w"),
+            o.get("hist", b.p("hist")), o.get("S", pool_S), o.get("n_slots", d.B),
+            o.get("ins", sp()), o.get("outs", sp(64)), o.get("y", b.p("y")), b.p("ws"),
+            o.get("ws_bytes", need), None)
+
+    assert call(T=0) == INVALID
+    assert call(T=5) == INVALID
+    assert call(n_slots=0) == INVALID
+    assert call(ins=None) == INVALID
+    assert call(y=b.p("S")) == ALIAS
+    assert call(S=b.p("S", 4)) == ALIGN
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert b.unchanged()
+
+
+def test_prefill_varlen_rejects_bad_tables_and_leaves_buffers_untouched(lib, dims):
+    d = dims
+    d.B = 3
+    cu = np.array([0, 5, 5, 12], np.int64)
+    pcu = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    need = lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(d), pcu(cu), 64)
+    assert need > 0
+    one = lib.gdn_prefill_workspace_bytes(ctypes.byref(d), 7, 64)  # B=3 here: an upper bound
+    assert need <= one
+    b = Bufs(d, 4, need)  # 3 * 4 = 12 token rows
+    slots = np.array([2, 0, 1], np.int32)
+
+    def call(cu_=cu, slots_=slots, n_slots=3, chunk=64, **o):
+        return lib.gdn_prefill_varlen(
+            ctypes.byref(d), pcu(cu_), chunk, b.p("x"), b.p("z"), b.p("g"), b.p("beta"),
+            b.p("w"), b.p("hist"), b.p("S"), n_slots, slots_.ctypes.data_as(ctypes.c_void_p),
+            o.get("y", b.p("y")), b.p("ws"), o.get("ws_bytes", need), None)
+
+    assert call(cu_=np.array([1, 5, 5, 12], np.int64)) == INVALID   # does not start at 0
+    assert call(cu_=np.array([0, 5, 4, 12], np.int64)) == INVALID   # decreasing
+    assert call(slots_=np.array([2, 0, 3], np.int32)) == INVALID    # slot out of range
+    assert call(slots_=np.array([2, 0, 2], np.int32)) == INVALID    # two sequences, one slot
+    assert call(chunk=48) == UNSUPPORTED
+    assert call(y=b.p("x")) == ALIAS
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(d), None, 64) == 0
+    assert b.unchanged()
+
+
 def test_injected_launch_failure_leaves_buffers_untouched(lib, dims, monkeypatch):
     d, T, C = dims, 20, 32
     need = lib.gdn_prefill_workspace_bytes(ctypes.byref(d), T, C)
