@@ -18,13 +18,14 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import _lib
-from ._lib import BF16, F32, GdnError
+from ._lib import BF16, F16, F32, GdnError
 
 __all__ = [
     "Dims", "GdnError", "conv1d", "prefill_chunked", "decode_step", "decode_step_noalloc",
-    "decode_multi", "prefill_varlen", "prefill_varlen_workspace_bytes", "state_save",
+    "decode_multi", "prefill_varlen", "prefill_varlen_workspace_bytes", "gated_rmsnorm",
+    "state_save",
     "state_restore", "state_check", "prefill_workspace_bytes", "decode_workspace_bytes",
-    "rec_state_bytes", "conv_state_bytes", "state_blob_bytes", "F32", "BF16",
+    "rec_state_bytes", "conv_state_bytes", "state_blob_bytes", "F32", "BF16", "F16",
 ]
 
 
@@ -58,12 +59,17 @@ def _torch():
 
 def _dt(code: int):
     torch = _torch()
-    return torch.float32 if code == F32 else torch.bfloat16
+    return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[code]
 
 
 def _stream():
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_opt(t, name, shape, dtype):
+    """_need for an optional tensor (None passes a null pointer)."""
+    return ctypes.c_void_p(None) if t is None else _need(t, name, shape, dtype)
 
 
 def _need(t, name, shape, dtype):
@@ -137,7 +143,7 @@ def prefill_chunked(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, chunk
     dt = _dt(d.in_dtype)
     args = [
         _need(x, "x", (d.B, T, d.C_ch), dt),
-        _need(z, "z", (d.B, T, d.H_v, d.d_v), dt),
+        _need_opt(z, "z", (d.B, T, d.H_v, d.d_v), dt),
         _need(g, "g", (d.B, T, d.H_v), torch.float32),
         _need(beta, "beta", (d.B, T, d.H_v), torch.float32),
         _need(conv_w, "conv_w", (d.C_ch, d.W), dt),
@@ -170,10 +176,12 @@ def decode_step(d: Dims, x, z, g, beta, conv_w, conv_state, rec_state, y=None, w
     torch = _torch()
     L = _lib.load()
     dt = _dt(d.in_dtype)
-    zshape = tuple(z.shape)
+    zshape = tuple(z.shape) if z is not None else (
+        (d.B, d.H_v, d.d_v) if x.dim() == 2 else (d.B, 1, d.H_v, d.d_v))
     args = [
         _need(x.reshape(d.B, d.C_ch), "x", (d.B, d.C_ch), dt),
-        _need(z.reshape(d.B, d.H_v, d.d_v), "z", (d.B, d.H_v, d.d_v), dt),
+        _need_opt(None if z is None else z.reshape(d.B, d.H_v, d.d_v), "z", (d.B, d.H_v, d.d_v),
+                  dt),
         _need(g.reshape(d.B, d.H_v), "g", (d.B, d.H_v), torch.float32),
         _need(beta.reshape(d.B, d.H_v), "beta", (d.B, d.H_v), torch.float32),
         _need(conv_w, "conv_w", (d.C_ch, d.W), dt),
@@ -209,7 +217,7 @@ def decode_multi(d: Dims, x, z, g, beta, conv_w, conv_pool, rec_pool, in_slots, 
     dt = _dt(d.in_dtype)
     args = [
         _need(x, "x", (d.B, T, d.C_ch), dt),
-        _need(z, "z", (d.B, T, d.H_v, d.d_v), dt),
+        _need_opt(z, "z", (d.B, T, d.H_v, d.d_v), dt),
         _need(g, "g", (d.B, T, d.H_v), torch.float32),
         _need(beta, "beta", (d.B, T, d.H_v), torch.float32),
         _need(conv_w, "conv_w", (d.C_ch, d.W), dt),
@@ -255,7 +263,7 @@ def prefill_varlen(d: Dims, cu_seqlens, x, z, g, beta, conv_w, conv_pool, rec_po
     dt = _dt(d.in_dtype)
     args = [
         _need(x, "x", (T_total, d.C_ch), dt),
-        _need(z, "z", (T_total, d.H_v, d.d_v), dt),
+        _need_opt(z, "z", (T_total, d.H_v, d.d_v), dt),
         _need(g, "g", (T_total, d.H_v), torch.float32),
         _need(beta, "beta", (T_total, d.H_v), torch.float32),
         _need(conv_w, "conv_w", (d.C_ch, d.W), dt),
@@ -274,6 +282,28 @@ def prefill_varlen(d: Dims, cu_seqlens, x, z, g, beta, conv_w, conv_pool, rec_po
                               ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                               _stream())
     _lib.check(rc, "gdn_prefill_varlen")
+    return y
+
+
+def gated_rmsnorm(d: Dims, o, z, norm_w=None, norm_eps: float = 1e-6, y=None):
+    """Zero-centred grouped RMS norm + sigmoid gate over the ungated readout
+    o (fp32, [..., H_v, d_v], from a layer call with z=None); z like o in the
+    input dtype, or None (no gate); norm_w fp32 [d_v] or None.  Returns y in
+    d.out_dtype, shaped like o."""
+    torch = _torch()
+    L = _lib.load()
+    if tuple(o.shape[-2:]) != (d.H_v, d.d_v):
+        raise ValueError(f"o: trailing shape {tuple(o.shape[-2:])} != {(d.H_v, d.d_v)}")
+    rows = o.numel() // (d.H_v * d.d_v)
+    shape = tuple(o.shape)
+    po = _need(o, "o", shape, torch.float32)
+    pz = _need_opt(z, "z", shape, _dt(d.in_dtype))
+    pw = _need_opt(norm_w, "norm_w", (d.d_v,), torch.float32)
+    if y is None:
+        y = torch.empty(shape, dtype=_dt(d.out_dtype), device=o.device)
+    py = _need(y, "y", shape, _dt(d.out_dtype))
+    _lib.check(L.gdn_gated_rmsnorm(ctypes.byref(d.c()), rows, po, pz, pw, norm_eps, py, _stream()),
+               "gdn_gated_rmsnorm")
     return y
 
 

@@ -19,7 +19,7 @@ STATUS = {
     -7: "GDN_ERR_BLOB_VERSION", -8: "GDN_ERR_BLOB_SHAPE", -9: "GDN_ERR_BLOB_SIZE",
     -10: "GDN_ERR_BLOB_CHECKSUM", -11: "GDN_ERR_HIP", -12: "GDN_ERR_TOO_LARGE",
 }
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 ABI_VERSION = 1
 
 EXPORTS = (
@@ -28,7 +28,7 @@ EXPORTS = (
     "gdn_decode_workspace_bytes", "gdn_conv1d", "gdn_prefill_chunked", "gdn_decode_step",
     "gdn_state_save", "gdn_state_restore", "gdn_state_check", "gdn_prefill_chunked_timed",
     "gdn_decode_step_timed", "gdn_decode_step_noalloc", "gdn_decode_multi",
-    "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_bytes",
+    "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_bytes", "gdn_gated_rmsnorm",
 )
 
 
@@ -91,6 +91,8 @@ def load():
     L.gdn_prefill_varlen.restype = ctypes.c_int
     L.gdn_prefill_varlen.argtypes = [dp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz,
                                      vp]
+    L.gdn_gated_rmsnorm.restype = ctypes.c_int
+    L.gdn_gated_rmsnorm.argtypes = [dp, i64, vp, vp, vp, ctypes.c_float, vp, vp]
     L.gdn_decode_step_noalloc.restype = ctypes.c_int
     L.gdn_decode_step_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_state_save.restype = ctypes.c_int

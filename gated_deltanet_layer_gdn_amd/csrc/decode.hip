@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256) void decode_kernel(Geom g, const float *__rest
   const int sin = in_slot(sa, b);
   if (sin < 0) {  // padding row
     if (j == 0)
-      for (int t = 0; t < TT; ++t) store_elem<DTY>(y, ((bt0 + t) * g.H_v + h) * D + i, 0.f);
+      for (int t = 0; t < TT; ++t)
+        store_elem<out_type(DTY)>(y, ((bt0 + t) * g.H_v + h) * D + i, 0.f);
     return;
   }
   const size_t row_off = (static_cast<size_t>(h) * D + i) * D;
@@ -171,7 +172,10 @@ __global__ __launch_bounds__(256) void decode_kernel(Geom g, const float *__rest
     }
     if (j == 0) {
       const size_t yi = gh * D + i;
-      store_elem<DTY>(y, yi, o * sigmoidf_(load_elem<DTZ>(z, yi)));
+      if constexpr (out_gated(DTY))
+        store_elem<out_type(DTY)>(y, yi, o * sigmoidf_(load_elem<DTZ>(z, yi)));
+      else
+        store_elem<out_type(DTY)>(y, yi, o);
     }
   }
 }
@@ -183,13 +187,9 @@ static void launch_decode_t(const Geom &g, const float *qkv, const void *z, cons
   const int64_t rows = static_cast<int64_t>(g.B) * g.H_v * D;
   const dim3 grid(static_cast<unsigned>((rows + DecodeShape<D, NPL>::RPB - 1) /
                                         DecodeShape<D, NPL>::RPB));
-  const int key = (g.in_dt << 1) | g.out_dt;
-  switch (key) {
-    case 0: hipLaunchKernelGGL((decode_kernel<D, NPL, 0, 0, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows); break;
-    case 1: hipLaunchKernelGGL((decode_kernel<D, NPL, 0, 1, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, NPL, 1, 0, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, NPL, 1, 1, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows); break;
-  }
+#define GDN_DEC(ZT, OC) hipLaunchKernelGGL((decode_kernel<D, NPL, ZT, OC, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows)
+  GDN_OUT_DISPATCH(g.in_dt, out_code(g.out_dt, z), GDN_DEC);
+#undef GDN_DEC
 }
 
 template <int TT>

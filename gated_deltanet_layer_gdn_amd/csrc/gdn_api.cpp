@@ -48,7 +48,7 @@ int check_dims(const gdn_dims *d, Geom *g) {
   if (d->d_k != d->d_v || (d->d_k != 16 && d->d_k != 128)) return GDN_ERR_UNSUPPORTED;
   if (d->W != 4) return GDN_ERR_UNSUPPORTED;
   if ((d->in_dtype != GDN_F32 && d->in_dtype != GDN_BF16) ||
-      (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16))
+      (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16 && d->out_dtype != GDN_F16))
     return GDN_ERR_UNSUPPORTED;
   if (!(d->l2_eps >= 0.f) || !(d->l2_eps < 1e30f)) return GDN_ERR_INVALID_ARG;
   if (!(d->q_scale > -1e30f && d->q_scale < 1e30f)) return GDN_ERR_INVALID_ARG;
@@ -73,8 +73,13 @@ int check_dims(const gdn_dims *d, Geom *g) {
 struct Buf {
   const void *p;
   size_t n;
-  size_t align;  // required alignment in bytes
+  size_t align;  // required alignment in bytes; 0: an optional buffer left out
 };
+
+// z may be null (ungated output); then its entry is left out of the checks.
+Buf optional_buf(const void *p, size_t n, size_t align) {
+  return p ? Buf{p, n, align} : Buf{nullptr, 0, 0};
+}
 
 bool overlaps(const Buf &a, const Buf &b) {
   if (!a.n || !b.n) return false;
@@ -87,6 +92,7 @@ bool overlaps(const Buf &a, const Buf &b) {
 int check_buffers(const Buf *in, int n_in, const Buf *out, int n_out) {
   for (int i = 0; i < n_in + n_out; ++i) {
     const Buf &b = i < n_in ? in[i] : out[i - n_in];
+    if (!b.align) continue;
     if (!b.p) return GDN_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(b.p) % b.align) return GDN_ERR_ALIGNMENT;
   }
@@ -322,7 +328,7 @@ static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const vo
   const size_t bt = static_cast<size_t>(g.B) * T;
   // x and the conv history are read in 16-byte pieces by the state pass.
   const Buf in[] = {{x, bt * g.C_ch * es, 16},
-                    {z, bt * g.H_v * g.D * es, 16},
+                    optional_buf(z, bt * g.H_v * g.D * es, 16),
                     {gl, bt * g.H_v * 4, 4},
                     {beta, bt * g.H_v * 4, 4},
                     {conv_w, static_cast<size_t>(g.C_ch) * g.W * es, es}};
@@ -388,7 +394,7 @@ static int decode_run(const gdn_dims *dims, const DecodeArgs &a, const char *whe
   const size_t ns = static_cast<size_t>(a.n_slots);
   const size_t need = decode_ws_bytes(g, a.T);
   Buf in[7] = {{a.x, bt * g.C_ch * es, es},
-               {a.z, bt * g.H_v * g.D * es, es},
+               optional_buf(a.z, bt * g.H_v * g.D * es, es),
                {a.gl, bt * g.H_v * 4, 4},
                {a.beta, bt * g.H_v * 4, 4},
                {a.conv_w, static_cast<size_t>(g.C_ch) * g.W * es, es}};
@@ -535,7 +541,7 @@ int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, int32_t 
   const size_t conv_slot = static_cast<size_t>(g.W - 1) * g.C_ch * es;
   const size_t rec_slot = static_cast<size_t>(g.H_v) * g.D * g.D * 4;
   const Buf in[] = {{x, tt * g.C_ch * es, 16},
-                    {z, tt * g.H_v * g.D * es, 16},
+                    optional_buf(z, tt * g.H_v * g.D * es, 16),
                     {gl, tt * g.H_v * 4, 4},
                     {beta, tt * g.H_v * 4, 4},
                     {conv_w, static_cast<size_t>(g.C_ch) * g.W * es, es}};
@@ -571,6 +577,26 @@ int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, int32_t 
     if (e != hipSuccess) return set_hip_error(e, "gdn_prefill_varlen");
   }
   return GDN_OK;
+}
+
+int gdn_gated_rmsnorm(const gdn_dims *dims, int64_t rows, const float *o, const void *z,
+                      const float *norm_w, float norm_eps, void *y, void *stream) {
+  Geom g;
+  int rc = check_dims(dims, &g);
+  if (rc) return rc;
+  if (rows < 0 || rows > (int64_t(1) << 40) / (static_cast<int64_t>(g.H_v) * g.D))
+    return GDN_ERR_INVALID_ARG;
+  if (!(norm_eps >= 0.f) || !(norm_eps < 1e30f)) return GDN_ERR_INVALID_ARG;
+  const size_t n = static_cast<size_t>(rows) * g.H_v * g.D;
+  const Buf in[] = {{o, n * 4, 16}, optional_buf(z, n * esize(g.in_dt), 16),
+                    optional_buf(norm_w, static_cast<size_t>(g.D) * 4, 16)};
+  const Buf out[] = {{y, n * esize(g.out_dt), 16}};
+  if (rows == 0) return GDN_OK;
+  if ((rc = check_buffers(in, 3, out, 1))) return rc;
+  if (injected_launch_failure()) return GDN_ERR_HIP;
+  const hipError_t e = launch_gated_rmsnorm(g, rows, o, z, norm_w, norm_eps, y,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_gated_rmsnorm");
 }
 
 int gdn_state_check(const gdn_dims *dims, const void *blob, size_t blob_bytes) {

@@ -102,21 +102,37 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) 
   lo = static_cast<uint16_t>(l);
 }
 
-template <int DT>  // 0 = fp32, 1 = bf16
+// float -> fp16 bits, round to nearest even (the hardware convert).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+template <int DT>  // 0 = fp32, 1 = bf16, 2 = fp16 (outputs only)
 __device__ __forceinline__ float load_elem(const void *p, size_t i) {
   if constexpr (DT == 0)
     return static_cast<const float *>(p)[i];
-  else
+  else if constexpr (DT == 1)
     return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+  else
+    return static_cast<float>(static_cast<const _Float16 *>(p)[i]);
 }
 
 template <int DT>
 __device__ __forceinline__ void store_elem(void *p, size_t i, float v) {
   if constexpr (DT == 0)
     static_cast<float *>(p)[i] = v;
-  else
+  else if constexpr (DT == 1)
     static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(v);
+  else
+    static_cast<uint16_t *>(p)[i] = f32_to_f16_bits(v);
 }
+
+// Output codes of the kernels' DTY template parameter: the low two bits are
+// the element type of y (0 fp32, 1 bf16, 2 fp16); bit 2 set means no gate
+// (y = o, the readout before the sigmoid gate; z is not read).
+__host__ __device__ constexpr int out_type(int code) { return code & 3; }
+__host__ __device__ constexpr bool out_gated(int code) { return (code & 4) == 0; }
+__host__ __device__ constexpr int out_bytes(int code) { return (code & 3) == 0 ? 4 : 2; }
 
 // e^{-x} as the hardware base-2 exponential of -x log2(e): one v_exp_f32
 // without the library's denormal range handling.  A result that underflows

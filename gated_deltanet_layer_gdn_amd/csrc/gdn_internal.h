@@ -9,11 +9,41 @@
 
 namespace gdn {
 
+// Output code of the kernels' DTY template parameter (see gdn_device.h):
+// y's element type, plus 4 when z is null (no gate, y = o).
+inline int out_code(int out_dt, const void *z) { return out_dt | (z ? 0 : 4); }
+
+// LAUNCH(ZT, OC) with the input element type ZT (0 fp32, 1 bf16) and the
+// output code OC as compile-time constants.
+#define GDN_OUT_DISPATCH(IN_DT, OC, LAUNCH)                                       \
+  do {                                                                            \
+    const int oc_ = (OC);                                                         \
+    if ((IN_DT) == 0) {                                                           \
+      switch (oc_) {                                                              \
+        case 0: LAUNCH(0, 0); break;                                              \
+        case 1: LAUNCH(0, 1); break;                                              \
+        case 2: LAUNCH(0, 2); break;                                              \
+        case 4: LAUNCH(0, 4); break;                                              \
+        case 5: LAUNCH(0, 5); break;                                              \
+        default: LAUNCH(0, 6); break;                                             \
+      }                                                                           \
+    } else {                                                                      \
+      switch (oc_) {                                                              \
+        case 0: LAUNCH(1, 0); break;                                              \
+        case 1: LAUNCH(1, 1); break;                                              \
+        case 2: LAUNCH(1, 2); break;                                              \
+        case 4: LAUNCH(1, 4); break;                                              \
+        case 5: LAUNCH(1, 5); break;                                              \
+        default: LAUNCH(1, 6); break;                                             \
+      }                                                                           \
+    }                                                                             \
+  } while (0)
+
 // Everything a kernel needs to know about the geometry, as plain values.
 struct Geom {
   int B, H_k, H_v, D, W, G;  // D = d_k = d_v, G = H_v / H_k
   int C_ch;                  // 2*H_k*D + H_v*D
-  int in_dt, out_dt;         // 0 = fp32, 1 = bf16
+  int in_dt, out_dt;         // 0 = fp32, 1 = bf16 (, 2 = fp16 for out_dt)
   float eps, q_scale;
 };
 
@@ -81,6 +111,10 @@ hipError_t launch_conv_step(const Geom &g, int T, const void *x, const void *w, 
 hipError_t launch_decode(const Geom &g, int T, const float *qkv, const void *z, const float *gl,
                          const float *beta, float *S, void *y, int n_slots,
                          const int32_t *in_slots, const int32_t *out_slots, hipStream_t s);
+// Zero-centred grouped RMS norm + sigmoid gate over rows * H_v groups of D
+// values (z may be null: no gate; w may be null: unit scale).
+hipError_t launch_gated_rmsnorm(const Geom &g, int64_t rows, const float *o, const void *z,
+                                const float *w, float eps, void *y, hipStream_t s);
 // Also rolls the conv history (x, hist) after the sequence.
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
                                const float *beta, char *ws, const void *x, void *hist,

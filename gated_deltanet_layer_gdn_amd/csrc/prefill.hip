@@ -253,13 +253,15 @@ struct StateKernel {
       // z of this tile: 16 token rows of ROWS elements, one 16-byte piece per
       // lane; rows past the sequence end re-read its last row (their outputs
       // are not stored).
+      if constexpr (out_gated(DTY)) {
 #pragma unroll
-      for (int k = 0; k < ZK; ++k) {
-        int idx = x.lane + 64 * k;
-        idx = idx < 16 * ZL ? idx : 16 * ZL - 1;
-        int t = 16 * m + idx / ZL;
-        t = t < n_valid ? t : n_valid - 1;
-        o.z[i][k] = ldb<uint4>(zb, t * tstride + (idx % ZL) * 16);
+        for (int k = 0; k < ZK; ++k) {
+          int idx = x.lane + 64 * k;
+          idx = idx < 16 * ZL ? idx : 16 * ZL - 1;
+          int t = 16 * m + idx / ZL;
+          t = t < n_valid ? t : n_valid - 1;
+          o.z[i][k] = ldb<uint4>(zb, t * tstride + (idx % ZL) * 16);
+        }
       }
     }
   }
@@ -384,9 +386,11 @@ struct StateKernel {
     for (int i = 0; i < MW; ++i) {
       const int m = wave + i * NWV;
       if (m < NT) {
+        if constexpr (out_gated(DTY)) {
 #pragma unroll
-        for (int k = 0; k < ZK; ++k)
-          if (lane + 64 * k < 16 * ZL) sm.z[wave][lane + 64 * k] = o.z[i][k];
+          for (int k = 0; k < ZK; ++k)
+            if (lane + 64 * k < 16 * ZL) sm.z[wave][lane + 64 * k] = o.z[i][k];
+        }
         // Other lanes of this wave read what was just written: keep the
         // compiler from moving those reads above the stores (LDS operations of
         // one wave execute in order).
@@ -406,13 +410,17 @@ struct StateKernel {
             }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int off = ((4 * gq + r) * ROWS + 16 * n + c) * EZ;
-            float zz;
-            if constexpr (DTZ == 0)
-              zz = *reinterpret_cast<const float *>(zt + off);
-            else
-              zz = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(zt + off));
-            out[i][n][r] = acc[r] * sigmoidf_(zz);
+            if constexpr (out_gated(DTY)) {
+              const int off = ((4 * gq + r) * ROWS + 16 * n + c) * EZ;
+              float zz;
+              if constexpr (DTZ == 0)
+                zz = *reinterpret_cast<const float *>(zt + off);
+              else
+                zz = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(zt + off));
+              out[i][n][r] = acc[r] * sigmoidf_(zz);
+            } else {
+              out[i][n][r] = acc[r];
+            }
           }
         }
         asm volatile("" ::: "memory");
@@ -447,7 +455,7 @@ struct StateKernel {
     load_gates(x, next, o);
 
     // 6. Gated outputs of the owned tiles.
-    constexpr int ey = DTY == 0 ? 4 : 2;
+    constexpr int ey = out_bytes(DTY);
     char *yb = static_cast<char *>(x.y) + static_cast<size_t>(chunk) * C * x.H_v * D * ey;
     const uint32_t tstride = x.H_v * D * ey;
 #pragma unroll
@@ -461,10 +469,12 @@ struct StateKernel {
             const int t = 16 * m + 4 * gq + r;
             if (t < n_valid) {
               char *dst = yb + (x.o_zy + 16 * n) * ey + (16 * m + r) * tstride;
-              if constexpr (DTY == 0)
+              if constexpr (out_type(DTY) == 0)
                 *reinterpret_cast<float *>(dst) = out[i][n][r];
-              else
+              else if constexpr (out_type(DTY) == 1)
                 *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16_bits(out[i][n][r]);
+              else
+                *reinterpret_cast<uint16_t *>(dst) = f32_to_f16_bits(out[i][n][r]);
             }
           }
       }
@@ -510,7 +520,7 @@ __global__ __launch_bounds__((StateShape<D, C>::NWV * 64)) void state_kernel(
             (static_cast<size_t>(b) * g.H_v + h) * L.NC * 3 * C;
   const size_t zy = (static_cast<size_t>(b) * L.T * g.H_v + h) * D + ROWS * rb;
   x.z = static_cast<const char *>(z) + zy * K::EZ;
-  x.y = static_cast<char *>(y) + zy * (DTY == 0 ? 4 : 2);
+  x.y = static_cast<char *>(y) + zy * out_bytes(DTY);
   x.T = L.T;
   x.H_v = g.H_v;
   x.NC = L.NC;
@@ -869,6 +879,7 @@ struct StateKernelWS {
 
 
   static __device__ __forceinline__ void load_z(const Ctx &x, int chunk, OutOps &o) {
+    if constexpr (!out_gated(DTY)) return;  // no gate: z is not read
     const int n_valid = valid_of(x, chunk);
     const char *zb = static_cast<const char *>(x.z) + static_cast<size_t>(chunk) * C * x.H_v * D * EZ;
     const uint32_t tstride = x.H_v * D * EZ;
@@ -1060,7 +1071,7 @@ struct StateKernelWS {
     load_gam(x, 0, o);
     asm volatile("" ::: "memory");
     __syncthreads();
-    constexpr int ey = DTY == 0 ? 4 : 2;
+    constexpr int ey = out_bytes(DTY);
     const uint32_t ystride = x.H_v * D * ey;
 
     // One chunk; `last` (a compile-time flag) marks the final chunk, the only
@@ -1094,7 +1105,10 @@ struct StateKernelWS {
       //    turns it into D-register order.  Only this wave touches the slot,
       //    and LDS keeps one wave's accesses in order.
       float sg[NB][4];
-      {
+      if constexpr (!out_gated(DTY)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sg[0][r] = sg[1][r] = 1.0f;
+      } else {
 #pragma unroll
         for (int k = 0; k < ZK; ++k)
           if (lane + 64 * k < 16 * ZL) sm.z[m][lane + 64 * k] = o.z[k];
@@ -1161,13 +1175,17 @@ struct StateKernelWS {
         const int t = 16 * m + 4 * gq + r;
         if (!kLast || t < n_valid) {
           const uint32_t so = r * ystride;
-          if constexpr (DTY == 0) {
+          if constexpr (out_type(DTY) == 0) {
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             const u32x2 v = {__float_as_uint(out[0][r]), __float_as_uint(out[1][r])};
             __builtin_amdgcn_raw_buffer_store_b64(v, ry, yoff, so, kYNt);
-          } else {
+          } else if constexpr (out_type(DTY) == 1) {
             const uint32_t v = static_cast<uint32_t>(f32_to_bf16_bits(out[0][r])) |
                                (static_cast<uint32_t>(f32_to_bf16_bits(out[1][r])) << 16);
+            __builtin_amdgcn_raw_buffer_store_b32(v, ry, yoff, so, kYNt);
+          } else {
+            const uint32_t v = static_cast<uint32_t>(f32_to_f16_bits(out[0][r])) |
+                               (static_cast<uint32_t>(f32_to_f16_bits(out[1][r])) << 16);
             __builtin_amdgcn_raw_buffer_store_b32(v, ry, yoff, so, kYNt);
           }
         }
@@ -1242,7 +1260,7 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
   x.gates = reinterpret_cast<const float *>(ws + L.gates) + (static_cast<size_t>(b) * g.H_v + h) * L.NC * 4 * C;
   const size_t zy = (static_cast<size_t>(b) * L.T * g.H_v + h) * D + ROWS * rb;
   x.z = static_cast<const char *>(z) + zy * K::EZ;
-  x.y = static_cast<char *>(y) + zy * (DTY == 0 ? 4 : 2);
+  x.y = static_cast<char *>(y) + zy * out_bytes(DTY);
   x.T = L.T;
   x.H_v = g.H_v;
   x.NC = L.NC;
@@ -1270,13 +1288,9 @@ static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, flo
   if constexpr (D == 128 && C == 64) {
     dim3 grid(g.B * g.H_v * (D / StateKernelWS<0, 0>::ROWS));
     dim3 block(StateKernelWS<0, 0>::kThreads);
-    const int key = (g.in_dt << 1) | g.out_dt;
-    switch (key) {
-      case 0: hipLaunchKernelGGL((state_kernel_ws<0, 0>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist); break;
-      case 1: hipLaunchKernelGGL((state_kernel_ws<0, 1>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist); break;
-      case 2: hipLaunchKernelGGL((state_kernel_ws<1, 0>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist); break;
-      default: hipLaunchKernelGGL((state_kernel_ws<1, 1>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist); break;
-    }
+#define GDN_WS(ZT, OC) hipLaunchKernelGGL((state_kernel_ws<ZT, OC>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist)
+    GDN_OUT_DISPATCH(g.in_dt, out_code(g.out_dt, z), GDN_WS);
+#undef GDN_WS
     return;
   }
   (void)x;
@@ -1284,13 +1298,9 @@ static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, flo
   (void)hist;
   dim3 grid(g.B * g.H_v * (D / StateShape<D, C>::ROWS));
   dim3 block(StateShape<D, C>::NWV * 64);
-  const int key = (g.in_dt << 1) | g.out_dt;
-  switch (key) {
-    case 0: hipLaunchKernelGGL((state_kernel<D, C, 0, 0>), grid, block, 0, s, g, L, z, S, y, ws); break;
-    case 1: hipLaunchKernelGGL((state_kernel<D, C, 0, 1>), grid, block, 0, s, g, L, z, S, y, ws); break;
-    case 2: hipLaunchKernelGGL((state_kernel<D, C, 1, 0>), grid, block, 0, s, g, L, z, S, y, ws); break;
-    default: hipLaunchKernelGGL((state_kernel<D, C, 1, 1>), grid, block, 0, s, g, L, z, S, y, ws); break;
-  }
+#define GDN_ST(ZT, OC) hipLaunchKernelGGL((state_kernel<D, C, ZT, OC>), grid, block, 0, s, g, L, z, S, y, ws)
+  GDN_OUT_DISPATCH(g.in_dt, out_code(g.out_dt, z), GDN_ST);
+#undef GDN_ST
 }
 
 hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z, float *S,

@@ -45,6 +45,9 @@
  *    copy has completed.
  *  - conv_state and rec_state are updated in place.  Outputs and workspace
  *    must not overlap any input or state buffer.
+ *  - z may be NULL in every layer call: y is then the ungated readout
+ *    o_t = S_t q_t (for a caller that applies its own epilogue, such as
+ *    gdn_gated_rmsnorm below).
  *  - Every argument is validated before anything is enqueued; on any error
  *    no caller byte has changed (fail before partial execution: issue #95,
  *    implementation comment).  Values are not checked on the device: inputs
@@ -85,13 +88,15 @@ extern "C" {
 #define GDN_ERR_HIP (-11)          /* HIP runtime error; see gdn_last_hip_error */
 #define GDN_ERR_TOO_LARGE (-12)    /* beyond the fixed scratch of gdn_decode_step_noalloc */
 
-/* Element types. */
+/* Element types.  GDN_F16 is an output type only (y). */
 #define GDN_F32 0
 #define GDN_BF16 1
+#define GDN_F16 2
 
 /* Geometry and numeric options, passed by pointer to every call.
  * Built geometries: d_k = d_v in {16, 128}, W = 4, H_v a multiple of H_k,
- * in_dtype and out_dtype in {GDN_F32, GDN_BF16}, l2_eps >= 0. */
+ * in_dtype in {GDN_F32, GDN_BF16}, out_dtype in {GDN_F32, GDN_BF16, GDN_F16},
+ * l2_eps >= 0. */
 typedef struct gdn_dims {
   int32_t abi;       /* must be GDN_ABI_VERSION                     */
   int32_t B;         /* sequences                                    */
@@ -99,7 +104,7 @@ typedef struct gdn_dims {
   int32_t d_k, d_v;  /* head dimensions                              */
   int32_t W;         /* conv taps                                    */
   int32_t in_dtype;  /* x, z, conv_w, conv_state                     */
-  int32_t out_dtype; /* y                                            */
+  int32_t out_dtype; /* y (GDN_F16 allowed)                          */
   float l2_eps;      /* epsilon inside the root of the L2 norm       */
   float q_scale;     /* extra factor on normalised q                 */
 } gdn_dims;
@@ -214,6 +219,21 @@ GDN_API int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, 
                                const void *conv_w, void *conv_pool, float *rec_pool,
                                int32_t n_slots, const int32_t *slots, void *y, void *ws,
                                size_t ws_bytes, void *stream);
+
+/* Zero-centred grouped RMS norm before the sigmoid output gate ("Implement
+ * the Qwen3.8 Flash Next Rust and Metal text core", section Implementation:
+ * zero-centred norms; its implementation comment: zero-centred grouped RMS
+ * and the sigmoid output gate), over the ungated readout of a layer call
+ * (made with z = NULL and out_dtype GDN_F32).  For each of the rows * H_v
+ * groups (one value head of one token, d_v values):
+ *   y = o / sqrt(mean(o^2) + norm_eps) * (1 + norm_w) * sigmoid(z)
+ *   o [rows][H_v][d_v] fp32; z [rows][H_v][d_v] in_dtype, or NULL (no gate);
+ *   norm_w [d_v] fp32, the zero-centred weight shared by the heads, or NULL
+ *   (all zero); y [rows][H_v][d_v] out_dtype; norm_eps >= 0.
+ * o, z, norm_w and y 16-byte aligned; y must not overlap the inputs.
+ * rows = B * T of the layer call (0: nothing to do). */
+GDN_API int gdn_gated_rmsnorm(const gdn_dims *dims, int64_t rows, const float *o, const void *z,
+                              const float *norm_w, float norm_eps, void *y, void *stream);
 
 /* gdn_decode_step without a workspace argument and without any allocation,
  * for callers that cannot allocate device memory: code under HIP graph

@@ -55,8 +55,9 @@ def _lib():
         L.oracle_recurrence.argtypes = [i32, i64, i32, i32, i32, i32] + [vp] * 9
         L.oracle_layer.argtypes = ([i32, i64, i32, i32, i32, i32, i32, i32, dp, dp]
                                    + [vp] * 8 + [vp, i32, i32])
+        L.oracle_gated_rmsnorm.argtypes = [i64, i32, vp, vp, vp, dp, vp]
         for f in (L.oracle_conv_silu, L.oracle_conv_history_next, L.oracle_l2norm,
-                  L.oracle_recurrence, L.oracle_layer):
+                  L.oracle_recurrence, L.oracle_layer, L.oracle_gated_rmsnorm):
             f.restype = i32
         _LIB = L
     return _LIB
@@ -146,18 +147,21 @@ def layer(x, z, g, beta, w, hist, S0, *, H_k: int, H_v: int, d_k: int, d_v: int,
     """Whole GDN layer from raw inputs.
 
     Returns (y float64 [B,T,H_v,d_v], S float64 [B,H_v,d_v,d_k], hist_next).
+    ``z=None`` gives the ungated readout y = o = S_t q_t.
     ``heads``: optional iterable of (b, h) pairs; only those are computed (other
     entries of y are NaN and other state heads keep S0).
     """
-    x, z, w, hist = _c(x), _c(z), _c(w), _c(hist)
+    x, w, hist = _c(x), _c(w), _c(hist)
+    z = None if z is None else _c(z)
     g, beta = _c(g, np.float32), _c(beta, np.float32)
     dt = _dtype_code(x)
-    for a in (z, w, hist):
+    for a in (w, hist) if z is None else (z, w, hist):
         assert _dtype_code(a) == dt
     B, T, C = x.shape
     W = w.shape[1]
     assert C == 2 * H_k * d_k + H_v * d_v, (C, H_k, d_k, H_v, d_v)
-    assert z.shape == (B, T, H_v, d_v) and g.shape == (B, T, H_v) == beta.shape
+    assert z is None or z.shape == (B, T, H_v, d_v)
+    assert g.shape == (B, T, H_v) == beta.shape
     assert hist.shape == (B, W - 1, C)
     S = _c(S0, np.float64).copy()
     assert S.shape == (B, H_v, d_v, d_k)
@@ -173,6 +177,22 @@ def layer(x, z, g, beta, w, hist, S0, *, H_k: int, H_v: int, d_k: int, d_v: int,
                              _ptr(tasks), n, nth)
     assert rc == 0, rc
     return y, S, conv_history_next(x, hist)
+
+
+def gated_rmsnorm(o, z, w, eps: float):
+    """Zero-centred grouped RMS norm over the last axis, then the sigmoid gate:
+    o / sqrt(mean(o^2) + eps) * (1 + w) * sigmoid(z) (float64).  z may be None
+    (no gate), w may be None (all zero)."""
+    o = _c(o, np.float64)
+    d = o.shape[-1]
+    zz = None if z is None else _c(z, np.float64)
+    ww = None if w is None else _c(w, np.float64)
+    assert zz is None or zz.shape == o.shape
+    assert ww is None or ww.shape == (d,)
+    y = np.empty_like(o)
+    rc = _lib().oracle_gated_rmsnorm(o.size // d, d, _ptr(o), _ptr(zz), _ptr(ww), eps, _ptr(y))
+    assert rc == 0, rc
+    return y
 
 
 # ---------------------------------------------------------------------------

@@ -234,7 +234,8 @@ static void layer_task(layer_job *J, int b, int h) {
     double a = exp((double)J->g[bth]);
     delta_step(d_v, d_k, Sh, k, v, q, a, (double)J->beta[bth], p, o);
     for (int i = 0; i < d_v; ++i)
-      J->y[bth * d_v + i] = o[i] * sigmoid(widen(J->z, bth * d_v + i, J->dtype));
+      J->y[bth * d_v + i] =
+          J->z ? o[i] * sigmoid(widen(J->z, bth * d_v + i, J->dtype)) : o[i];
   }
   free(buf);
 }
@@ -252,7 +253,9 @@ static void *layer_worker(void *arg) {
 }
 
 /* Full layer.
- *   x: [B,T,C_ch] dtype; z: [B,T,H_v,d_v] dtype; g, beta: [B,T,H_v] fp32;
+ *   x: [B,T,C_ch] dtype; z: [B,T,H_v,d_v] dtype, or NULL for the ungated
+ *   readout y = o = S_t q_t (the recurrence's output before the sigmoid
+ *   gate); g, beta: [B,T,H_v] fp32;
  *   w: [C_ch,W] dtype; hist: [B,W-1,C_ch] dtype, read only (use
  *   oracle_conv_history_next for the updated history);
  *   S: [B,H_v,d_v,d_k] double in/out; y: [B,T,H_v,d_v] double out.
@@ -298,4 +301,28 @@ int oracle_layer(int B, int64_t T, int H_k, int H_v, int d_k, int d_v, int W,
   pthread_mutex_destroy(&J.mu);
   free(all);
   return J.failed ? -2 : 0;
+}
+
+/* Zero-centred grouped RMS norm, then the sigmoid output gate ("Implement the
+ * Qwen3.8 Flash Next Rust and Metal text core", section Implementation:
+ * zero-centred norms; its implementation comment: zero-centred grouped RMS
+ * and the sigmoid output gate).  Reading taken: a group is the d values of
+ * one value head of one token; each is divided by the square root of the
+ * group's mean square plus eps and multiplied by (1 + w[i]) (a zero-centred
+ * weight: w = 0 is the identity scale), then by sigmoid(z[i]) when z is
+ * given.  groups x d values in o, z and y; w has d entries (NULL: all 0). */
+int oracle_gated_rmsnorm(int64_t groups, int d, const double *o, const double *z,
+                         const double *w, double eps, double *y) {
+  if (groups < 0 || d <= 0 || eps < 0) return -1;
+  for (int64_t gi = 0; gi < groups; ++gi) {
+    const double *og = o + gi * d;
+    double ss = 0.0;
+    for (int i = 0; i < d; ++i) ss += og[i] * og[i];
+    double inv = 1.0 / sqrt(ss / d + eps);
+    for (int i = 0; i < d; ++i) {
+      double v = og[i] * inv * (1.0 + (w ? w[i] : 0.0));
+      y[gi * d + i] = z ? v * sigmoid(z[gi * d + i]) : v;
+    }
+  }
+  return 0;
 }
