@@ -140,8 +140,13 @@ GDN_API size_t gdn_decode_workspace_bytes(const gdn_dims *dims);
 GDN_API int gdn_conv1d(const gdn_dims *dims, int64_t T, const void *x, const void *conv_w,
                void *conv_state, float *qkv_out, void *stream);
 
-/* The whole layer over 1 <= T <= 2^24 tokens per sequence, processed in chunks of
- * `chunk` in {16, 32, 64, 128} tokens (the last chunk may be partial).
+/* The whole layer over 1 <= T <= 2^24 tokens per sequence, processed in
+ * chunks of `chunk` in {16, 32, 64, 128} tokens (the last chunk may be
+ * partial): the separately tuned GDN prefill behind the one semantic
+ * interface ("Add a performance-parity Qwen3.8-27B Q4 and Q8 text backend on
+ * Metal", section Scope), equal to token-by-token decode across chunk sizes
+ * ("Implement the Qwen3.8 Flash Next Rust and Metal text core", section
+ * Verification).
  * conv_state and rec_state carry the sequence in and out, so calls can be
  * chained: splitting a sequence at a multiple of `chunk` gives bit-identical
  * outputs and states.  `ws` is device workspace of at least
