@@ -143,8 +143,8 @@ def main():
     ap.add_argument("--decode-rounds", type=int, default=5,
                     help="graph replays per decode timing (each replays R rotated steps)")
     ap.add_argument("--legs", default="all",
-                    help="comma list of: long64, long128, t4096, decode_b1, decode_b64, cpu "
-                         "(default all); the headline leg always runs")
+                    help="comma list of: long64, long128, t4096, decode_b1, decode_b64, in_proj, "
+                         "cpu (default all); the headline leg always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run --steps plain device copies of MIB MiB (for scaling the HBM "
@@ -180,7 +180,7 @@ def main():
         return
 
     legs = set(args.legs.split(",")) if args.legs != "all" else {
-        "long64", "long128", "t4096", "decode_b1", "decode_b64", "cpu"}
+        "long64", "long128", "t4096", "decode_b1", "decode_b64", "in_proj", "cpu"}
     if args.no_cpu_baseline:
         legs.discard("cpu")
     head_leg = "long64" if args.chunk == 64 else "long128"
@@ -406,6 +406,56 @@ def main():
             f"eager; state kernel {k_state * 1e3:.2f} us = {ach:.0f} GB/s")
         del Ss, Hs, Dd
 
+    # ------------------------------------------------------------ input projections
+    proj = None
+    if "in_proj" in legs:
+        # The GDN input projections (one fused bf16 GEMM, hidden 5120 -> C_ch +
+        # H_v d_v + 2 H_v = 16,480 outputs, with the decay/beta epilogue) over
+        # the T=4096 prefill's tokens.  A torch bf16 matmul of the same shape
+        # is timed beside it as the attainable-GEMM reference of this GPU.
+        from gdn_inputs import make_proj_inputs
+        Tp, hidden = 4096, 5120
+        dp = gdn.Dims(B=1, H_k=16, H_v=48, d_k=128, d_v=128)
+        P = make_proj_inputs(1, Tp, hidden, 16, 48, 128, seed=5)
+        hP, wP = dev(P["h"]), dev(P["w_in"])
+        AP, dP = dev(P["A_log"]), dev(P["dt_bias"])
+        outs = gdn.in_proj(dp, hP, wP, AP, dP)
+        for _ in range(args.warmup):
+            gdn.in_proj(dp, hP, wP, AP, dP, *outs)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            gdn.in_proj(dp, hP, wP, AP, dP, *outs)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_p = e0.elapsed_time(e1) / args.steps
+        Np = dp.C_ch + dp.H_v * dp.d_v + 2 * dp.H_v
+        Fp = 2.0 * Tp * Np * hidden
+        h2 = hP.reshape(Tp, hidden)
+        for _ in range(3):
+            r_ = h2 @ wP.t()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            r_ = h2 @ wP.t()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_t = e0.elapsed_time(e1) / args.steps
+        del r_
+        proj = {"workload": f"input projections, {Tp} tokens, hidden {hidden} -> {Np} outputs "
+                            f"(x, z, beta, log decay), bf16 in/out, fp32 accumulation",
+                "us_per_call": round(ms_p * 1e3, 1),
+                "roofline": {"bound": "mfma", "achieved": round(Fp / ms_p / 1e9, 1),
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(Fp / ms_p / 1e9 / PEAK_BF16_TFLOPS, 4),
+                             "alg_flops_per_call": int(Fp)},
+                "attainable_gemm_TFLOPs": round(Fp / ms_t / 1e9, 1)}
+        log(f"[bench] in_proj: {ms_p * 1e3:.1f} us = {Fp / ms_p / 1e9:.0f} TFLOP/s; torch matmul of "
+            f"the same shape {Fp / ms_t / 1e9:.0f} TFLOP/s")
+        del hP, wP, outs
+
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if "cpu" in legs:
@@ -457,6 +507,7 @@ def main():
         "step_fractions": H["step_fractions"],
         "prefill": out_legs,
         "decode": decode,
+        "in_proj": proj,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -22,7 +22,7 @@ from ._lib import BF16, F16, F32, GdnError
 
 __all__ = [
     "Dims", "GdnError", "conv1d", "prefill_chunked", "decode_step", "decode_step_noalloc",
-    "decode_multi", "prefill_varlen", "prefill_varlen_workspace_bytes", "gated_rmsnorm",
+    "decode_multi", "prefill_varlen", "prefill_varlen_workspace_bytes", "gated_rmsnorm", "in_proj",
     "state_save",
     "state_restore", "state_check", "prefill_workspace_bytes", "decode_workspace_bytes",
     "rec_state_bytes", "conv_state_bytes", "state_blob_bytes", "F32", "BF16", "F16",
@@ -283,6 +283,31 @@ def prefill_varlen(d: Dims, cu_seqlens, x, z, g, beta, conv_w, conv_pool, rec_po
                               _stream())
     _lib.check(rc, "gdn_prefill_varlen")
     return y
+
+
+def in_proj(d: Dims, h, w_in, A_log, dt_bias, x=None, z=None, g=None, beta=None):
+    """Input projections: h [B,T,hidden] bf16, w_in [C_ch + H_v*d_v + 2*H_v,
+    hidden] bf16, A_log/dt_bias fp32 [H_v].  Returns (x [B,T,C_ch] bf16,
+    z [B,T,H_v,d_v] bf16, g [B,T,H_v] fp32, beta [B,T,H_v] fp32)."""
+    torch = _torch()
+    L = _lib.load()
+    B, T, hidden = h.shape
+    N = d.C_ch + d.H_v * d.d_v + 2 * d.H_v
+    dev = h.device
+    x = torch.empty((d.B, T, d.C_ch), dtype=torch.bfloat16, device=dev) if x is None else x
+    z = torch.empty((d.B, T, d.H_v, d.d_v), dtype=torch.bfloat16, device=dev) if z is None else z
+    g = torch.empty((d.B, T, d.H_v), dtype=torch.float32, device=dev) if g is None else g
+    beta = torch.empty((d.B, T, d.H_v), dtype=torch.float32, device=dev) if beta is None else beta
+    args = [_need(h, "h", (d.B, T, hidden), torch.bfloat16),
+            _need(w_in, "w_in", (N, hidden), torch.bfloat16),
+            _need(A_log, "A_log", (d.H_v,), torch.float32),
+            _need(dt_bias, "dt_bias", (d.H_v,), torch.float32),
+            _need(x, "x", (d.B, T, d.C_ch), torch.bfloat16),
+            _need(z, "z", (d.B, T, d.H_v, d.d_v), torch.bfloat16),
+            _need(g, "g", (d.B, T, d.H_v), torch.float32),
+            _need(beta, "beta", (d.B, T, d.H_v), torch.float32)]
+    _lib.check(L.gdn_in_proj(ctypes.byref(d.c()), T, hidden, *args, _stream()), "gdn_in_proj")
+    return x, z, g, beta
 
 
 def gated_rmsnorm(d: Dims, o, z, norm_w=None, norm_eps: float = 1e-6, y=None):

@@ -29,6 +29,7 @@ EXPORTS = (
     "gdn_state_save", "gdn_state_restore", "gdn_state_check", "gdn_prefill_chunked_timed",
     "gdn_decode_step_timed", "gdn_decode_step_noalloc", "gdn_decode_multi",
     "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_bytes", "gdn_gated_rmsnorm",
+    "gdn_in_proj",
 )
 
 
@@ -91,6 +92,8 @@ def load():
     L.gdn_prefill_varlen.restype = ctypes.c_int
     L.gdn_prefill_varlen.argtypes = [dp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz,
                                      vp]
+    L.gdn_in_proj.restype = ctypes.c_int
+    L.gdn_in_proj.argtypes = [dp, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_gated_rmsnorm.restype = ctypes.c_int
     L.gdn_gated_rmsnorm.argtypes = [dp, i64, vp, vp, vp, ctypes.c_float, vp, vp]
     L.gdn_decode_step_noalloc.restype = ctypes.c_int

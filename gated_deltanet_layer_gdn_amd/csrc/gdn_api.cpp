@@ -599,6 +599,32 @@ int gdn_gated_rmsnorm(const gdn_dims *dims, int64_t rows, const float *o, const 
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_gated_rmsnorm");
 }
 
+int gdn_in_proj(const gdn_dims *dims, int64_t T, int32_t hidden, const void *h,
+                const void *w_in, const float *A_log, const float *dt_bias, void *x, void *z,
+                float *gl, float *beta, void *stream) {
+  Geom g;
+  int rc = check_dims(dims, &g);
+  if (rc) return rc;
+  if (g.in_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;  // bf16 activations and weights
+  if (T < 1 || T > kMaxTokens) return GDN_ERR_INVALID_ARG;
+  if (hidden < 64 || hidden % 64 || hidden > (1 << 20)) return GDN_ERR_UNSUPPORTED;
+  const size_t M = static_cast<size_t>(g.B) * T;
+  const size_t N = static_cast<size_t>(g.C_ch) + g.H_v * g.D + 2 * g.H_v;
+  const Buf in[] = {{h, M * hidden * 2, 16},
+                    {w_in, N * hidden * 2, 16},
+                    {A_log, static_cast<size_t>(g.H_v) * 4, 4},
+                    {dt_bias, static_cast<size_t>(g.H_v) * 4, 4}};
+  const Buf out[] = {{x, M * g.C_ch * 2, 2},
+                     {z, M * g.H_v * g.D * 2, 2},
+                     {gl, M * g.H_v * 4, 4},
+                     {beta, M * g.H_v * 4, 4}};
+  if ((rc = check_buffers(in, 4, out, 4))) return rc;
+  if (injected_launch_failure()) return GDN_ERR_HIP;
+  const hipError_t e = launch_in_proj(g, static_cast<int64_t>(M), hidden, h, w_in, A_log, dt_bias,
+                                      x, z, gl, beta, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_in_proj");
+}
+
 int gdn_state_check(const gdn_dims *dims, const void *blob, size_t blob_bytes) {
   Geom g;
   int rc = check_dims(dims, &g);

@@ -111,6 +111,12 @@ hipError_t launch_conv_step(const Geom &g, int T, const void *x, const void *w, 
 hipError_t launch_decode(const Geom &g, int T, const float *qkv, const void *z, const float *gl,
                          const float *beta, float *S, void *y, int n_slots,
                          const int32_t *in_slots, const int32_t *out_slots, hipStream_t s);
+// Input projections: Y = H W^T over M rows of `hidden` bf16 values, W
+// [C_ch + H_v D + 2 H_v][hidden] bf16; x, z in bf16, beta and the log decay
+// g in fp32 (see proj.hip).
+hipError_t launch_in_proj(const Geom &g, int64_t M, int hidden, const void *h, const void *w,
+                          const float *A_log, const float *dt_bias, void *x, void *z, float *gl,
+                          float *beta, hipStream_t s);
 // Zero-centred grouped RMS norm + sigmoid gate over rows * H_v groups of D
 // values (z may be null: no gate; w may be null: unit scale).
 hipError_t launch_gated_rmsnorm(const Geom &g, int64_t rows, const float *o, const void *z,

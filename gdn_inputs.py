@@ -138,3 +138,19 @@ def workload_inputs(index: int, **overrides) -> tuple[Workload, dict]:
     wl = WORKLOADS[index]
     geom = replace(wl.geom, **overrides) if overrides else wl.geom
     return replace(wl, geom=geom), make_inputs(geom, seed=index)
+
+
+def make_proj_inputs(B: int, T: int, hidden: int, H_k: int, H_v: int, d: int, seed: int) -> dict:
+    """Inputs of the input projections: hidden states h ~ N(0, 1) and the fused
+    weight w_in ~ N(0, 1/hidden) (so the products are about N(0, 1)), both bf16;
+    per value head A_log ~ U(0, 2.77) and dt_bias ~ U(-6.9, -2.25), fp32 (the
+    usual initialisation ranges of this kind of gate: exp(A_log) in [1, 16],
+    a decay step of 0.001 to 0.1 at zero input)."""
+    rng = np.random.default_rng(seed)
+    C_ch = 2 * H_k * d + H_v * d
+    N = C_ch + H_v * d + 2 * H_v
+    h = _normal_cast(rng, (B, T, hidden), 1.0, "bf16")
+    w_in = _normal_cast(rng, (N, hidden), hidden ** -0.5, "bf16")
+    A_log = rng.uniform(0.0, 2.77, H_v).astype(np.float32)
+    dt_bias = rng.uniform(-6.9, -2.25, H_v).astype(np.float32)
+    return dict(h=h, w_in=w_in, A_log=A_log, dt_bias=dt_bias)

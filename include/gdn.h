@@ -225,6 +225,28 @@ GDN_API int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, 
                                int32_t n_slots, const int32_t *slots, void *y, void *ws,
                                size_t ws_bytes, void *stream);
 
+/* The GDN input projections, with the decay and beta parametrisation fused
+ * into their epilogue ("Implement the Qwen3.8 Flash Next Rust and Metal text
+ * core", section Verification: primitive vectors for the GDN projection).
+ * One bf16 GEMM on the MFMA with fp32 accumulation over M = B * T token rows:
+ *   h     [B][T][hidden] bf16 (hidden a multiple of 64; dims->in_dtype must
+ *         be GDN_BF16);
+ *   w_in  [C_ch + H_v*d_v + 2*H_v][hidden] bf16, rows in this order: the C_ch
+ *         conv inputs x ([q | k | v], head-major, as for the layer), the
+ *         H_v*d_v gate inputs z, H_v rows b, H_v rows a;
+ *   A_log, dt_bias [H_v] fp32 (per value head);
+ * outputs, laid out as the layer calls take them:
+ *   x [B][T][C_ch] bf16, z [B][T][H_v][d_v] bf16 (the products rounded to
+ *   bf16), beta [B][T][H_v] = sigmoid(b), g [B][T][H_v] = -exp(A_log) *
+ *   softplus(a + dt_bias) fp32 (so the decay exp(g) lies in (0, 1)).
+ * The decay and beta parametrisation is not on the pages; this is the
+ * Mamba2-style gate of Gated DeltaNet.  All buffers 16-byte aligned (h,
+ * w_in) or aligned to their element size (the rest); outputs must not
+ * overlap the inputs. */
+GDN_API int gdn_in_proj(const gdn_dims *dims, int64_t T, int32_t hidden, const void *h,
+                        const void *w_in, const float *A_log, const float *dt_bias, void *x,
+                        void *z, float *g, float *beta, void *stream);
+
 /* Zero-centred grouped RMS norm before the sigmoid output gate ("Implement
  * the Qwen3.8 Flash Next Rust and Metal text core", section Implementation:
  * zero-centred norms; its implementation comment: zero-centred grouped RMS

@@ -271,3 +271,44 @@ def decode_multi(x, z, g, beta, w, hist_pool, S_pool, in_slots, out_slots, *, H_
                 S_out[o] = St[0]
                 h_out[o] = ht[0]
     return y, S_out, h_out
+
+
+# ---------------------------------------------------------------------------
+# Input projections ("Implement the Qwen3.8 Flash Next Rust and Metal text
+# core", section Verification: primitive vectors for the GDN projection).
+# The pages give no formula; the reading: one fused weight whose rows are the
+# C_ch conv inputs x, the H_v d_v gate inputs z, H_v rows b and H_v rows a;
+# beta = sigmoid(b) and the log decay g = -exp(A_log) softplus(a + dt_bias)
+# (Gated DeltaNet's Mamba2-style gate), per value head.
+
+def _widen(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def decay_beta(a, b, A_log, dt_bias):
+    """beta = sigmoid(b), g = -exp(A_log) * softplus(a + dt_bias), float64;
+    a, b [..., H_v]; A_log, dt_bias [H_v]."""
+    a, b = _widen(a), _widen(b)
+    A_log, dt_bias = np.asarray(A_log, np.float64), np.asarray(dt_bias, np.float64)
+    beta = 1.0 / (1.0 + np.exp(-b))
+    g = -np.exp(A_log) * np.logaddexp(0.0, a + dt_bias)
+    return g, beta
+
+
+def in_proj(h, w_in, A_log, dt_bias, *, C_ch: int, Z: int, H_v: int):
+    """h [..., hidden] (bf16 bits or float32), w_in [C_ch + Z + 2 H_v, hidden]:
+    returns (x [..., C_ch], z [..., Z], g [..., H_v], beta [..., H_v]), all
+    float64 (x and z unrounded)."""
+    H = _widen(h)
+    W = _widen(w_in)
+    assert W.shape[0] == C_ch + Z + 2 * H_v and W.shape[1] == H.shape[-1]
+    Y = H @ W.T  # library matmul as the product step
+    x = Y[..., :C_ch]
+    z = Y[..., C_ch:C_ch + Z]
+    b = Y[..., C_ch + Z:C_ch + Z + H_v]
+    a = Y[..., C_ch + Z + H_v:]
+    g, beta = decay_beta(a, b, A_log, dt_bias)
+    return x, z, g, beta

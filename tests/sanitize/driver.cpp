@@ -56,6 +56,10 @@ hipError_t launch_decode(const Geom &, int, const float *, const void *, const f
                          hipStream_t) { reached("decode"); }
 hipError_t launch_gated_rmsnorm(const Geom &, int64_t, const float *, const void *, const float *,
                                 float, void *, hipStream_t) { reached("gated_rmsnorm"); }
+hipError_t launch_in_proj(const Geom &, int64_t, int, const void *, const void *, const float *,
+                          const float *, void *, void *, float *, float *, hipStream_t) {
+  reached("in_proj");
+}
 hipError_t launch_prefill_prep(const Geom &, const PrefillWs &, const float *, const float *,
                                char *, const void *, void *, hipStream_t) { reached("prep"); }
 hipError_t launch_prefill_state(const Geom &, const PrefillWs &, const void *, float *, void *,
@@ -146,6 +150,9 @@ static void boundary(const gdn_dims &d0) {
                             nullptr) == GDN_ERR_INVALID_ARG);
   EXPECT(gdn_gated_rmsnorm(&d, 3, static_cast<const float *>(y.p()), z.p(), nullptr, -1.f, z.p(),
                            nullptr) == GDN_ERR_INVALID_ARG);
+  EXPECT(gdn_in_proj(&d, T, 100, x.p(), w.p(), static_cast<const float *>(g.p()),
+                     static_cast<const float *>(be.p()), y.p(), z.p(), static_cast<float *>(S.p()),
+                     static_cast<float *>(hist.p()), nullptr) == GDN_ERR_UNSUPPORTED);  // hidden % 64
   EXPECT(x.unchanged() && z.unchanged() && g.unchanged() && be.unchanged() && w.unchanged() &&
          hist.unchanged() && S.unchanged() && y.unchanged() && wsb.unchanged());
   for (int c = -13; c <= 0; ++c) EXPECT(gdn_status_str(c) != nullptr);
