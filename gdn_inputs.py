@@ -154,3 +154,22 @@ def make_proj_inputs(B: int, T: int, hidden: int, H_k: int, H_v: int, d: int, se
     A_log = rng.uniform(0.0, 2.77, H_v).astype(np.float32)
     dt_bias = rng.uniform(-6.9, -2.25, H_v).astype(np.float32)
     return dict(h=h, w_in=w_in, A_log=A_log, dt_bias=dt_bias)
+
+
+def make_attn_inputs(B: int, T: int, pos0: int, T_max: int, H_q: int, H_kv: int, d: int, seed: int,
+                     q_std: float = 1.0) -> dict:
+    """Inputs of one full-attention call: q [B, T, H_q, d] ~ N(0, q_std^2),
+    k, v [B, T, H_kv, d] ~ N(0, 1), all bf16; the KV cache [B, T_max, H_kv, d]
+    holds N(0, 1) bf16 keys and values at positions 0 .. pos0 - 1 (the earlier
+    context) and zeros after.  With the score scale 1/sqrt(d), q_std = 1 gives
+    scores of about unit spread; a larger q_std gives sharper attention."""
+    rng = np.random.default_rng(seed)
+    q = _normal_cast(rng, (B, T, H_q, d), q_std, "bf16")
+    k = _normal_cast(rng, (B, T, H_kv, d), 1.0, "bf16")
+    v = _normal_cast(rng, (B, T, H_kv, d), 1.0, "bf16")
+    kc = np.zeros((B, T_max, H_kv, d), np.uint16)
+    vc = np.zeros_like(kc)
+    if pos0:
+        kc[:, :pos0] = _normal_cast(rng, (B, pos0, H_kv, d), 1.0, "bf16")
+        vc[:, :pos0] = _normal_cast(rng, (B, pos0, H_kv, d), 1.0, "bf16")
+    return dict(q=q, k=k, v=v, k_cache=kc, v_cache=vc)

@@ -312,3 +312,84 @@ def in_proj(h, w_in, A_log, dt_bias, *, C_ch: int, Z: int, H_v: int):
     a = Y[..., C_ch + Z + H_v:]
     g, beta = decay_beta(a, b, A_log, dt_bias)
     return x, z, g, beta
+
+
+# ---------------------------------------------------------------------------
+# Full attention of the hybrid schedule ("Add a performance-parity Qwen3.8-27B
+# Q4 and Q8 text backend on Metal", section Model and reference contract:
+# three Gated DeltaNet layers to one full-attention layer; section
+# Measurements and gates: the hybrid block; "Implement the Qwen3.8 Flash Next
+# Rust and Metal text core", section Implementation: Qwen RoPE and exact dense
+# 24Q/2KV causal attention; its implementation comment: BF16 KV storage).
+# Readings: RoPE rotates the pairs (i, i + r/2), i < r/2, of the first r
+# dimensions of each head by pos * base^(-2i/r) (the rotate-half form); query
+# head h reads key/value head h / (H_q / H_kv); o = softmax(scale q k^T over
+# keys at positions <= the query's) v; the cache holds the rotated keys and
+# the values in bf16.
+
+def _to_bf16_bits(a):
+    """float64 -> bf16 bits, round to nearest even (the cache's storage)."""
+    a = np.ascontiguousarray(a, np.float64)
+    bits = a.view(np.uint64)
+    lsb = (bits >> np.uint64(45)) & np.uint64(1)
+    r = ((bits + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)).view(np.float64)
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def rope(u, pos, rot_dim: int, base: float):
+    """Rotate the first rot_dim dimensions of u [..., T, H, d] (float64) at
+    positions pos [T]."""
+    u = np.array(u, np.float64, copy=True)
+    half = rot_dim // 2
+    if half == 0:
+        return u
+    inv = base ** (-2.0 * np.arange(half) / rot_dim)
+    ang = np.asarray(pos, np.float64)[:, None] * inv[None, :]  # [T, half]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    a = u[..., :half].copy()
+    b = u[..., half:rot_dim].copy()
+    u[..., :half] = a * c - b * s
+    u[..., half:rot_dim] = b * c + a * s
+    return u
+
+
+def attention(q, k, v, q_pos, k_pos, scale: float):
+    """Causal GQA attention in float64: q [B, Tq, H_q, d] at positions q_pos
+    [Tq], k, v [B, Tk, H_kv, d] at positions k_pos [Tk]; query t sees the keys
+    with k_pos <= q_pos[t].  Returns o [B, Tq, H_q, d]."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    B, Tq, H_q, d = q.shape
+    H_kv = k.shape[2]
+    G = H_q // H_kv
+    o = np.empty_like(q)
+    mask = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]  # [Tq, Tk]
+    for b in range(B):
+        for h in range(H_q):
+            kh = h // G
+            s = scale * (q[b, :, h] @ k[b, :, kh].T)  # [Tq, Tk]
+            s = np.where(mask, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            o[b, :, h] = p @ v[b, :, kh]
+    return o
+
+
+def attn_layer(q, k, v, k_cache, v_cache, pos0: int, *, rot_dim: int, base: float, scale: float):
+    """One attention call over T new tokens at positions pos0 .. pos0+T-1 with
+    the cache's first pos0 positions as earlier context.  q [B, T, H_q, d],
+    k, v [B, T, H_kv, d] (bf16 bits or float32); k_cache, v_cache [B, T_max,
+    H_kv, d] bf16 bits.  Returns (o float64, k_cache, v_cache updated: the
+    rotated keys and the values of the new tokens, rounded to bf16)."""
+    T = np.asarray(q).shape[1]
+    pos = np.arange(pos0, pos0 + T)
+    qr = rope(_widen(q), pos, rot_dim, base)
+    kr = rope(_widen(k), pos, rot_dim, base)
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    kc[:, pos0:pos0 + T] = _to_bf16_bits(kr)
+    vc[:, pos0:pos0 + T] = _to_bf16_bits(_widen(v))
+    L = pos0 + T
+    o = attention(qr, _widen(kc[:, :L]), _widen(vc[:, :L]), pos, np.arange(L), scale)
+    return o, kc, vc
