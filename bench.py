@@ -133,6 +133,120 @@ def fractions(F, Bytes, t_s):
     return {"mfma": round(mf, 4), "hbm": round(hf, 4), "roofline": round(max(mf, hf), 4)}
 
 
+def attn_causal_flops(B, T, pos0, H_q, d):
+    """Products of causal attention: 2 d flops per (query, visible key) pair
+    for q k^T and as many for P v, per query head."""
+    pairs = T * pos0 + T * (T + 1) / 2
+    return 4.0 * d * H_q * B * pairs
+
+
+def attn_bytes(B, T, pos0, H_q, H_kv, d, out_bytes):
+    """Algorithmic HBM bytes of one attention call: q, k, v in (bf16), the new
+    keys and values written to the cache, the whole visible cache read once,
+    o out."""
+    L = pos0 + T
+    return B * (T * (H_q + 2 * H_kv) * d * 2 + T * 2 * H_kv * d * 2 + L * 2 * H_kv * d * 2
+                + T * H_q * d * out_bytes)
+
+
+def hybrid_leg(args, gdn, torch, np, dev, T):
+    """The 3 GDN : 1 full-attention block over one T-token prefill (B=1,
+    hidden 5120): three times (GDN input projections, then the GDN layer with
+    its sigmoid gate, bf16 y) and once (RoPE + KV-cache write + causal GQA
+    attention, 24 query / 2 KV heads of 256, bf16 o).  The attention layer's
+    q/k/v/o projections, the GDN output projections and the MLPs are plain
+    GEMMs outside this path and are not timed."""
+    from gdn_inputs import make_attn_inputs, make_inputs, make_proj_inputs, Geometry
+    hidden = 5120
+    d = gdn.Dims(B=1, H_k=16, H_v=48, d_k=128, d_v=128, in_dtype=gdn.BF16, out_dtype=gdn.BF16)
+    geom = Geometry(B=1, T=T, H_k=16, H_v=48, d_k=128, d_v=128)
+    layers = []
+    for li in range(3):
+        P = make_proj_inputs(1, T, hidden, 16, 48, 128, seed=40 + li)
+        I = make_inputs(geom, seed=50 + li)
+        L = {"h": dev(P["h"]), "w": dev(P["w_in"]), "A": dev(P["A_log"]), "dtb": dev(P["dt_bias"]),
+             "cw": dev(I["w"]), "hist": dev(I["hist"]), "S": dev(I["S"])}
+        L["out"] = gdn.in_proj(d, L["h"], L["w"], L["A"], L["dtb"])
+        L["y"] = torch.empty((1, T, 48, 128), dtype=torch.bfloat16, device="cuda")
+        L["ws"] = torch.empty(gdn.prefill_workspace_bytes(d, T, 64), dtype=torch.uint8,
+                              device="cuda")
+        L["S0"], L["h0"] = L["S"].clone(), L["hist"].clone()
+        layers.append(L)
+    a = gdn.AttnDims(B=1, H_q=24, H_kv=2, d_h=256, rot_dim=64, rope_base=1e7,
+                     out_dtype=gdn.BF16)
+    A = {k: dev(v) for k, v in make_attn_inputs(1, T, 0, T, 24, 2, 256, seed=60).items()}
+    o = torch.empty((1, T, 24, 256), dtype=torch.bfloat16, device="cuda")
+    aws = torch.empty(gdn.attn_workspace_bytes(a, T, 0), dtype=torch.uint8, device="cuda")
+
+    def gdn_layer(L):
+        x, z, g, beta = L["out"]
+        gdn.in_proj(d, L["h"], L["w"], L["A"], L["dtb"], x, z, g, beta)
+        L["S"].copy_(L["S0"])
+        L["hist"].copy_(L["h0"])
+        gdn.prefill_chunked(d, x, z, g, beta, L["cw"], L["hist"], L["S"], chunk=64, y=L["y"],
+                            ws=L["ws"])
+
+    def attn_layer():
+        gdn.attn_prefill(a, A["q"], A["k"], A["v"], A["k_cache"], A["v_cache"], pos0=0, o=o,
+                         ws=aws)
+
+    def block():
+        for L in layers:
+            gdn_layer(L)
+        attn_layer()
+
+    def timed(fn, reps):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = max(args.steps // 2, 3)
+    ms_block = timed(block, reps)
+    ms_gdn = timed(lambda: gdn_layer(layers[0]), reps)
+    ms_attn = timed(attn_layer, reps)
+    # torch's fused attention on the same shapes (KV heads expanded) for context
+    qt = A["q"].transpose(1, 2).contiguous()
+    kt = A["k"].transpose(1, 2).repeat_interleave(12, 1).contiguous()
+    vt = A["v"].transpose(1, 2).repeat_interleave(12, 1).contiguous()
+    sdpa = lambda: torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    try:
+        ms_sdpa = timed(sdpa, reps)
+    except RuntimeError:  # pragma: no cover
+        ms_sdpa = None
+    Fa = attn_causal_flops(1, T, 0, 24, 256)
+    Ba = attn_bytes(1, T, 0, 24, 2, 256, 2)
+    res = {
+        "workload": f"hybrid block, 3 GDN layers (input projections hidden {hidden} + GDN prefill "
+                    f"chunk 64, bf16 y) + 1 attention layer (RoPE rot 64 base 1e7, 24Q/2KV heads "
+                    f"of 256, bf16 KV cache and o), B=1 T={T}",
+        "tokens_per_s": round(T / (ms_block * 1e-3), 1),
+        "us_per_block": round(ms_block * 1e3, 1),
+        "us_per_gdn_layer": round(ms_gdn * 1e3, 1),
+        "us_attention_layer": round(ms_attn * 1e3, 1),
+        "attention": {
+            "roofline": {"bound": "mfma", "achieved": round(Fa / ms_attn / 1e9, 1),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(Fa / ms_attn / 1e9 / PEAK_BF16_TFLOPS, 4),
+                         "alg_flops_per_call": int(Fa), "alg_bytes_per_call": int(Ba)},
+            "torch_sdpa_us": None if ms_sdpa is None else round(ms_sdpa * 1e3, 1),
+        },
+    }
+    log(f"[bench] hybrid block T={T}: {ms_block * 1e3:.0f} us ({T / ms_block * 1e-3:.2f} M tokens/s); "
+        f"GDN layer {ms_gdn * 1e3:.0f} us, attention {ms_attn * 1e3:.0f} us = "
+        f"{Fa / ms_attn / 1e9:.0f} TFLOP/s (torch sdpa {res['attention']['torch_sdpa_us']} us)")
+    del layers, A, o, aws, qt, kt, vt
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,7 +258,7 @@ def main():
                     help="graph replays per decode timing (each replays R rotated steps)")
     ap.add_argument("--legs", default="all",
                     help="comma list of: long64, long128, t4096, decode_b1, decode_b64, in_proj, "
-                         "cpu (default all); the headline leg always runs")
+                         "hybrid, cpu (default all); the headline leg always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run --steps plain device copies of MIB MiB (for scaling the HBM "
@@ -180,7 +294,7 @@ def main():
         return
 
     legs = set(args.legs.split(",")) if args.legs != "all" else {
-        "long64", "long128", "t4096", "decode_b1", "decode_b64", "in_proj", "cpu"}
+        "long64", "long128", "t4096", "decode_b1", "decode_b64", "in_proj", "hybrid", "cpu"}
     if args.no_cpu_baseline:
         legs.discard("cpu")
     head_leg = "long64" if args.chunk == 64 else "long128"
@@ -456,6 +570,13 @@ def main():
             f"the same shape {Fp / ms_t / 1e9:.0f} TFLOP/s")
         del hP, wP, outs
 
+    # ------------------------------------------------------------ hybrid 3:1 block
+    hybrid = None
+    if "hybrid" in legs:
+        # 2048 tokens: within the dense-attention budget of the pages' text
+        # core; 4096: dense attention past it (an upper bound of its cost)
+        hybrid = {f"T{T}": hybrid_leg(args, gdn, torch, np, dev, T) for T in (2048, 4096)}
+
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if "cpu" in legs:
@@ -508,6 +629,7 @@ def main():
         "prefill": out_legs,
         "decode": decode,
         "in_proj": proj,
+        "hybrid_block": hybrid,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

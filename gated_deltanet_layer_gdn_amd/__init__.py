@@ -23,6 +23,7 @@ from ._lib import BF16, F16, F32, GdnError
 __all__ = [
     "Dims", "GdnError", "conv1d", "prefill_chunked", "decode_step", "decode_step_noalloc",
     "decode_multi", "prefill_varlen", "prefill_varlen_workspace_bytes", "gated_rmsnorm", "in_proj",
+    "AttnDims", "attn_prefill", "attn_workspace_bytes",
     "state_save",
     "state_restore", "state_check", "prefill_workspace_bytes", "decode_workspace_bytes",
     "rec_state_bytes", "conv_state_bytes", "state_blob_bytes", "F32", "BF16", "F16",
@@ -50,6 +51,24 @@ class Dims:
     def c(self) -> _lib.GdnDims:
         return _lib.GdnDims(_lib.ABI_VERSION, self.B, self.H_k, self.H_v, self.d_k, self.d_v,
                             self.W, self.in_dtype, self.out_dtype, self.l2_eps, self.q_scale)
+
+
+@dataclass(frozen=True)
+class AttnDims:
+    """Full-attention geometry (mirrors ``gdn_attn_dims``)."""
+    B: int
+    H_q: int = 24
+    H_kv: int = 2
+    d_h: int = 256
+    rot_dim: int = 64
+    out_dtype: int = BF16
+    rope_base: float = 1e7
+    scale: float | None = None
+
+    def c(self) -> _lib.GdnAttnDims:
+        sc = self.d_h ** -0.5 if self.scale is None else self.scale
+        return _lib.GdnAttnDims(_lib.ABI_VERSION, self.B, self.H_q, self.H_kv, self.d_h,
+                                self.rot_dim, BF16, self.out_dtype, self.rope_base, sc)
 
 
 def _torch():
@@ -283,6 +302,37 @@ def prefill_varlen(d: Dims, cu_seqlens, x, z, g, beta, conv_w, conv_pool, rec_po
                               _stream())
     _lib.check(rc, "gdn_prefill_varlen")
     return y
+
+
+def attn_workspace_bytes(a: AttnDims, T: int, pos0: int = 0) -> int:
+    return _lib.load().gdn_attn_workspace_bytes(ctypes.byref(a.c()), T, pos0)
+
+
+def attn_prefill(a: AttnDims, q, k, v, k_cache, v_cache, pos0: int = 0, o=None, ws=None):
+    """Attention over T new tokens at positions pos0..pos0+T-1: q [B,T,H_q,d_h],
+    k/v [B,T,H_kv,d_h] bf16; k_cache/v_cache [B,T_max,H_kv,d_h] bf16 (updated);
+    returns o [B,T,H_q,d_h] in a.out_dtype."""
+    torch = _torch()
+    L = _lib.load()
+    T = q.shape[1]
+    T_max = k_cache.shape[1]
+    args = [_need(q, "q", (a.B, T, a.H_q, a.d_h), torch.bfloat16),
+            _need(k, "k", (a.B, T, a.H_kv, a.d_h), torch.bfloat16),
+            _need(v, "v", (a.B, T, a.H_kv, a.d_h), torch.bfloat16),
+            _need(k_cache, "k_cache", (a.B, T_max, a.H_kv, a.d_h), torch.bfloat16),
+            _need(v_cache, "v_cache", (a.B, T_max, a.H_kv, a.d_h), torch.bfloat16)]
+    if o is None:
+        o = torch.empty((a.B, T, a.H_q, a.d_h), dtype=_dt(a.out_dtype), device=q.device)
+    po = _need(o, "o", (a.B, T, a.H_q, a.d_h), _dt(a.out_dtype))
+    need = L.gdn_attn_workspace_bytes(ctypes.byref(a.c()), T, pos0)
+    if need == 0:
+        raise GdnError(-1, "gdn_attn_prefill", "invalid geometry or positions")
+    ws = _workspace(need, q, ws)
+    rc = L.gdn_attn_prefill(ctypes.byref(a.c()), T, pos0, *args, T_max, po,
+                            ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                            _stream())
+    _lib.check(rc, "gdn_attn_prefill")
+    return o
 
 
 def in_proj(d: Dims, h, w_in, A_log, dt_bias, x=None, z=None, g=None, beta=None):

@@ -29,7 +29,7 @@ EXPORTS = (
     "gdn_state_save", "gdn_state_restore", "gdn_state_check", "gdn_prefill_chunked_timed",
     "gdn_decode_step_timed", "gdn_decode_step_noalloc", "gdn_decode_multi",
     "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_bytes", "gdn_gated_rmsnorm",
-    "gdn_in_proj",
+    "gdn_in_proj", "gdn_attn_workspace_bytes", "gdn_attn_prefill",
 )
 
 
@@ -39,6 +39,15 @@ class GdnDims(ctypes.Structure):
         ("H_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
         ("W", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("l2_eps", ctypes.c_float), ("q_scale", ctypes.c_float),
+    ]
+
+
+class GdnAttnDims(ctypes.Structure):
+    _fields_ = [
+        ("abi", ctypes.c_int32), ("B", ctypes.c_int32), ("H_q", ctypes.c_int32),
+        ("H_kv", ctypes.c_int32), ("d_h", ctypes.c_int32), ("rot_dim", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("rope_base", ctypes.c_float), ("scale", ctypes.c_float),
     ]
 
 
@@ -92,6 +101,11 @@ def load():
     L.gdn_prefill_varlen.restype = ctypes.c_int
     L.gdn_prefill_varlen.argtypes = [dp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz,
                                      vp]
+    ap = ctypes.POINTER(GdnAttnDims)
+    L.gdn_attn_workspace_bytes.restype = sz
+    L.gdn_attn_workspace_bytes.argtypes = [ap, i64, i64]
+    L.gdn_attn_prefill.restype = ctypes.c_int
+    L.gdn_attn_prefill.argtypes = [ap, i64, i64, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]
     L.gdn_in_proj.restype = ctypes.c_int
     L.gdn_in_proj.argtypes = [dp, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_gated_rmsnorm.restype = ctypes.c_int

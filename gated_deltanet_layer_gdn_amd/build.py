@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "conv.hip", "decode.hip", "prep.hip", "prefill.hip", "epilogue.hip", "proj.hip"]
+SOURCES = ["gdn_api.cpp", "conv.hip", "decode.hip", "prep.hip", "prefill.hip", "epilogue.hip", "proj.hip", "attn.hip"]
 HEADERS = ["gdn_device.h", "gdn_internal.h"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 

@@ -223,6 +223,40 @@ size_t decode_ws_bytes(const Geom &g, int T) {
   return round_up(static_cast<size_t>(g.B) * T * g.C_ch * 4, 256);
 }
 
+int check_attn(const gdn_attn_dims *d, AttnGeom *a) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  if (d->abi != GDN_ABI_VERSION) return GDN_ERR_UNSUPPORTED;
+  if (d->B < 1 || d->B > kMaxBatch || d->H_q < 1 || d->H_kv < 1 || d->H_q > 4096)
+    return GDN_ERR_INVALID_ARG;
+  if (d->H_q % d->H_kv) return GDN_ERR_UNSUPPORTED;
+  if (d->d_h != 128 && d->d_h != 256) return GDN_ERR_UNSUPPORTED;
+  if (d->rot_dim < 0 || d->rot_dim > d->d_h || d->rot_dim % 2) return GDN_ERR_INVALID_ARG;
+  if (d->in_dtype != GDN_BF16 || (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16))
+    return GDN_ERR_UNSUPPORTED;
+  if (!(d->rope_base > 1.f && d->rope_base < 1e30f)) return GDN_ERR_INVALID_ARG;
+  if (!(d->scale > -1e30f && d->scale < 1e30f)) return GDN_ERR_INVALID_ARG;
+  a->B = d->B;
+  a->H_q = d->H_q;
+  a->H_kv = d->H_kv;
+  a->D = d->d_h;
+  a->rot = d->rot_dim;
+  a->base = d->rope_base;
+  a->scale = d->scale;
+  a->in_dt = d->in_dtype;
+  a->out_dt = d->out_dtype;
+  return GDN_OK;
+}
+
+// The launches of an attention call keep their work-item counts (grid x
+// block) below 2^31: the RoPE pass B T (H_q + H_kv) d_h / 2, the attention
+// pass about 4 B H_q T.
+bool attn_fits(const AttnGeom &a, int64_t T, int64_t pos0) {
+  constexpr int64_t lim = int64_t(1) << 31;
+  (void)pos0;
+  return int64_t(a.B) * T * (a.H_q + a.H_kv) * (a.D / 2) < lim &&
+         int64_t(a.B) * a.H_q * T * 4 + int64_t(a.B) * a.H_kv * 512 < lim;
+}
+
 }  // namespace gdn
 
 using namespace gdn;
@@ -623,6 +657,37 @@ int gdn_in_proj(const gdn_dims *dims, int64_t T, int32_t hidden, const void *h,
   const hipError_t e = launch_in_proj(g, static_cast<int64_t>(M), hidden, h, w_in, A_log, dt_bias,
                                       x, z, gl, beta, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_in_proj");
+}
+
+size_t gdn_attn_workspace_bytes(const gdn_attn_dims *dims, int64_t T, int64_t pos0) {
+  AttnGeom a;
+  if (check_attn(dims, &a) || T < 1 || pos0 < 0 || pos0 + T > kMaxTokens || !attn_fits(a, T, pos0))
+    return 0;
+  return attn_ws_bytes(a, T, pos0);
+}
+
+int gdn_attn_prefill(const gdn_attn_dims *dims, int64_t T, int64_t pos0, const void *q,
+                     const void *k, const void *v, void *k_cache, void *v_cache, int64_t T_max,
+                     void *o, void *ws, size_t ws_bytes, void *stream) {
+  AttnGeom a;
+  int rc = check_attn(dims, &a);
+  if (rc) return rc;
+  if (T < 1 || pos0 < 0 || T_max < 1 || T_max > kMaxTokens || pos0 + T > T_max ||
+      !attn_fits(a, T, pos0))
+    return GDN_ERR_INVALID_ARG;
+  const size_t bt = static_cast<size_t>(a.B) * T, D = static_cast<size_t>(a.D);
+  const size_t need = attn_ws_bytes(a, T, pos0);
+  const size_t cache = static_cast<size_t>(a.B) * T_max * a.H_kv * D * 2;
+  const Buf in[] = {{q, bt * a.H_q * D * 2, 16}, {k, bt * a.H_kv * D * 2, 16},
+                    {v, bt * a.H_kv * D * 2, 16}};
+  const Buf out[] = {{k_cache, cache, 16}, {v_cache, cache, 16},
+                     {o, bt * a.H_q * D * esize(a.out_dt), esize(a.out_dt)}, {ws, need, 16}};
+  if ((rc = check_buffers(in, 3, out, 4))) return rc;
+  if (ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (injected_launch_failure()) return GDN_ERR_HIP;
+  const hipError_t e = launch_attn_prefill(a, T, pos0, q, k, v, k_cache, v_cache, T_max, o, ws,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_attn_prefill");
 }
 
 int gdn_state_check(const gdn_dims *dims, const void *blob, size_t blob_bytes) {

@@ -111,6 +111,17 @@ hipError_t launch_conv_step(const Geom &g, int T, const void *x, const void *w, 
 hipError_t launch_decode(const Geom &g, int T, const float *qkv, const void *z, const float *gl,
                          const float *beta, float *S, void *y, int n_slots,
                          const int32_t *in_slots, const int32_t *out_slots, hipStream_t s);
+// Full attention of the hybrid schedule (attn.hip): geometry of one call.
+struct AttnGeom {
+  int B, H_q, H_kv, D, rot;  // D = head dimension (128 or 256), rot = rotary width
+  float base, scale;         // RoPE base, score scale
+  int in_dt, out_dt;
+};
+size_t attn_ws_bytes(const AttnGeom &a, int64_t T, int64_t pos0);
+hipError_t launch_attn_prefill(const AttnGeom &a, int64_t T, int64_t pos0, const void *q,
+                               const void *k, const void *v, void *kc, void *vc, int64_t T_max,
+                               void *o, void *ws, hipStream_t s);
+
 // Input projections: Y = H W^T over M rows of `hidden` bf16 values, W
 // [C_ch + H_v D + 2 H_v][hidden] bf16; x, z in bf16, beta and the log decay
 // g in fp32 (see proj.hip).

@@ -247,6 +247,47 @@ GDN_API int gdn_in_proj(const gdn_dims *dims, int64_t T, int32_t hidden, const v
                         const void *w_in, const float *A_log, const float *dt_bias, void *x,
                         void *z, float *g, float *beta, void *stream);
 
+/* The full-attention layer of the hybrid schedule (3 GDN : 1 attention):
+ * Qwen RoPE, a bf16 KV cache and causal grouped-query attention ("Implement
+ * the Qwen3.8 Flash Next Rust and Metal text core", section Implementation:
+ * Qwen RoPE and an exact dense 24Q/2KV causal attention; its implementation
+ * comment: BF16 KV storage; "Add a performance-parity Qwen3.8-27B Q4 and Q8
+ * text backend on Metal", section Measurements and gates: full attention and
+ * the hybrid block measured in isolation). */
+typedef struct gdn_attn_dims {
+  int32_t abi;        /* GDN_ABI_VERSION                                   */
+  int32_t B;          /* sequences                                          */
+  int32_t H_q, H_kv;  /* query heads, key/value heads (H_q % H_kv == 0)      */
+  int32_t d_h;        /* head dimension: 128 or 256                         */
+  int32_t rot_dim;    /* rotary width r (even, <= d_h)                      */
+  int32_t in_dtype;   /* q, k, v and the cache: GDN_BF16                    */
+  int32_t out_dtype;  /* o: GDN_F32 or GDN_BF16                             */
+  float rope_base;    /* RoPE base (> 1)                                    */
+  float scale;        /* score scale, usually 1/sqrt(d_h)                   */
+} gdn_attn_dims;
+
+/* Attention over T new tokens per sequence at positions pos0 .. pos0+T-1,
+ * with the cache's positions 0 .. pos0-1 as earlier context (pos0 = 0: a
+ * fresh prefill; T = 1: one decode step at position pos0).
+ *   q [B][T][H_q][d_h], k, v [B][T][H_kv][d_h] bf16 (before RoPE);
+ *   k_cache, v_cache [B][T_max][H_kv][d_h] bf16, in/out: positions
+ *   pos0 .. pos0+T-1 receive the rotated keys and the values;
+ *   o [B][T][H_q][d_h] out_dtype.
+ * RoPE (a reading of "Qwen RoPE"): the pairs (i, i + r/2), i < r/2, of the
+ * first r dimensions turn by pos * rope_base^(-2i/r).  Query head h reads
+ * KV head h / (H_q / H_kv); o = softmax(scale q k^T over the keys at
+ * positions <= the query's) v, the softmax in fp32, the products on bf16
+ * MFMA with fp32 accumulation.  pos0 + T <= T_max <= 2^24, and
+ * B T (H_q + H_kv) d_h / 2 and 4 B H_q T + 512 B H_kv each below 2^31 (else GDN_ERR_INVALID_ARG; a single sequence at d_h = 256 with
+ * 24 + 2 heads takes T up to 2^19 tokens).  `ws`: at least
+ * gdn_attn_workspace_bytes(dims, T, pos0) bytes (contents ignored).  All
+ * buffers 16-byte aligned (o: its element size); outputs, caches and
+ * workspace must not overlap each other or the inputs. */
+GDN_API size_t gdn_attn_workspace_bytes(const gdn_attn_dims *dims, int64_t T, int64_t pos0);
+GDN_API int gdn_attn_prefill(const gdn_attn_dims *dims, int64_t T, int64_t pos0, const void *q,
+                             const void *k, const void *v, void *k_cache, void *v_cache,
+                             int64_t T_max, void *o, void *ws, size_t ws_bytes, void *stream);
+
 /* Zero-centred grouped RMS norm before the sigmoid output gate ("Implement
  * the Qwen3.8 Flash Next Rust and Metal text core", section Implementation:
  * zero-centred norms; its implementation comment: zero-centred grouped RMS

@@ -56,6 +56,10 @@ hipError_t launch_decode(const Geom &, int, const float *, const void *, const f
                          hipStream_t) { reached("decode"); }
 hipError_t launch_gated_rmsnorm(const Geom &, int64_t, const float *, const void *, const float *,
                                 float, void *, hipStream_t) { reached("gated_rmsnorm"); }
+size_t attn_ws_bytes(const AttnGeom &, int64_t, int64_t) { return 256; }
+hipError_t launch_attn_prefill(const AttnGeom &, int64_t, int64_t, const void *, const void *,
+                               const void *, void *, void *, int64_t, void *, void *,
+                               hipStream_t) { reached("attn"); }
 hipError_t launch_in_proj(const Geom &, int64_t, int, const void *, const void *, const float *,
                           const float *, void *, void *, float *, float *, hipStream_t) {
   reached("in_proj");

@@ -264,6 +264,55 @@ def test_prefill_varlen_rejects_bad_tables_and_leaves_buffers_untouched(lib, dim
     assert b.unchanged()
 
 
+def test_attn_rejects_and_leaves_buffers_untouched(lib):
+    from gated_deltanet_layer_gdn_amd import _lib
+
+    B, T, T_max, H_q, H_kv, d = 2, 40, 64, 6, 2, 128
+    a = _lib.GdnAttnDims(_lib.ABI_VERSION, B, H_q, H_kv, d, 32, 1, 0, 1e4, d ** -0.5)
+    need = lib.gdn_attn_workspace_bytes(ctypes.byref(a), T, 0)
+    assert need >= B * T * H_q * d * 2  # rotated queries (+ split partials)
+    assert lib.gdn_attn_workspace_bytes(ctypes.byref(a), 0, 0) == 0
+    assert lib.gdn_attn_workspace_bytes(ctypes.byref(a), 1 << 22, 0) == 0  # launch size limit
+    rng = np.random.default_rng(0)
+    mk = lambda n: rng.integers(0, 255, n, dtype=np.uint8)
+    bufs = dict(q=mk(B * T * H_q * d * 2 + 64), k=mk(B * T * H_kv * d * 2 + 64),
+                v=mk(B * T * H_kv * d * 2 + 64), kc=mk(B * T_max * H_kv * d * 2 + 64),
+                vc=mk(B * T_max * H_kv * d * 2 + 64), o=mk(B * T * H_q * d * 4 + 64),
+                ws=mk(need + 64))
+    copies = {n: v.copy() for n, v in bufs.items()}
+    p = lambda n, off=0: ctypes.c_void_p(bufs[n].ctypes.data + (-bufs[n].ctypes.data % 16) + off)
+
+    def call(dims_=a, T_=T, pos0=0, T_max_=T_max, ws_bytes=need, **o):
+        return lib.gdn_attn_prefill(ctypes.byref(dims_), T_, pos0, o.get("q", p("q")), p("k"), p("v"),
+                                    o.get("kc", p("kc")), p("vc"), T_max_, o.get("o", p("o")),
+                                    p("ws"), ws_bytes, None)
+
+    def variant(**f):
+        b = _lib.GdnAttnDims.from_buffer_copy(a)
+        for k_, v_ in f.items():
+            setattr(b, k_, v_)
+        return b
+
+    assert call(T_=0) == INVALID
+    assert call(pos0=T_max - T + 1) == INVALID                  # past the cache
+    assert call(T_max_=T - 1) == INVALID
+    assert call(dims_=variant(H_q=5)) == UNSUPPORTED            # not a multiple of H_kv
+    assert call(dims_=variant(d_h=64)) == UNSUPPORTED
+    assert call(dims_=variant(rot_dim=33)) == INVALID
+    assert call(dims_=variant(rot_dim=130)) == INVALID
+    assert call(dims_=variant(in_dtype=0)) == UNSUPPORTED
+    assert call(dims_=variant(out_dtype=2)) == UNSUPPORTED
+    assert call(dims_=variant(rope_base=1.0)) == INVALID
+    assert call(dims_=variant(abi=7)) == UNSUPPORTED
+    assert call(q=None) == INVALID
+    assert call(q=p("q", 2)) == ALIGN
+    assert call(o=p("kc")) == ALIAS
+    assert call(kc=p("vc")) == ALIAS
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    for n in bufs:
+        np.testing.assert_array_equal(bufs[n], copies[n], err_msg=n)
+
+
 def test_injected_launch_failure_leaves_buffers_untouched(lib, dims, monkeypatch):
     d, T, C = dims, 20, 32
     need = lib.gdn_prefill_workspace_bytes(ctypes.byref(d), T, C)
