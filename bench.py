@@ -40,16 +40,33 @@ ROTATE_BYTES = 512 << 20   # rotated state sets per decode timing
 COLD_BYTES = 512 << 20     # device write between cold repetitions
 CSRC = os.path.join(ROOT, "gated_deltanet_layer_gdn_amd", "csrc")
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs (one
+# HBM bytes per call from rocprofv3 FETCH_SIZE and WRITE_SIZE runs (one
 # counter per run), scaled by what the same counters read on a 1 GiB device
 # copy (reads x2, writes x1; the summaries under profiles/ give the commands
-# and the raw figures).  They hold for the kernel sources whose combined
-# SHA-256 is recorded with them; after any change under csrc/ the bench
-# reports the traffic as null until the counters are taken again.
+# and the raw figures).  Each leg's figures hold for the sources of its
+# kernels, whose combined SHA-256 is recorded with them; after any change to
+# those sources the bench reports the leg's traffic as null until the
+# counters are taken again.
+LEG_SOURCES = {
+    "long64": ("conv.hip", "prep.hip", "prefill.hip", "gdn_device.h", "gdn_internal.h"),
+    "long128": ("conv.hip", "prep.hip", "prefill.hip", "gdn_device.h", "gdn_internal.h"),
+    "t4096": ("conv.hip", "prep.hip", "prefill.hip", "gdn_device.h", "gdn_internal.h"),
+    "decode_b1": ("conv.hip", "decode.hip", "gdn_device.h", "gdn_internal.h"),
+    "decode_b64": ("conv.hip", "decode.hip", "gdn_device.h", "gdn_internal.h"),
+}
 MEASURED_TRAFFIC = {
-    "csrc_sha256": None,
-    # leg -> {kernel: (read_bytes, write_bytes)}
-    "legs": {},
+    # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
+    # profiles/gdn_hbm_bytes_prefill_t65536_t4096_decode.txt (sums over the leg's kernels)
+    "long64": {"sha256": "7c9a6c4487d1b89462d60b1535135688cf75956fd95d2abbbe6342d56ffc77bb",
+               "read": 5857750000, "write": 3226520000},
+    "long128": {"sha256": "7c9a6c4487d1b89462d60b1535135688cf75956fd95d2abbbe6342d56ffc77bb",
+               "read": 9667510000, "write": 7288920000},
+    "t4096": {"sha256": "7c9a6c4487d1b89462d60b1535135688cf75956fd95d2abbbe6342d56ffc77bb",
+               "read": 326740000, "write": 204550000},
+    "decode_b1": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
+               "read": 3560000, "write": 3270000},
+    "decode_b64": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
+               "read": 218460000, "write": 209450000},
 }
 
 
@@ -57,9 +74,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def csrc_sha256() -> str:
+def sources_sha256(names) -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(names):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -67,11 +84,11 @@ def csrc_sha256() -> str:
 
 def measured_traffic(leg):
     """Measured HBM bytes per call of a leg (read + write over its kernels),
-    or None if the sources changed since the counters were taken."""
-    e = MEASURED_TRAFFIC["legs"].get(leg)
-    if not e or MEASURED_TRAFFIC["csrc_sha256"] != csrc_sha256():
+    or None if its sources changed since the counters were taken."""
+    e = MEASURED_TRAFFIC.get(leg)
+    if not e or e["sha256"] != sources_sha256(LEG_SOURCES[leg]):
         return None
-    return int(sum(r + w for r, w in e.values()))
+    return int(e["read"] + e["write"])
 
 
 def prefill_flops_per_token(H_k, H_v, d_k, d_v, C):
@@ -263,6 +280,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run --steps plain device copies of MIB MiB (for scaling the HBM "
                          "byte counters of rocprofv3 against a kernel of known traffic)")
+    ap.add_argument("--decode-graph-only", type=int, default=0, metavar="ROUNDS",
+                    help="only replay the captured B=1 decode graph ROUNDS times (for a kernel "
+                         "trace of the graph replay alone, without eager or timed launches)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -293,6 +313,46 @@ def main():
                           "copies": args.steps}), flush=True)
         return
 
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    if args.decode_graph_only:
+        # The B=1 decode step as a captured graph of R steps on rotated state
+        # sets, replayed; no other launch reaches the GPU after the capture.
+        wl_d, Id = workload_inputs(1)
+        Gd = wl_d.geom
+        dd = gdn.Dims(B=1, H_k=Gd.H_k, H_v=Gd.H_v, d_k=Gd.d_k, d_v=Gd.d_v, in_dtype=gdn.BF16,
+                      out_dtype=gdn.F32)
+        R = max(2, math.ceil(ROTATE_BYTES / Id["S"].nbytes))
+        Dd = {k: dev(v) for k, v in Id.items()}
+        Ss = [Dd["S"].clone() for _ in range(R)]
+        Hs = [Dd["hist"].clone() for _ in range(R)]
+        yd = torch.empty((1, Gd.H_v, Gd.d_v), dtype=torch.float32, device="cuda")
+        wsd = torch.empty(gdn.decode_workspace_bytes(dd), dtype=torch.uint8, device="cuda")
+        args_d = (Dd["x"].reshape(1, Gd.C_ch), Dd["z"].reshape(1, Gd.H_v, Gd.d_v),
+                  Dd["g"].reshape(1, Gd.H_v), Dd["beta"].reshape(1, Gd.H_v), Dd["w"])
+        for r in range(R):
+            gdn.decode_step(dd, *args_d, Hs[r], Ss[r], y=yd, ws=wsd)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for r in range(R):
+                gdn.decode_step(dd, *args_d, Hs[r], Ss[r], y=yd, ws=wsd)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.decode_graph_only):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (args.decode_graph_only * R)
+        print(json.dumps({"decode_graph_us_per_step": round(us, 3), "steps_per_graph": R,
+                          "replays": args.decode_graph_only}), flush=True)
+        return
+
     legs = set(args.legs.split(",")) if args.legs != "all" else {
         "long64", "long128", "t4096", "decode_b1", "decode_b64", "in_proj", "hybrid", "cpu"}
     if args.no_cpu_baseline:
@@ -301,11 +361,6 @@ def main():
     if args.chunk not in (64, 128):
         raise SystemExit("--chunk must be 64 or 128 (the long-context workload's chunk sizes)")
     legs.add(head_leg)
-
-    def dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
 
     cold_buf = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device="cuda")
 
