@@ -12,12 +12,14 @@
 // query's) v.
 //
 // Launches per call:
-//   rope_cache_kernel  rotates q (into the workspace, bf16) and k (into the
-//                      cache), copies v into the cache, at positions
-//                      pos0 .. pos0 + T - 1; the angle is formed in double
-//                      and reduced mod 2 pi before the fp32 sin/cos, so long
-//                      positions keep their accuracy;
-//   attn_kernel        flash-style causal attention.  A block of 8 waves owns
+//   kv_cache_kernel    the new keys, rotated, and values into the cache, and
+//                      the cos and sin of the RoPE angles of the new
+//                      positions into the workspace (T x r/2 pairs; the angle
+//                      formed in double and reduced mod 2 pi before the fp32
+//                      sin/cos, so long positions keep their accuracy);
+//   attn_kernel        flash-style causal attention; each lane rotates its
+//                      query operand while loading it (the rotated queries
+//                      never go to memory).  A block of 8 waves owns
 //                      128 (token, head) rows of one KV head's query group
 //                      and walks 64-position KV tiles staged in LDS (V
 //                      transposed on the way in).  S^T = K Q^T on the MFMA,
@@ -40,48 +42,47 @@ namespace {
 
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
-// One thread per pair index p < D/2 of one (b, t, head): p < r/2 rotates
-// dimensions (p, p + r/2); the others copy two of the dimensions past r.
+// The new keys, rotated, and the new values into the cache at positions
+// pos0 .. pos0 + T - 1, and the RoPE table of those positions for the
+// attention pass.  One thread per pair of dimensions of one (b, t, KV head):
+// thread p < r/2 turns the pair (p, p + r/2) by the angle (pos0 + t) *
+// base^(-2p/r), formed in double and reduced mod 2 pi before the fp32
+// sincos (positions of 10^5 and more keep their accuracy), and the blocks of
+// sequence 0, KV head 0 store its cos and sin as cs[t][p]; the other threads
+// copy two dimensions past r.  Every thread copies two dimensions of v.
 template <int D>
-__global__ __launch_bounds__(D / 2) void rope_cache_kernel(AttnGeom a, int64_t T, int64_t pos0,
-                                                           int64_t T_max, const uint16_t *q,
-                                                           const uint16_t *k,
-                                                           const uint16_t *v, uint16_t *qr,
-                                                           uint16_t *kc, uint16_t *vc) {
+__global__ __launch_bounds__(D / 2) void kv_cache_kernel(AttnGeom a, int64_t T, int64_t pos0,
+                                                         int64_t T_max, const uint16_t *k,
+                                                         const uint16_t *v, float2 *cs,
+                                                         uint16_t *kc, uint16_t *vc) {
   const int p = threadIdx.x;
-  int64_t idx = blockIdx.x;  // ((b * T + t) * (H_q + H_kv) + head)
-  const int heads = a.H_q + a.H_kv;
-  const int head = static_cast<int>(idx % heads);
-  idx /= heads;
+  int64_t idx = blockIdx.x;  // (b * T + t) * H_kv + head
+  const int head = static_cast<int>(idx % a.H_kv);
+  idx /= a.H_kv;
   const int64_t t = idx % T;
   const int b = static_cast<int>(idx / T);
-  const int64_t pos = pos0 + t;
-  const bool is_q = head < a.H_q;
-  const uint16_t *src = is_q ? q + ((b * T + t) * a.H_q + head) * D
-                             : k + ((b * T + t) * a.H_kv + (head - a.H_q)) * D;
-  uint16_t *dst = is_q ? qr + ((b * T + t) * a.H_q + head) * D
-                       : kc + ((b * T_max + pos) * a.H_kv + (head - a.H_q)) * D;
+  const uint16_t *src = k + ((b * T + t) * a.H_kv + head) * D;
+  const int64_t crow = ((b * T_max + pos0 + t) * a.H_kv + head) * D;
+  uint16_t *dst = kc + crow;
   const int half = a.rot / 2;
   if (p < half) {
     const double inv = pow(static_cast<double>(a.base), -2.0 * p / a.rot);
-    double ang = static_cast<double>(pos) * inv;
+    double ang = static_cast<double>(pos0 + t) * inv;
     ang -= kTwoPi * floor(ang / kTwoPi);
-    float sn, cs;
-    sincosf(static_cast<float>(ang), &sn, &cs);
+    float sn, c;
+    sincosf(static_cast<float>(ang), &sn, &c);
+    if (b == 0 && head == 0) cs[t * half + p] = make_float2(c, sn);
     const float x0 = bf16_bits_to_f32(src[p]), x1 = bf16_bits_to_f32(src[p + half]);
-    dst[p] = f32_to_bf16_bits(x0 * cs - x1 * sn);
-    dst[p + half] = f32_to_bf16_bits(x1 * cs + x0 * sn);
+    dst[p] = f32_to_bf16_bits(x0 * c - x1 * sn);
+    dst[p + half] = f32_to_bf16_bits(x1 * c + x0 * sn);
   } else {
     const int j = a.rot + 2 * (p - half);
     dst[j] = src[j];
     dst[j + 1] = src[j + 1];
   }
-  if (!is_q) {
-    const uint16_t *vs = v + ((b * T + t) * a.H_kv + (head - a.H_q)) * D;
-    uint16_t *vd = vc + ((b * T_max + pos) * a.H_kv + (head - a.H_q)) * D;
-    vd[2 * p] = vs[2 * p];
-    vd[2 * p + 1] = vs[2 * p + 1];
-  }
+  const uint16_t *vs = v + ((b * T + t) * a.H_kv + head) * D;
+  vc[crow + 2 * p] = vs[2 * p];
+  vc[crow + 2 * p + 1] = vs[2 * p + 1];
 }
 
 // Geometry of the attention pass, fixed on the host per call.
@@ -92,7 +93,8 @@ struct AttnArgs {
   int n_fb;          // row blocks per (sequence, KV head)
   int64_t rows_pad;  // n_fb * rows per block
   int n_split, tps;  // KV splits and KV tiles per split (1, all: no split)
-  const uint16_t *qr, *kc, *vc;
+  const uint16_t *q, *kc, *vc;  // q as given (RoPE applied here, on load)
+  const float2 *cs;             // RoPE cos / sin of the new positions [T][r/2]
   void *o;
   float *part_o, *part_ml;  // partial results when n_split > 1
 };
@@ -153,18 +155,46 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs p) {
   const int64_t qpos = p.pos0 + tq;
   u16x8 qb[NS];
   {
-    const uint16_t *qp = p.qr + ((b * p.T + tq) * a.H_q + hq) * D + 8 * g;
+    // The lane's eight dimensions 32 s + 8 g .. + 7 of each K step, turned by
+    // RoPE in fp32 (dimension d < r/2 pairs with d + r/2) and rounded to bf16;
+    // r is a multiple of 16, so an 8-dimension block lies wholly below r/2,
+    // in [r/2, r) or past r.
+    const uint16_t *qp = p.q + ((b * p.T + tq) * a.H_q + hq) * D;
+    const int half = a.rot / 2;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qb[s] = *reinterpret_cast<const u16x8 *>(qp + 32 * s);
+    for (int s = 0; s < NS; ++s) {
+      const int d0 = 32 * s + 8 * g;
+      qb[s] = *reinterpret_cast<const u16x8 *>(qp + d0);
+      if (d0 < a.rot) {
+        const bool lo = d0 < half;
+        const int i0 = lo ? d0 : d0 - half;
+        const u16x8 pq = *reinterpret_cast<const u16x8 *>(qp + (lo ? d0 + half : d0 - half));
+        const float4 *cp = reinterpret_cast<const float4 *>(p.cs + tq * half + i0);
+        u16x8 r;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float4 c2 = cp[e2];  // (cos, sin) of pairs i0 + 2 e2, i0 + 2 e2 + 1
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int e = 2 * e2 + h2;
+            const float cs_ = h2 ? c2.z : c2.x, sn_ = h2 ? c2.w : c2.y;
+            const float x = bf16_bits_to_f32(qb[s][e]), y = bf16_bits_to_f32(pq[e]);
+            r[e] = f32_to_bf16_bits(lo ? x * cs_ - y * sn_ : x * cs_ + y * sn_);
+          }
+        }
+        qb[s] = r;
+      }
+    }
   }
   const float sl2 = a.scale * 1.4426950408889634f;  // scores in log2 units
   f32x4 acc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_lane = 0.f;
 
   // KV tiles up to the block's last query position, this split's share.
   const int64_t f_last = f0 + R - 1 < TG ? f0 + R - 1 : TG - 1;
+  const int64_t q_first = p.pos0 + f0 / p.G;  // the block's first query position
   const int n_kv = static_cast<int>((p.pos0 + f_last / p.G) / 64 + 1);
   const int kt0 = s_idx * p.tps;
   const int kt1 = kt0 + p.tps < n_kv ? kt0 + p.tps : n_kv;
@@ -245,52 +275,70 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs p) {
     }
     // Online softmax of row c (log2 units, causal mask).  A row with no
     // visible key yet (possible only in a split) keeps p = 0 and alpha = 0.
+    // Tiles wholly at or before the block's first query position need no
+    // mask (the test is the same for the whole block).
     float mx = -INFINITY;
+    if (t0 + 63 <= q_first) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t kp = t0 + 16 * m + 4 * g + r;
-        const float sv = kp <= qpos ? st[m][r] * sl2 : -INFINITY;
-        st[m][r] = sv;
-        mx = fmaxf(mx, sv);
-      }
+        for (int r = 0; r < 4; ++r) {
+          st[m][r] *= sl2;
+          mx = fmaxf(mx, st[m][r]);
+        }
+    } else {
+      const int dk = static_cast<int>(qpos - t0) - 4 * g;  // key 16 m + r visible iff <= dk
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sv = 16 * m + r <= dk ? st[m][r] * sl2 : -INFINITY;
+          st[m][r] = sv;
+          mx = fmaxf(mx, sv);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
+    // Lazy rescaling: a row keeps its reference maximum until the tile's
+    // exceeds it by more than 8 (log2 units), so its weights stay below 2^8
+    // and most tiles skip the rescale of O; numerator and denominator use
+    // the same reference, so the normalised result is unchanged.
+    const bool grow = mx > m_run + 8.f;
+    const float m_new = grow ? mx : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float rs = 0.f;
+    if (__ballot(grow)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 1 for rows that keep it
+      l_lane *= alpha;
+      // O's rows are 4 g + r, whose factors sit in lanes c = 4 g + r.
+      float al[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, kWave);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] *= al[r];
+    }
+    m_run = m_new;
+    // This lane's share of the row sum (reduced over the row's four lanes once, at the end).
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pv = __builtin_amdgcn_exp2f(st[m][r] - m_use);
         st[m][r] = pv;
-        rs += pv;
+        l_lane += pv;
       }
-    rs += __shfl_xor(rs, 16, kWave);
-    rs += __shfl_xor(rs, 32, kWave);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    // Rescale O: its rows are 4 g + r, whose factors sit in lanes c = 4 g + r.
-    float al[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, kWave);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[j][r] *= al[r];
-    // O += P V: P (bf16) as the A operand straight from the score registers.
+    // O += P V: P (bf16, the packed round-to-nearest-even convert) as the A
+    // operand straight from the score registers.
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       uint32_t pw[4];
 #pragma unroll
       for (int r = 0; r < 4; r += 2) {
-        pw[r / 2] = static_cast<uint32_t>(f32_to_bf16_bits(st[2 * s2][r])) |
-                    (static_cast<uint32_t>(f32_to_bf16_bits(st[2 * s2][r + 1])) << 16);
-        pw[2 + r / 2] = static_cast<uint32_t>(f32_to_bf16_bits(st[2 * s2 + 1][r])) |
-                        (static_cast<uint32_t>(f32_to_bf16_bits(st[2 * s2 + 1][r + 1])) << 16);
+        const f32x2 a0 = {st[2 * s2][r], st[2 * s2][r + 1]};
+        const f32x2 a1 = {st[2 * s2 + 1][r], st[2 * s2 + 1][r + 1]};
+        pw[r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a0, bf16x2));
+        pw[2 + r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a1, bf16x2));
       }
       const u32x4 pa = {pw[0], pw[1], pw[2], pw[3]};
       const u16x8 pop = __builtin_bit_cast(u16x8, pa);
@@ -302,6 +350,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs p) {
     }
     __syncthreads();
   }
+  float l_run = l_lane + __shfl_xor(l_lane, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
   if (SPLIT) {
     // Unnormalised rows 4 g + r with the row maximum (log2 units) and sum.
     const int64_t rows_total = static_cast<int64_t>(n_bk) * p.rows_pad;
@@ -383,7 +433,7 @@ constexpr int kAttnSplitBelow = 64;      // split only below this many row block
 struct AttnPlan {
   int G, n_fb, n_split, tps;
   int64_t rows_pad;
-  size_t q_bytes, part_o_bytes, part_ml_bytes;
+  size_t cs_bytes, part_o_bytes, part_ml_bytes;
 };
 
 AttnPlan attn_plan(const AttnGeom &a, int64_t T, int64_t pos0) {
@@ -403,7 +453,7 @@ AttnPlan attn_plan(const AttnGeom &a, int64_t T, int64_t pos0) {
   }
   pl.tps = (n_kv + split - 1) / split;
   pl.n_split = (n_kv + pl.tps - 1) / pl.tps;
-  pl.q_bytes = (static_cast<size_t>(a.B) * T * a.H_q * a.D * 2 + 255) / 256 * 256;
+  pl.cs_bytes = (static_cast<size_t>(T) * (a.rot / 2) * 8 + 255) / 256 * 256;
   const size_t rows = static_cast<size_t>(pl.n_split) * a.B * a.H_kv * pl.rows_pad;
   pl.part_o_bytes = pl.n_split > 1 ? (rows * a.D * 4 + 255) / 256 * 256 : 0;
   pl.part_ml_bytes = pl.n_split > 1 ? (rows * 2 * 4 + 255) / 256 * 256 : 0;
@@ -430,7 +480,7 @@ void launch_attn_core(const AttnArgs &p, hipStream_t s) {
 
 size_t attn_ws_bytes(const AttnGeom &a, int64_t T, int64_t pos0) {
   const AttnPlan pl = attn_plan(a, T, pos0);
-  return pl.q_bytes + pl.part_o_bytes + pl.part_ml_bytes;
+  return pl.cs_bytes + pl.part_o_bytes + pl.part_ml_bytes;
 }
 
 hipError_t launch_attn_prefill(const AttnGeom &a, int64_t T, int64_t pos0, const void *q,
@@ -448,29 +498,29 @@ hipError_t launch_attn_prefill(const AttnGeom &a, int64_t T, int64_t pos0, const
   p.rows_pad = pl.rows_pad;
   p.n_split = pl.n_split;
   p.tps = pl.tps;
-  p.qr = reinterpret_cast<const uint16_t *>(wsb);
+  p.q = static_cast<const uint16_t *>(q);
   p.kc = static_cast<const uint16_t *>(kc);
   p.vc = static_cast<const uint16_t *>(vc);
+  p.cs = reinterpret_cast<const float2 *>(wsb);
   p.o = o;
-  p.part_o = reinterpret_cast<float *>(wsb + pl.q_bytes);
-  p.part_ml = reinterpret_cast<float *>(wsb + pl.q_bytes + pl.part_o_bytes);
-  uint16_t *qr = reinterpret_cast<uint16_t *>(wsb);
-  const auto *q16 = static_cast<const uint16_t *>(q);
+  p.part_o = reinterpret_cast<float *>(wsb + pl.cs_bytes);
+  p.part_ml = reinterpret_cast<float *>(wsb + pl.cs_bytes + pl.part_o_bytes);
   const auto *k16 = static_cast<const uint16_t *>(k);
   const auto *v16 = static_cast<const uint16_t *>(v);
   auto *kc16 = static_cast<uint16_t *>(kc);
   auto *vc16 = static_cast<uint16_t *>(vc);
-  const dim3 g1(static_cast<unsigned>(static_cast<int64_t>(a.B) * T * (a.H_q + a.H_kv)));
+  float2 *cs = reinterpret_cast<float2 *>(wsb);
+  const dim3 g1(static_cast<unsigned>(static_cast<int64_t>(a.B) * T * a.H_kv));
   if (a.D == 256) {
-    hipLaunchKernelGGL((rope_cache_kernel<256>), g1, dim3(128), 0, s, a, T, pos0, T_max, q16, k16,
-                       v16, qr, kc16, vc16);
+    hipLaunchKernelGGL((kv_cache_kernel<256>), g1, dim3(128), 0, s, a, T, pos0, T_max, k16, v16, cs,
+                       kc16, vc16);
     if (a.out_dt == 0)
       launch_attn_core<256, 0>(p, s);
     else
       launch_attn_core<256, 1>(p, s);
   } else {
-    hipLaunchKernelGGL((rope_cache_kernel<128>), g1, dim3(64), 0, s, a, T, pos0, T_max, q16, k16,
-                       v16, qr, kc16, vc16);
+    hipLaunchKernelGGL((kv_cache_kernel<128>), g1, dim3(64), 0, s, a, T, pos0, T_max, k16, v16, cs,
+                       kc16, vc16);
     if (a.out_dt == 0)
       launch_attn_core<128, 0>(p, s);
     else

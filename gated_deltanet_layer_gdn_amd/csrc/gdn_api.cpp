@@ -230,7 +230,7 @@ int check_attn(const gdn_attn_dims *d, AttnGeom *a) {
     return GDN_ERR_INVALID_ARG;
   if (d->H_q % d->H_kv) return GDN_ERR_UNSUPPORTED;
   if (d->d_h != 128 && d->d_h != 256) return GDN_ERR_UNSUPPORTED;
-  if (d->rot_dim < 0 || d->rot_dim > d->d_h || d->rot_dim % 2) return GDN_ERR_INVALID_ARG;
+  if (d->rot_dim < 0 || d->rot_dim > d->d_h || d->rot_dim % 16) return GDN_ERR_INVALID_ARG;
   if (d->in_dtype != GDN_BF16 || (d->out_dtype != GDN_F32 && d->out_dtype != GDN_BF16))
     return GDN_ERR_UNSUPPORTED;
   if (!(d->rope_base > 1.f && d->rope_base < 1e30f)) return GDN_ERR_INVALID_ARG;

@@ -259,7 +259,7 @@ typedef struct gdn_attn_dims {
   int32_t B;          /* sequences                                          */
   int32_t H_q, H_kv;  /* query heads, key/value heads (H_q % H_kv == 0)      */
   int32_t d_h;        /* head dimension: 128 or 256                         */
-  int32_t rot_dim;    /* rotary width r (even, <= d_h)                      */
+  int32_t rot_dim;    /* rotary width r (a multiple of 16, <= d_h)          */
   int32_t in_dtype;   /* q, k, v and the cache: GDN_BF16                    */
   int32_t out_dtype;  /* o: GDN_F32 or GDN_BF16                             */
   float rope_base;    /* RoPE base (> 1)                                    */

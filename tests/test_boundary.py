@@ -270,7 +270,7 @@ def test_attn_rejects_and_leaves_buffers_untouched(lib):
     B, T, T_max, H_q, H_kv, d = 2, 40, 64, 6, 2, 128
     a = _lib.GdnAttnDims(_lib.ABI_VERSION, B, H_q, H_kv, d, 32, 1, 0, 1e4, d ** -0.5)
     need = lib.gdn_attn_workspace_bytes(ctypes.byref(a), T, 0)
-    assert need >= B * T * H_q * d * 2  # rotated queries (+ split partials)
+    assert need >= T * 16 * 8  # RoPE cos/sin table (+ split partials)
     assert lib.gdn_attn_workspace_bytes(ctypes.byref(a), 0, 0) == 0
     assert lib.gdn_attn_workspace_bytes(ctypes.byref(a), 1 << 22, 0) == 0  # launch size limit
     rng = np.random.default_rng(0)
@@ -299,6 +299,7 @@ def test_attn_rejects_and_leaves_buffers_untouched(lib):
     assert call(dims_=variant(H_q=5)) == UNSUPPORTED            # not a multiple of H_kv
     assert call(dims_=variant(d_h=64)) == UNSUPPORTED
     assert call(dims_=variant(rot_dim=33)) == INVALID
+    assert call(dims_=variant(rot_dim=24)) == INVALID             # not a multiple of 16
     assert call(dims_=variant(rot_dim=130)) == INVALID
     assert call(dims_=variant(in_dtype=0)) == UNSUPPORTED
     assert call(dims_=variant(out_dtype=2)) == UNSUPPORTED
