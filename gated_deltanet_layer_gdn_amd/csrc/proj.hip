@@ -49,6 +49,7 @@ struct ProjArgs {
   float *g, *beta;     // [M][H_v]
   int64_t M;
   int K, N, C_ch, Z, H_v;
+  int n_begin, n_count;  // the columns this launch covers: [n_begin, n_begin + n_count)
 };
 
 __device__ __forceinline__ float softplus_f(float u) {
@@ -159,7 +160,7 @@ void proj_kernel(ProjArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_mt = static_cast<int>((a.M + BM - 1) / BM);
-  const int n_nt = (a.N + BN - 1) / BN;
+  const int n_nt = (a.n_count + BN - 1) / BN;
   const int lid = xcd_remap_p(blockIdx.x, n_mt * n_nt);
   // grouped raster: kGroupM M tiles share each N tile in turn
   const int per_group = kGroupM * n_nt;
@@ -170,7 +171,7 @@ void proj_kernel(ProjArgs a) {
   const int mt = first_mt + in_grp % gm;
   const int nt = in_grp / gm;
   const int64_t m0 = static_cast<int64_t>(mt) * BM;
-  const int n0 = nt * BN;
+  const int n0 = a.n_begin + nt * BN;
 
   // Rows past M or N re-read the last row (their products are not stored).
   const int row0 = tid >> 3, part = tid & 7;
@@ -247,7 +248,7 @@ void proj_kernel(ProjArgs a) {
 template <int BM, int BN, int WGM, int WGN, int STAGES>
 void launch_tiles(const ProjArgs &a, hipStream_t s) {
   const int64_t n_mt = (a.M + BM - 1) / BM;
-  const int64_t n_nt = (a.N + BN - 1) / BN;
+  const int64_t n_nt = (a.n_count + BN - 1) / BN;
   hipLaunchKernelGGL((proj_kernel<BM, BN, WGM, WGN, STAGES>), dim3(static_cast<unsigned>(n_mt * n_nt)),
                      dim3(ProjShape<BM, BN, WGM, WGN>::kThreads), 0, s, a);
 }
@@ -259,6 +260,7 @@ void launch_tiles(const ProjArgs &a, hipStream_t s) {
 // stages 828 / 970; 256 x 128 or 128 x 256, 8 waves of 64 x 64, two stages
 // 801-817 / 877-882.
 constexpr int kProjBM = 256, kProjBN = 256, kProjWGM = 2, kProjWGN = 4, kProjStages = 2;
+constexpr int kProjRemBM = 64;  // M tile of the blocks that cover the last, partial N tile
 
 }  // namespace
 
@@ -280,7 +282,21 @@ hipError_t launch_in_proj(const Geom &g, int64_t M, int hidden, const void *h, c
   a.Z = g.H_v * g.D;
   a.H_v = g.H_v;
   a.N = g.C_ch + a.Z + 2 * g.H_v;
-  launch_tiles<kProjBM, kProjBN, kProjWGM, kProjWGN, kProjStages>(a, s);
+  // The full 256-column tiles, then the remaining columns (96 at the Qwen
+  // geometry) in 64-row tiles: as 256 x 256 tiles they would be a last round
+  // of blocks at the cost of a full one for a third of the work (at M = 4096,
+  // 16 such blocks after 1024 full ones on 256 compute units).
+  const int n_full = a.N / kProjBN * kProjBN;
+  if (n_full > 0) {
+    a.n_begin = 0;
+    a.n_count = n_full;
+    launch_tiles<kProjBM, kProjBN, kProjWGM, kProjWGN, kProjStages>(a, s);
+  }
+  if (n_full < a.N) {
+    a.n_begin = n_full;
+    a.n_count = a.N - n_full;
+    launch_tiles<kProjRemBM, kProjBN, kProjWGM, kProjWGN, kProjStages>(a, s);
+  }
   return hipGetLastError();
 }
 
