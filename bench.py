@@ -238,6 +238,54 @@ def hybrid_leg(args, gdn, torch, np, dev, T):
         ms_sdpa = timed(sdpa, reps)
     except RuntimeError:  # pragma: no cover
         ms_sdpa = None
+    # Decode side: one token through the block's token mixing at context T (3
+    # GDN decode steps and one attention step at position T over the cached
+    # T positions), captured as one graph and replayed.  The projections of a
+    # decode step are weight-streaming GEMVs outside this path and are not
+    # in it.
+    gd = Geometry(B=1, T=1, H_k=16, H_v=48, d_k=128, d_v=128, zero_state=False)
+    Id = make_inputs(gd, seed=70)
+    dd = gdn.Dims(B=1, H_k=16, H_v=48, d_k=128, d_v=128, in_dtype=gdn.BF16, out_dtype=gdn.BF16)
+    dls = []
+    for li in range(3):
+        Dd = {k: dev(v) for k, v in Id.items()}
+        Dd["y"] = torch.empty((1, 48, 128), dtype=torch.bfloat16, device="cuda")
+        Dd["ws"] = torch.empty(gdn.decode_workspace_bytes(dd), dtype=torch.uint8, device="cuda")
+        dls.append(Dd)
+    A1 = {k: dev(v) for k, v in make_attn_inputs(1, 1, T, T + 1, 24, 2, 256, seed=71).items()}
+    o1 = torch.empty((1, 1, 24, 256), dtype=torch.bfloat16, device="cuda")
+    aws1 = torch.empty(gdn.attn_workspace_bytes(a, 1, T), dtype=torch.uint8, device="cuda")
+
+    def dec_attn():
+        gdn.attn_prefill(a, A1["q"], A1["k"], A1["v"], A1["k_cache"], A1["v_cache"], pos0=T,
+                         o=o1, ws=aws1)
+
+    def dec_block():
+        for Dd in dls:
+            gdn.decode_step(dd, Dd["x"].reshape(1, -1), Dd["z"].reshape(1, 48, 128),
+                            Dd["g"].reshape(1, 48), Dd["beta"].reshape(1, 48), Dd["w"],
+                            Dd["hist"], Dd["S"], y=Dd["y"], ws=Dd["ws"])
+        dec_attn()
+
+    def graph_us(fn, reps=50):
+        fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    us_dec_block = graph_us(dec_block)
+    us_dec_attn = graph_us(dec_attn)
     Fa = attn_causal_flops(1, T, 0, 24, 256)
     Ba = attn_bytes(1, T, 0, 24, 2, 256, 2)
     res = {
@@ -255,11 +303,19 @@ def hybrid_leg(args, gdn, torch, np, dev, T):
                          "alg_flops_per_call": int(Fa), "alg_bytes_per_call": int(Ba)},
             "torch_sdpa_us": None if ms_sdpa is None else round(ms_sdpa * 1e3, 1),
         },
+        "decode": {
+            "workload": f"one token at context {T}: 3 GDN decode steps (B=1, bf16 y) + 1 "
+                        f"attention step over {T} cached positions, one graph replayed",
+            "us_per_token": round(us_dec_block, 2),
+            "us_attention_step": round(us_dec_attn, 2),
+            "attention_kv_bytes": int(2 * T * 2 * 256 * 2),
+        },
     }
     log(f"[bench] hybrid block T={T}: {ms_block * 1e3:.0f} us ({T / ms_block * 1e-3:.2f} M tokens/s); "
         f"GDN layer {ms_gdn * 1e3:.0f} us, attention {ms_attn * 1e3:.0f} us = "
-        f"{Fa / ms_attn / 1e9:.0f} TFLOP/s (torch sdpa {res['attention']['torch_sdpa_us']} us)")
-    del layers, A, o, aws, qt, kt, vt
+        f"{Fa / ms_attn / 1e9:.0f} TFLOP/s (torch sdpa {res['attention']['torch_sdpa_us']} us); "
+        f"decode token {us_dec_block:.1f} us (attention step {us_dec_attn:.1f} us)")
+    del layers, A, o, aws, qt, kt, vt, dls, A1
     torch.cuda.empty_cache()
     return res
 
