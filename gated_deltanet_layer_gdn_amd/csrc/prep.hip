@@ -87,7 +87,7 @@ __device__ __forceinline__ void roll_history(int C_ch, int64_t T, int b, int c0,
   }
 }
 
-template <int D, int C>
+template <int D, int C, bool STAGE>
 __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, PrefillWs L,
                                                    const float *__restrict__ gl,
                                                    const float *__restrict__ beta,
@@ -98,7 +98,13 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
   constexpr int NT = Sh::NT, NTRI = Sh::NTRI, Dp = Sh::Dp, Cp = Sh::Cp;
   __shared__ float KK[NTRI][256];  // Gram tiles, row-major 16 x 16
   __shared__ float QK[NTRI][256];
-  __shared__ float TI[NTRI][256];  // A, then (I + A)^{-1} in place
+  // A, then (I + A)^{-1} in place; before that (STAGE, chunks of at most 64
+  // tokens), the chunk's K tiles as MFMA operands (hi and lo, bf16).
+  constexpr bool kStageK = STAGE && C <= 64;
+  constexpr size_t kTiBytes = sizeof(float) * NTRI * 256;
+  constexpr size_t kStageBytes = kStageK ? size_t(2) * NT * 16 * Dp * 2 : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char ti_raw[kTiBytes > kStageBytes ? kTiBytes : kStageBytes];
+  float (*TI)[256] = reinterpret_cast<float (*)[256]>(ti_raw);
   __shared__ float Gs[C], Bs[C];
 
   const int chunk = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
@@ -121,10 +127,14 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
       roll_history(g.C_ch, L.T, b, c0, c1, static_cast<const uint16_t *>(x), static_cast<uint16_t *>(hist));
   }
 
-  // 1. K K^T and Q K^T, lower tiles only, split operands.  The tiles go to
-  //    the waves in contiguous runs of the column-major order (column nt,
-  //    then row mt), so a wave loads each K column tile it needs (the B
-  //    operand of both products) once, and each K and Q row tile once.
+  // 1. K K^T and Q K^T, lower tiles only, split operands.  With STAGE, K is
+  //    staged in LDS (each tile read from the workspace once; the grids of
+  //    long sequences, which are bound by HBM traffic, take this form);
+  //    otherwise the tiles go to the waves in contiguous runs of the
+  //    column-major order (column nt, then row mt), so a wave loads each K
+  //    column tile it needs (the B operand of both products) once, and each
+  //    K and Q row tile once, and the smaller LDS footprint keeps four blocks
+  //    on a compute unit.
   {
     constexpr int KS = Sh::KS_D;
     const size_t head0 = (static_cast<size_t>(b) * g.H_k + kh) * (Dp / 32);  // first 32-slice
@@ -147,39 +157,91 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
           l[ks] = load8(lo + o);
       }
     };
-    // Owner of the tile at column-major position cm.
-    auto owner = [](int cm) { return cm * 4 / NTRI; };
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int cm0 = nt * NT - nt * (nt - 1) / 2;  // column-major position of (nt, nt)
-      if (owner(cm0) > wave || owner(cm0 + NT - 1 - nt) < wave) continue;
-      u16x8 bh[KS], bl[KS];
-      load_tile(khi, klo, L.k_lo_scale, nt, bh, bl);
-#pragma unroll
-      for (int mt = nt; mt < NT; ++mt) {
-        if (owner(cm0 + mt - nt) != wave) continue;
-        u16x8 akh[KS], akl[KS], aqh[KS], aql[KS];
-        if (mt == nt) {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            akh[ks] = bh[ks];
-            akl[ks] = bl[ks];
-          }
-        } else {
-          load_tile(khi, klo, L.k_lo_scale, mt, akh, akl);
-        }
-        load_tile(qhi, qlo, L.q_lo_scale, mt, aqh, aql);
-        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kStageK) {
+      // Each wave loads token tile `wave` of K (hi, lo widened) and of Q once;
+      // K goes to LDS for the other waves.  Wave w then computes the Gram tiles
+      // of row tile w: K_w K_n^T and Q_w K_n^T for n <= w, with its own K_w
+      // and Q_w from registers and K_n from LDS (the same operands, in the
+      // same order, as tile-by-tile loads from the workspace would give).
+      // Rows of Dp bf16; the 16-byte piece p of row t sits at piece p ^ (t mod
+      // NP), so the 16 rows that one operand read touches land on distinct
+      // banks without padding.
+      typedef uint16_t KRow[Dp];
+      constexpr int NP = Dp / 8;
+      KRow *Kh = reinterpret_cast<KRow *>(ti_raw);            // [NT * 16][Dp]
+      KRow *Kl = reinterpret_cast<KRow *>(ti_raw) + NT * 16;  // low halves, bf16
+      const int sw = c & (NP - 1);
+      u16x8 akh[KS], akl[KS], aqh[KS], aql[KS];
+      if (wave < NT) {
+        load_tile(khi, klo, L.k_lo_scale, wave, akh, akl);
+        load_tile(qhi, qlo, L.q_lo_scale, wave, aqh, aql);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          kk = mfma_split3(akh[ks], akl[ks], bh[ks], bl[ks], kk);
-          qk = mfma_split3(aqh[ks], aql[ks], bh[ks], bl[ks], qk);
+          const int off = 8 * ((4 * ks + gq) ^ sw);
+          *reinterpret_cast<u16x8 *>(&Kh[16 * wave + c][off]) = akh[ks];
+          *reinterpret_cast<u16x8 *>(&Kl[16 * wave + c][off]) = akl[ks];
         }
-        const int tri = tri_index(mt, nt);
+      }
+      __syncthreads();
+      if (wave < NT) {
+        const int mt = wave;
+        for (int nt = 0; nt <= mt; ++nt) {
+          u16x8 bh[KS], bl[KS];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          KK[tri][(4 * gq + r) * 16 + c] = kk[r];
-          QK[tri][(4 * gq + r) * 16 + c] = qk[r];
+          for (int ks = 0; ks < KS; ++ks) {
+            const int off = 8 * ((4 * ks + gq) ^ sw);
+            bh[ks] = *reinterpret_cast<const u16x8 *>(&Kh[16 * nt + c][off]);
+            bl[ks] = *reinterpret_cast<const u16x8 *>(&Kl[16 * nt + c][off]);
+          }
+          f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            kk = mfma_split3(akh[ks], akl[ks], bh[ks], bl[ks], kk);
+            qk = mfma_split3(aqh[ks], aql[ks], bh[ks], bl[ks], qk);
+          }
+          const int tri = tri_index(mt, nt);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            KK[tri][(4 * gq + r) * 16 + c] = kk[r];
+            QK[tri][(4 * gq + r) * 16 + c] = qk[r];
+          }
+        }
+      }
+    } else {
+      // Owner of the tile at column-major position cm.
+      auto owner = [](int cm) { return cm * 4 / NTRI; };
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int cm0 = nt * NT - nt * (nt - 1) / 2;  // column-major position of (nt, nt)
+        if (owner(cm0) > wave || owner(cm0 + NT - 1 - nt) < wave) continue;
+        u16x8 bh[KS], bl[KS];
+        load_tile(khi, klo, L.k_lo_scale, nt, bh, bl);
+#pragma unroll
+        for (int mt = nt; mt < NT; ++mt) {
+          if (owner(cm0 + mt - nt) != wave) continue;
+          u16x8 akh[KS], akl[KS], aqh[KS], aql[KS];
+          if (mt == nt) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              akh[ks] = bh[ks];
+              akl[ks] = bl[ks];
+            }
+          } else {
+            load_tile(khi, klo, L.k_lo_scale, mt, akh, akl);
+          }
+          load_tile(qhi, qlo, L.q_lo_scale, mt, aqh, aql);
+          f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            kk = mfma_split3(akh[ks], akl[ks], bh[ks], bl[ks], kk);
+            qk = mfma_split3(aqh[ks], aql[ks], bh[ks], bl[ks], qk);
+          }
+          const int tri = tri_index(mt, nt);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            KK[tri][(4 * gq + r) * 16 + c] = kk[r];
+            QK[tri][(4 * gq + r) * 16 + c] = qk[r];
+          }
         }
       }
     }
@@ -393,11 +455,20 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
 
 // ---------------------------------------------------------------- launcher
 
+// K staged in LDS once the grid spans more than 8 blocks per compute unit:
+// a 4096-token prefill (1,024 blocks) then keeps every block resident at
+// once (37 against 47 us staged), and 65,536 tokens (16,384 blocks, bound
+// by HBM traffic) read 1.31 instead of 1.84 GB (535 against 582 us).
+constexpr int64_t kPrepStageBlocks = 8 * 256;
+
 template <int D, int C>
 static void launch_prep_t(const Geom &g, const PrefillWs &L, const float *gl, const float *beta,
                           char *ws, const void *x, void *hist, hipStream_t s) {
   dim3 grid(L.NC, g.H_k, g.B);
-  hipLaunchKernelGGL((prep_kernel<D, C>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
+  if (C <= 64 && static_cast<int64_t>(L.NC) * g.H_k * g.B > kPrepStageBlocks)
+    hipLaunchKernelGGL((prep_kernel<D, C, true>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
+  else
+    hipLaunchKernelGGL((prep_kernel<D, C, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
 }
 
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
