@@ -57,12 +57,12 @@ LEG_SOURCES = {
 MEASURED_TRAFFIC = {
     # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
     # profiles/gdn_hbm_bytes_prefill_t65536_t4096_decode.txt (sums over the leg's kernels)
-    "long64": {"sha256": "7c9a6c4487d1b89462d60b1535135688cf75956fd95d2abbbe6342d56ffc77bb",
-               "read": 5857750000, "write": 3226520000},
-    "long128": {"sha256": "7c9a6c4487d1b89462d60b1535135688cf75956fd95d2abbbe6342d56ffc77bb",
-               "read": 9667510000, "write": 7288920000},
-    "t4096": {"sha256": "7c9a6c4487d1b89462d60b1535135688cf75956fd95d2abbbe6342d56ffc77bb",
-               "read": 326740000, "write": 204550000},
+    "long64": {"sha256": "06b52ce5e3b625f0b50b34cfca2d83cdf90bdffd4f44b6018c81a99e35e5a5fa",
+               "read": 5320960000, "write": 3225470000},
+    "long128": {"sha256": "06b52ce5e3b625f0b50b34cfca2d83cdf90bdffd4f44b6018c81a99e35e5a5fa",
+               "read": 9667060000, "write": 7288920000},
+    "t4096": {"sha256": "06b52ce5e3b625f0b50b34cfca2d83cdf90bdffd4f44b6018c81a99e35e5a5fa",
+               "read": 326390000, "write": 204550000},
     "decode_b1": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
                "read": 3560000, "write": 3270000},
     "decode_b64": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
