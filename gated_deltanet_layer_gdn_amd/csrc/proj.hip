@@ -13,20 +13,26 @@
 // in fp32 (the gated delta rule's beta_t and log decay g_t = log a_t, with the
 // decay parametrised as in Gated DeltaNet's Mamba2-style gate).
 //
-// Tiling: 256 x 256 output tiles, K in steps of 64, 512 threads as 2 x 4
-// waves of 128 x 64 (8 x 4 MFMA tiles of 16 x 16, v_mfma_f32_16x16x32_bf16).
-// Both operands are K-contiguous in memory (H rows and W rows), which is the
-// MFMA operand layout (lane (g, c) supplies row c, K indices 8g .. 8g + 7),
-// so every operand read is one 16-byte LDS read.  LDS rows are padded by 16
-// bytes so that the sixteen rows one read touches land on distinct banks.
-// The tiles of K step kt + 2 are loaded into registers while the MFMAs run
-// on step kt (two register sets, double-buffered LDS, one barrier per step);
-// the staging registers are native vectors, which the compiler keeps in
-// registers (arrays of the struct-based uint4 went to scratch memory and
-// made the kernel four times slower).  Blocks are
-// numbered so that each XCD takes a contiguous range, walked in groups of 8
-// M tiles, so the blocks resident on an XCD at one time share their A and B
-// tiles through its L2.
+// Tiling.  Where C_ch and H_v d_v are multiples of 256 (the Qwen geometry:
+// 10,240 and 6,144), x and z are computed in 256 x 256 output tiles by
+// proj_dma_kernel: 512 threads as 2 x 4 waves of 128 x 64 (8 x 4 MFMA tiles of
+// 16 x 16, v_mfma_f32_16x16x32_bf16), K in steps of 32 through a ring of five
+// LDS stages (all 160 KB of the compute unit's LDS) filled by gfx950's
+// direct-to-LDS loads four steps ahead, and each step's operand fragments
+// read into registers while the previous step's MFMAs run.  Other
+// geometries, and the last 2 H_v columns (b and a), use proj_kernel, which
+// stages its tiles through registers: 256 x 256 tiles of 2 x 4 waves of
+// 128 x 64, K steps of 64, the tiles of step kt + 2 loaded into registers
+// while step kt computes (two register sets, double-buffered LDS rows padded
+// by 16 bytes against bank conflicts, one barrier per step; the staging
+// registers are native vectors, which the compiler keeps in registers:
+// arrays of the struct-based uint4 went to scratch memory and made the
+// kernel four times slower).  Both operands are K-contiguous in memory (H rows
+// and W rows), which is the MFMA operand layout (lane (g, c) supplies row c,
+// K indices 8g .. 8g + 7), so every operand read is one 16-byte LDS read.
+// Blocks are numbered so that each XCD takes a contiguous range, walked in
+// groups of 8 M tiles, so the blocks resident on an XCD at one time share
+// their A and B tiles through its L2.
 #include <utility>
 
 #include "gdn_device.h"
@@ -245,6 +251,205 @@ void proj_kernel(ProjArgs a) {
   epilogue_all(a, acc, m0 + wm + 4 * gq, n0 + wn + c, std::make_index_sequence<MI * NJ>{});
 }
 
+// Four rows of one output column into a bf16 matrix with row stride ld.
+__device__ __forceinline__ void store4_bf16(uint16_t *out, int64_t ld, int64_t M, const f32x4 &v,
+                                            int64_t m, int n) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (m + r < M) out[(m + r) * ld + n] = f32_to_bf16_bits(v[r]);
+}
+
+template <int MI, int NJ, size_t... Is>
+__device__ __forceinline__ void epilogue_bf16(uint16_t *out, int64_t ld, int64_t M,
+                                              const f32x4 (&acc)[MI][NJ], int64_t m_base,
+                                              int n_base, std::index_sequence<Is...>) {
+  (store4_bf16(out, ld, M, acc[Is / NJ][Is % NJ], m_base + 16 * static_cast<int>(Is / NJ),
+               n_base + 16 * static_cast<int>(Is % NJ)),
+   ...);
+}
+
+// ---- direct-to-LDS tiles.  gfx950's global_load_lds_dwordx4 moves 16-byte
+// pieces from memory into LDS without passing through registers, so loads can
+// run several K steps ahead at no register cost.  One such load writes a
+// wave's 64 pieces to 1 KB of consecutive LDS, lane by lane, so instead of
+// padding rows, the layout permutes the pieces within a row: a row is 32 bf16
+// (64 bytes, 4 pieces) and piece p of row r sits in slot p ^ ((r >> 2) & 3).
+// An operand read (16 lanes of one K quarter over 16 consecutive rows) then
+// touches 16 distinct 4-bank groups.  Measured side by side at M = 4096 /
+// 16,384, hidden 5120, N = 16,480 (TFLOP/s, bitwise equal results): the
+// register-staged kernel 816-896 / 1,010; direct-to-LDS with four stages
+// 966-1,064 / 1,130 and with five 995-1,082 / 1,160; four waves of 128 x 128
+// (256 accumulators each, in AGPRs) lost to the compiler's copies between
+// accumulator registers (824-879 / 931).
+constexpr int kDBK = 32;          // K per stage
+constexpr int kDStages = 5;       // LDS ring (5 x 32 KB); loads run kDStages - 1 steps ahead
+constexpr int kDRowBytes = kDBK * 2;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt vmcnt(N), other counters left at their maxima (gfx9 encoding:
+  // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+template <int BM, int BN, int WGM, int WGN>
+struct DmaShape {
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;         // wave tile
+  static constexpr int MI = WM / 16, NJ = WN / 16;
+  static constexpr int kStageBytes = (BM + BN) * kDRowBytes;  // A rows, then B rows
+  static constexpr int kLoads = (BM + BN) * kDRowBytes / 1024 / kWaves;  // 1 KB loads per wave and stage
+};
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void proj_dma_kernel(ProjArgs a) {
+  using Sh = DmaShape<BM, BN, WGM, WGN>;
+  constexpr int MI = Sh::MI, NJ = Sh::NJ, NL = Sh::kLoads;
+  __shared__ __attribute__((aligned(1024))) char lds[kDStages * Sh::kStageBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_mt = static_cast<int>((a.M + BM - 1) / BM);
+  const int n_nt = (a.n_count + BN - 1) / BN;
+  const int lid = xcd_remap_p(blockIdx.x, n_mt * n_nt);
+  const int per_group = kGroupM * n_nt;
+  const int grp = lid / per_group;
+  const int first_mt = grp * kGroupM;
+  const int gm = min(kGroupM, n_mt - first_mt);
+  const int in_grp = lid % per_group;
+  const int mt = first_mt + in_grp % gm;
+  const int nt = in_grp / gm;
+  const int64_t m0 = static_cast<int64_t>(mt) * BM;
+  const int n0 = a.n_begin + nt * BN;
+
+  // Load l of this wave covers tile rows 16 q .. 16 q + 15 (q = NL wave + l;
+  // A rows first): lane i fills row 16 q + i / 4, slot i % 4, which holds
+  // piece (i % 4) ^ ((i >> 4) & 3) of that row.  Rows past M or N re-read the
+  // last row (their products are not stored).
+  const uint16_t *src[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    const int q = NL * wave + l;
+    const int r = 16 * q + (lane >> 2);
+    const int piece = (lane & 3) ^ ((lane >> 4) & 3);
+    if (r < BM) {
+      int64_t ma = m0 + r;
+      ma = ma < a.M ? ma : a.M - 1;
+      src[l] = a.h + ma * a.K + piece * 8;
+    } else {
+      int nb = n0 + (r - BM);
+      nb = nb < a.N ? nb : a.N - 1;
+      src[l] = a.w + static_cast<int64_t>(nb) * a.K + piece * 8;
+    }
+  }
+  auto issue = [&](int stage, int k0) {
+    char *base = lds + stage * Sh::kStageBytes + NL * wave * 1024;
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
+      __builtin_amdgcn_global_load_lds((glb_void_t *)(src[l] + k0), (lds_void_t *)(base + 1024 * l),
+                                       16, 0, 0);
+  };
+
+  const int wm = (wave / WGN) * Sh::WM, wn = (wave % WGN) * Sh::WN;
+  const int c = lane & 15, gq = lane >> 4;
+  const int slot_off = 16 * (gq ^ (c >> 2));  // this lane's piece within its row
+  f32x4 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = a.K / kDBK;
+  // Fragments of one K step: the A operands of the wave's MI row tiles and the
+  // B operands of its NJ column tiles.
+  auto read_frags = [&](int stage, u16x8 (&av)[MI], u16x8 (&bv)[NJ]) {
+    const char *A = lds + stage * Sh::kStageBytes;
+    const char *B = A + BM * kDRowBytes;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      av[i] = *reinterpret_cast<const u16x8 *>(A + (wm + 16 * i + c) * kDRowBytes + slot_off);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      bv[j] = *reinterpret_cast<const u16x8 *>(B + (wn + 16 * j + c) * kDRowBytes + slot_off);
+  };
+  auto mma = [&](const u16x8 (&av)[MI], const u16x8 (&bv)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(av[i], bv[j], acc[i][j]);
+  };
+  // Step kt: wait for stage kt + 1 and publish it; refill the slot of stage
+  // kt, whose fragments are already in registers, with stage kt + S (S
+  // stages in the ring); read stage kt + 1's fragments into the other
+  // register set while the MFMAs of step kt run.  Steps of the main loop all
+  // do the same (kt + S < nk); the last ones are peeled.
+  auto publish_next = [&](int kt) {
+    // loads still in flight after stage kt + 1's: stages kt + 2 .. min(nk - 1, kt + S - 1)
+    const int ahead = min(nk - 1, kt + kDStages - 1) - (kt + 1);
+    if (ahead >= 3) wait_vm<3 * NL>();
+    else if (ahead == 2) wait_vm<2 * NL>();
+    else if (ahead == 1) wait_vm<NL>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
+    __builtin_amdgcn_s_barrier();
+  };
+  auto step_full = [&](int kt, const u16x8 (&av)[MI], const u16x8 (&bv)[NJ], u16x8 (&an)[MI],
+                       u16x8 (&bn)[NJ]) {
+    wait_vm<(kDStages - 2) * NL>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    issue(kt % kDStages, (kt + kDStages) * kDBK);
+    read_frags((kt + 1) % kDStages, an, bn);
+    mma(av, bv);
+  };
+  auto step_tail = [&](int kt, const u16x8 (&av)[MI], const u16x8 (&bv)[NJ], u16x8 (&an)[MI],
+                       u16x8 (&bn)[NJ]) {
+    if (kt + 1 < nk) {
+      publish_next(kt);
+      if (kt + kDStages < nk) issue(kt % kDStages, (kt + kDStages) * kDBK);
+      read_frags((kt + 1) % kDStages, an, bn);
+    }
+    mma(av, bv);
+  };
+
+#pragma unroll
+  for (int st = 0; st < kDStages; ++st)
+    if (st < nk) issue(st, st * kDBK);
+  publish_next(-1);  // stage 0
+  u16x8 a0[MI], b0[NJ], a1[MI], b1[NJ];
+  read_frags(0, a0, b0);
+  int kt = 0;
+  for (; kt + kDStages + 1 < nk; kt += 2) {  // nk is even (K is a multiple of 64)
+    step_full(kt, a0, b0, a1, b1);
+    step_full(kt + 1, a1, b1, a0, b0);
+  }
+  for (; kt < nk; kt += 2) {
+    step_tail(kt, a0, b0, a1, b1);
+    step_tail(kt + 1, a1, b1, a0, b0);
+  }
+
+  // The launch covers whole tiles of x or of z only (C_ch and H_v d_v are
+  // multiples of BN), so a tile stores bf16 to one output, chosen per block.
+  const int64_t mb = m0 + wm + 4 * gq;
+  constexpr auto seq = std::make_index_sequence<MI * NJ>{};
+  if (n0 < a.C_ch)
+    epilogue_bf16(a.x, a.C_ch, a.M, acc, mb, n0 + wn + c, seq);
+  else
+    epilogue_bf16(a.z, a.Z, a.M, acc, mb, n0 - a.C_ch + wn + c, seq);
+}
+
+template <int BM, int BN, int WGM, int WGN>
+void launch_dma_tiles(const ProjArgs &a, hipStream_t s) {
+  const int64_t n_mt = (a.M + BM - 1) / BM;
+  const int64_t n_nt = (a.n_count + BN - 1) / BN;
+  hipLaunchKernelGGL((proj_dma_kernel<BM, BN, WGM, WGN>), dim3(static_cast<unsigned>(n_mt * n_nt)),
+                     dim3(DmaShape<BM, BN, WGM, WGN>::kThreads), 0, s, a);
+}
+
 template <int BM, int BN, int WGM, int WGN, int STAGES>
 void launch_tiles(const ProjArgs &a, hipStream_t s) {
   const int64_t n_mt = (a.M + BM - 1) / BM;
@@ -261,6 +466,7 @@ void launch_tiles(const ProjArgs &a, hipStream_t s) {
 // 801-817 / 877-882.
 constexpr int kProjBM = 256, kProjBN = 256, kProjWGM = 2, kProjWGN = 4, kProjStages = 2;
 constexpr int kProjRemBM = 64;  // M tile of the blocks that cover the last, partial N tile
+constexpr int kDmaWGM = 2, kDmaWGN = 4;  // waves of the direct-to-LDS kernel (M x N)
 
 }  // namespace
 
@@ -286,8 +492,15 @@ hipError_t launch_in_proj(const Geom &g, int64_t M, int hidden, const void *h, c
   // geometry) in 64-row tiles: as 256 x 256 tiles they would be a last round
   // of blocks at the cost of a full one for a third of the work (at M = 4096,
   // 16 such blocks after 1024 full ones on 256 compute units).
-  const int n_full = a.N / kProjBN * kProjBN;
-  if (n_full > 0) {
+  int n_full = a.N / kProjBN * kProjBN;
+  if (a.C_ch % kProjBN == 0 && a.Z % kProjBN == 0) {
+    // x and z in whole 256-column tiles on the direct-to-LDS kernel; b and a
+    // (2 H_v columns) below with the remainder.
+    n_full = a.C_ch + a.Z;
+    a.n_begin = 0;
+    a.n_count = n_full;
+    launch_dma_tiles<kProjBM, kProjBN, kDmaWGM, kDmaWGN>(a, s);
+  } else if (n_full > 0) {
     a.n_begin = 0;
     a.n_count = n_full;
     launch_tiles<kProjBM, kProjBN, kProjWGM, kProjWGN, kProjStages>(a, s);

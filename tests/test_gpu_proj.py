@@ -68,6 +68,20 @@ def test_in_proj_small(B, T, hidden):
     check_proj(f"in_proj B={B} T={T} hidden={hidden}", got, ref)
 
 
+# Other head counts: C_ch = 640 (H_k=1, H_v=3) is not a multiple of 256, so
+# the register-staged tiles cover x and z (one tile holds both); at H_k=2,
+# H_v=4 (C_ch = 1024, H_v d_v = 512) the direct-to-LDS tiles do, with K = 192
+# and 320 (six and ten K steps: the pipeline's peeled last steps).
+@pytest.mark.parametrize("H_k,H_v,T,hidden", [(1, 3, 70, 192), (2, 4, 300, 320), (1, 3, 257, 64)])
+def test_in_proj_other_head_counts(H_k, H_v, T, hidden):
+    geom = Geometry(B=1, T=T, H_k=H_k, H_v=H_v, d_k=128, d_v=128)
+    P = make_proj_inputs(1, T, hidden, H_k, H_v, 128, seed=730 + T)
+    got = run_proj(dims_of(geom), P)
+    x, z, g, beta = oracle_proj(P, H_k, H_v, 128)
+    ref = (x, z.reshape(1, T, H_v, 128), g, beta)
+    check_proj(f"in_proj H={H_k}/{H_v} T={T} hidden={hidden}", got, ref)
+
+
 def test_in_proj_qwen_size_sampled_rows():
     # M = 4096 tokens, hidden 5120 (the pages' hidden size), all 16,480
     # output columns; the oracle computes 96 sampled token rows.
