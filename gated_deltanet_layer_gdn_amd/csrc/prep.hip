@@ -87,7 +87,196 @@ __device__ __forceinline__ void roll_history(int C_ch, int64_t T, int b, int c0,
   }
 }
 
-template <int D, int C, bool STAGE>
+// Value heads processed in parallel by the per-wave form of the kernel (one
+// head per wave, waves 0 .. kHeadSlots - 1; each head's inverse in a slot of
+// its own in LDS).
+constexpr int kHeadSlots = 3;
+
+// One value head h of one chunk (C <= 64), computed by one wave: the gate
+// table, A, Tm = (I + A)^{-1} in place in TI (the head's NTRI tiles), and the
+// stores of Tm and P.  The operations and their order are those of the
+// four-wave form in prep_kernel, entry by entry, so the results are the same
+// to the bit; G_t and beta_t stay in registers (lane t) and are read with
+// shuffles instead of from LDS.  All of it runs in one wave, whose LDS
+// accesses complete in program order, so the steps need no block barrier
+// (the compiler barriers below keep it from moving LDS accesses across
+// steps).
+template <int D, int C>
+__device__ __forceinline__ void prep_head_wave(const Geom &g, const PrefillWs &L,
+                                               const float *__restrict__ gl,
+                                               const float *__restrict__ beta, char *__restrict__ ws,
+                                               const float (*KK)[256], const float (*QK)[256],
+                                               float (*TI)[256], int b, int h, int chunk,
+                                               int64_t tau0, int n_valid) {
+  using Sh = PrepShape<D, C>;
+  constexpr int NT = Sh::NT, NTRI = Sh::NTRI, Cp = Sh::Cp;
+  static_assert(C <= 64, "one token per lane");
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g4 = lane >> 4;
+
+  // Lane t: G_t, the prefix sum of the log decay, and beta_t (0 past the end).
+  float g0, g1;
+  const size_t base = (static_cast<size_t>(b) * L.T + tau0) * g.H_v + h;
+  chunk_prefix<C>(gl, base, g.H_v, n_valid, g0, g1);
+  const float b0 = (lane < C && lane < n_valid) ? beta[base + static_cast<size_t>(lane) * g.H_v] : 0.f;
+  const float g_last = __shfl(g0, C - 1, kWave);
+
+  // Gate factors of this chunk for the state pass.
+  if constexpr (D == 128 && C == 64) {
+    float4 *gt = reinterpret_cast<float4 *>(ws + L.gates) +
+                 ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C;
+    gt[lane] = make_float4(__expf(g0), __expf(g_last - g0), b0, __expf(g_last));
+  } else {
+    float *gt = reinterpret_cast<float *>(ws + L.gates) +
+                ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * 3 * C;
+    if (lane < C) {
+      gt[lane] = __expf(g0);
+      gt[C + lane] = __expf(g_last - g0);
+      gt[2 * C + lane] = b0;
+    }
+  }
+
+  // (a) A[t][s] = beta_t exp(G_t - G_s) KK[t][s] for s < t, tile by tile.
+#pragma unroll
+  for (int tri = 0; tri < NTRI; ++tri) {
+    int mt = 0;
+    while (tri_index(mt + 1, 0) <= tri) ++mt;
+    const int nt = tri - tri_index(mt, 0);
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int e = lane + 64 * e4;
+      const int t = 16 * mt + (e >> 4), sc = 16 * nt + (e & 15);
+      const float bt = __shfl(b0, t, kWave), gtv = __shfl(g0, t, kWave), gsv = __shfl(g0, sc, kWave);
+      TI[tri][e] = sc < t ? bt * __expf(gtv - gsv) * KK[tri][e] : 0.f;
+    }
+  }
+  asm volatile("" ::: "memory");
+  // (b) diagonal blocks X_ii = (I + A_ii)^{-1} by forward substitution, one
+  //     lane per column (block lane / 16, column lane % 16).
+  if (lane < NT * 16) {
+    const int blk = lane >> 4, col = lane & 15;
+    const float *Ad = TI[tri_index(blk, blk)];
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < r; ++k) acc = __builtin_fmaf(Ad[r * 16 + k], x[k], acc);
+      x[r] = (r == col ? 1.f : 0.f) - acc;
+    }
+    float *Xd = TI[tri_index(blk, blk)];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Xd[r * 16 + col] = x[r];
+  }
+  asm volatile("" ::: "memory");
+  if constexpr (NT > 1) {
+    auto prod = [&](const float *A, const float *Bm, f32x4 acc) {
+      const float4 av = *reinterpret_cast<const float4 *>(A + c * 16 + 4 * g4);
+      const float a4[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[st], Bm[(4 * g4 + st) * 16 + c], acc, 0, 0, 0);
+      return acc;
+    };
+    // (c) Y_ik = X_ii A_ik in place of A_ik.
+#pragma unroll
+    for (int i = 1; i < NT; ++i)
+#pragma unroll
+      for (int k = 0; k < i; ++k) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 y = prod(TI[tri_index(i, i)], TI[tri_index(i, k)], zero);
+        float *dst = TI[tri_index(i, k)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(4 * g4 + r) * 16 + c] = y[r];
+        asm volatile("" ::: "memory");
+      }
+    // (d) block row i: X_ij = -sum_{k=j}^{i-1} Y_ik X_kj for j < i; the whole
+    //     row is read before any of it is written.
+#pragma unroll
+    for (int i = 1; i < NT; ++i) {
+      f32x4 xr[NT - 1];
+#pragma unroll
+      for (int j = 0; j < i; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = j; k < i; ++k) acc = prod(TI[tri_index(i, k)], TI[tri_index(k, j)], acc);
+        xr[j] = acc;
+      }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < i; ++j) {
+        float *dst = TI[tri_index(i, j)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(4 * g4 + r) * 16 + c] = -xr[j][r];
+      }
+      asm volatile("" ::: "memory");
+    }
+  }
+
+  // (e) Tm (bf16) and P (hi/lo) as A operands, as in the four-wave form.
+  const size_t mat = ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C * Cp;
+  uint16_t *Tm = reinterpret_cast<uint16_t *>(ws + L.Tm) + mat;
+  uint16_t *Ph = reinterpret_cast<uint16_t *>(ws + L.P_hi) + mat;
+  uint16_t *Pl = reinterpret_cast<uint16_t *>(ws + L.P_lo) + mat;
+  constexpr bool kLo8 = D == 128 && C == 64;
+  uint8_t *Pl8 = reinterpret_cast<uint8_t *>(ws + L.P_lo) + mat;
+  constexpr int ITEMS = kLo8 ? 384 : C * (Cp / 32) * 4;
+  static_assert(ITEMS % 64 == 0, "every lane takes the same number of items");
+  for (int it = lane; it < ITEMS; it += 64) {
+    int t, kk, q;
+    if constexpr (kLo8) {
+      kk = it >> 8;
+      t = 32 * kk + ((it & 255) >> 2);
+      q = it & 3;
+    } else {
+      t = it / (Cp / 8);
+      const int rem = it % (Cp / 8);
+      kk = rem >> 2;
+      q = rem & 3;
+    }
+    const float gtv = __shfl(g0, t & 63, kWave);
+    u16x8 tv8;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sc = 32 * kk + (i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4));
+      const float gsv = __shfl(g0, sc & 63, kWave);
+      float tv = 0.f;
+      pv[i] = 0.f;
+      if (sc < C && sc <= t) {
+        const int tr = tri_index(t >> 4, sc >> 4), off = (t & 15) * 16 + (sc & 15);
+        tv = TI[tr][off];
+        pv[i] = __expf(gtv - gsv) * QK[tr][off];
+      }
+      tv8[i] = f32_to_bf16_bits(tv);
+    }
+    const size_t o = static_cast<size_t>(t) * Cp + 32 * kk + 8 * q;
+    *reinterpret_cast<u16x8 *>(Tm + o) = tv8;
+    if constexpr (kLo8) {
+      uint32_t hh[4];
+      uint16_t ll[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split2_lo8(pv[2 * i], pv[2 * i + 1], L.q_lo_scale, hh[i], ll[i]);
+      const u32x4 hv = {hh[0], hh[1], hh[2], hh[3]};
+      *reinterpret_cast<u16x8 *>(Ph + o) = __builtin_bit_cast(u16x8, hv);
+      *reinterpret_cast<uint2 *>(Pl8 + o) =
+          make_uint2(ll[0] | (static_cast<uint32_t>(ll[1]) << 16), ll[2] | (static_cast<uint32_t>(ll[3]) << 16));
+    } else {
+      u16x8 ph8, pl8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint16_t hi, lo;
+        split_bf16(pv[i], hi, lo);
+        ph8[i] = hi;
+        pl8[i] = lo;
+      }
+      *reinterpret_cast<u16x8 *>(Ph + o) = ph8;
+      *reinterpret_cast<u16x8 *>(Pl + o) = pl8;
+    }
+  }
+}
+
+template <int D, int C, bool STAGE, bool PERWAVE>
 __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, PrefillWs L,
                                                    const float *__restrict__ gl,
                                                    const float *__restrict__ beta,
@@ -101,11 +290,12 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
   // A, then (I + A)^{-1} in place; before that (STAGE, chunks of at most 64
   // tokens), the chunk's K tiles as MFMA operands (hi and lo, bf16).
   constexpr bool kStageK = STAGE && C <= 64;
-  constexpr size_t kTiBytes = sizeof(float) * NTRI * 256;
+  constexpr size_t kTiBytes = sizeof(float) * NTRI * 256 * (PERWAVE ? kHeadSlots : 1);
   constexpr size_t kStageBytes = kStageK ? size_t(2) * NT * 16 * Dp * 2 : 0;
   __shared__ __attribute__((aligned(16))) unsigned char ti_raw[kTiBytes > kStageBytes ? kTiBytes : kStageBytes];
   float (*TI)[256] = reinterpret_cast<float (*)[256]>(ti_raw);
-  __shared__ float Gs[C], Bs[C];
+  // the four-wave form's gate prefix and beta (the per-wave form keeps them in registers)
+  __shared__ float Gs[PERWAVE ? 1 : C], Bs[PERWAVE ? 1 : C];
 
   const int chunk = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -247,6 +437,17 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
     }
   }
 
+  if constexpr (PERWAVE) {
+    // Value heads in parallel, one per wave (wave w: heads w, w + 3, ...),
+    // each in its own slot of TI.
+    static_assert(C <= 64, "per-wave heads need C <= 64");
+    __syncthreads();  // Gram tiles written; the K staging (aliased with TI) no longer read
+    if (wave < kHeadSlots)
+      for (int jv = wave; jv < g.G; jv += kHeadSlots)
+        prep_head_wave<D, C>(g, L, gl, beta, ws, KK, QK, TI + wave * NTRI, b, kh * g.G + jv, chunk,
+                             tau0, n_valid);
+    return;
+  } else {
   for (int jv = 0; jv < g.G; ++jv) {
     const int h = kh * g.G + jv;
     __syncthreads();  // Gram tiles written; previous head's readers done
@@ -451,6 +652,7 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
       }
     }
   }
+  }
 }
 
 // ---------------------------------------------------------------- launcher
@@ -465,10 +667,21 @@ template <int D, int C>
 static void launch_prep_t(const Geom &g, const PrefillWs &L, const float *gl, const float *beta,
                           char *ws, const void *x, void *hist, hipStream_t s) {
   dim3 grid(L.NC, g.H_k, g.B);
-  if (C <= 64 && static_cast<int64_t>(L.NC) * g.H_k * g.B > kPrepStageBlocks)
-    hipLaunchKernelGGL((prep_kernel<D, C, true>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
+  const bool stage = C <= 64 && static_cast<int64_t>(L.NC) * g.H_k * g.B > kPrepStageBlocks;
+  if constexpr (C <= 64) {
+    if (stage && g.G >= 2) {
+      // Value heads one per wave: 511-517 against 543-571 us at T = 65,536
+      // (bitwise equal).  Smaller grids keep the four-wave form, whose
+      // smaller LDS footprint keeps four blocks per compute unit (35 against
+      // 41 us at T = 4096).
+      hipLaunchKernelGGL((prep_kernel<D, C, true, true>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
+      return;
+    }
+  }
+  if (stage)
+    hipLaunchKernelGGL((prep_kernel<D, C, true, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
   else
-    hipLaunchKernelGGL((prep_kernel<D, C, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
+    hipLaunchKernelGGL((prep_kernel<D, C, false, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
 }
 
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,

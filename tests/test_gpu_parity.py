@@ -72,14 +72,18 @@ def test_prefill_head_groupings(H_k, H_v, B):
     check_layer(f"heads {H_k}/{H_v} B={B} 150 decode steps", gpu_decode_seq(geom, I), ref)
 
 
-@pytest.mark.parametrize("B,T,dtype", [(2, 4500, "bf16"), (3, 2800, "f32")])
-def test_prefill_prep_staged(B, T, dtype):
+@pytest.mark.parametrize("B,T,dtype,H_k,H_v", [(2, 4500, "bf16", 16, 48), (3, 2800, "f32", 16, 48),
+                                                (1, 70000, "bf16", 2, 8), (1, 33000, "bf16", 4, 8)])
+def test_prefill_prep_staged(B, T, dtype, H_k, H_v):
     # Grids of more than 2048 prep blocks (chunks x key heads x sequences)
-    # stage K in LDS: ragged T, several sequences, both input dtypes.
-    geom = Geometry(B=B, T=T, H_k=16, H_v=48, d_k=128, d_v=128, zero_state=False, dtype=dtype)
-    assert -(-T // 64) * 16 * B > 2048
+    # stage K in LDS and compute the value heads one per wave (wave w: heads
+    # w, w + 3, ...): ragged T, several sequences, both input dtypes, three,
+    # four (one wave takes two heads) and two value heads per key head.
+    geom = Geometry(B=B, T=T, H_k=H_k, H_v=H_v, d_k=128, d_v=128, zero_state=False, dtype=dtype)
+    assert -(-T // 64) * H_k * B > 2048
     I = make_inputs(geom, seed=160 + B)
-    check_layer(f"prep staged B={B} T={T} {dtype}", gpu_prefill(geom, I, 64), oracle_run(geom, I))
+    check_layer(f"prep staged B={B} T={T} {dtype} heads {H_k}/{H_v}", gpu_prefill(geom, I, 64),
+                oracle_run(geom, I))
 
 
 @pytest.mark.parametrize("chunk", [64, 128])
