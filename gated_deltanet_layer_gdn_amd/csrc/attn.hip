@@ -453,7 +453,11 @@ AttnPlan attn_plan(const AttnGeom &a, int64_t T, int64_t pos0) {
   }
   pl.tps = (n_kv + split - 1) / split;
   pl.n_split = (n_kv + pl.tps - 1) / pl.tps;
+  // the RoPE table, at least 256 bytes: a valid call never reports a zero
+  // workspace size (zero means invalid arguments), even without rotation
+  // and without KV splits
   pl.cs_bytes = (static_cast<size_t>(T) * (a.rot / 2) * 8 + 255) / 256 * 256;
+  if (pl.cs_bytes < 256) pl.cs_bytes = 256;
   const size_t rows = static_cast<size_t>(pl.n_split) * a.B * a.H_kv * pl.rows_pad;
   pl.part_o_bytes = pl.n_split > 1 ? (rows * a.D * 4 + 255) / 256 * 256 : 0;
   pl.part_ml_bytes = pl.n_split > 1 ? (rows * 2 * 4 + 255) / 256 * 256 : 0;

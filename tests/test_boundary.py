@@ -273,6 +273,10 @@ def test_attn_rejects_and_leaves_buffers_untouched(lib):
     assert need >= T * 16 * 8  # RoPE cos/sin table (+ split partials)
     assert lib.gdn_attn_workspace_bytes(ctypes.byref(a), 0, 0) == 0
     assert lib.gdn_attn_workspace_bytes(ctypes.byref(a), 1 << 22, 0) == 0  # launch size limit
+    # no rotation and no KV split (one block of rows): still a non-zero size,
+    # since zero means invalid arguments
+    a0 = _lib.GdnAttnDims(_lib.ABI_VERSION, 1, 4, 1, 256, 0, 1, 1, 1e7, 256 ** -0.5)
+    assert lib.gdn_attn_workspace_bytes(ctypes.byref(a0), 4, 60) > 0
     rng = np.random.default_rng(0)
     mk = lambda n: rng.integers(0, 255, n, dtype=np.uint8)
     bufs = dict(q=mk(B * T * H_q * d * 2 + 64), k=mk(B * T * H_kv * d * 2 + 64),

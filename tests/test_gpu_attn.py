@@ -184,3 +184,26 @@ def test_attn_split_kv_after_long_context(B, pos0, T):
     ref, kr, vr = oracle_call(I, pos0, a)
     check_out(f"attn split B={B} pos0={pos0} T={T}", o, ref, TOL_F32)
     check_cache("cache", kc, vc, kr, vr, pos0, T, I["k"], a)
+
+
+# Decode-shaped calls: a few query rows per KV head after a cached context
+# (a decode token, a short MTP step), through the split KV pass and the
+# combine, or one block when the context is short.
+@pytest.mark.parametrize("B,pos0,T,H_q,H_kv,d,rot,out_bf16", [
+    (1, 0, 1, 24, 2, 256, 64, False),       # the first token: one position
+    (2, 15, 1, 24, 2, 256, 64, False),      # a context of 16 positions
+    (3, 4113, 1, 24, 2, 256, 64, False),    # 65 KV tiles, a ragged last one
+    (1, 100000, 1, 24, 2, 256, 64, False),  # 1,563 KV tiles over the largest split count
+    (2, 37, 8, 8, 8, 128, 128, False),      # G = 1, 8 new tokens, rotation over the whole head
+    (1, 60, 4, 4, 1, 256, 0, True),         # no rotation, no split: the smallest workspace
+    (1, 62, 4, 4, 1, 256, 64, False),       # new tokens across a KV tile boundary
+    (2, 300, 1, 12, 1, 128, 32, True),      # d = 128, one KV head
+])
+def test_attn_decode_path(B, pos0, T, H_q, H_kv, d, rot, out_bf16):
+    a = attn_dims(B, H_q, H_kv, d, rot, 1e7 if d == 256 else 1e4, out_bf16)
+    I = make_attn_inputs(B, T, pos0, pos0 + T + 2, H_q, H_kv, d, seed=990 + pos0 % 97 + T)
+    o, kc, vc = run_gpu(a, I, pos0)
+    ref, kr, vr = oracle_call(I, pos0, a)
+    check_out(f"attn decode B={B} pos0={pos0} T={T} H={H_q}/{H_kv} d={d} r={rot}", o, ref,
+              TOL_BF16 if out_bf16 else TOL_F32)
+    check_cache("cache", kc, vc, kr, vr, pos0, T, I["k"], a)
