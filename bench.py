@@ -57,12 +57,12 @@ LEG_SOURCES = {
 MEASURED_TRAFFIC = {
     # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
     # profiles/gdn_hbm_bytes_prefill_t65536_t4096_decode.txt (sums over the leg's kernels)
-    "long64": {"sha256": "06b52ce5e3b625f0b50b34cfca2d83cdf90bdffd4f44b6018c81a99e35e5a5fa",
-               "read": 5320960000, "write": 3225470000},
-    "long128": {"sha256": "06b52ce5e3b625f0b50b34cfca2d83cdf90bdffd4f44b6018c81a99e35e5a5fa",
-               "read": 9667060000, "write": 7288920000},
-    "t4096": {"sha256": "06b52ce5e3b625f0b50b34cfca2d83cdf90bdffd4f44b6018c81a99e35e5a5fa",
-               "read": 326390000, "write": 204550000},
+    "long64": {"sha256": "0803121fc887610f726409d69a7aaf71e6ced6f81758d36aac022b325d079329",
+               "read": 5104550000, "write": 3292410000},
+    "long128": {"sha256": "0803121fc887610f726409d69a7aaf71e6ced6f81758d36aac022b325d079329",
+               "read": 9667140000, "write": 7288920000},
+    "t4096": {"sha256": "0803121fc887610f726409d69a7aaf71e6ced6f81758d36aac022b325d079329",
+               "read": 327990000, "write": 204560000},
     "decode_b1": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
                "read": 3560000, "write": 3270000},
     "decode_b64": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
