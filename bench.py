@@ -133,6 +133,157 @@ def decode_step_bytes_per_seq(C_ch, H_v, d_k, d_v, in_bytes, out_bytes):
             + 2 * 3 * C_ch * in_bytes + C_ch * in_bytes)
 
 
+def serving_legs(args, gdn, torch, np):
+    """The serving shapes and the output epilogue, each against the HBM
+    roofline (all HBM-bound):
+    * an MTP verify step (gdn_decode_multi): B = 64 sequences, T = 3 tokens,
+      the state after every token stored to a slot of its own, graph-replayed
+      over rotated slot groups so the state sets exceed the 256 MB Infinity
+      Cache; algorithmic bytes per sequence: the fp32 state read once and
+      written T times, the conv history likewise, T tokens of x, z, g, beta
+      and y;
+    * a packed variable-length prefill (gdn_prefill_varlen) of 8 sequences of
+      mixed lengths (4096 .. 129 tokens, 10,422 in all) from zero states,
+      chunk 64: the prefill's algorithmic bytes per token plus each sequence's
+      state in and out;
+    * the zero-centred grouped RMS norm and gate (gdn_gated_rmsnorm) over the
+      ungated readout of 4096 tokens: fp32 o and bf16 z read, bf16 y written.
+    Inputs are seeded draws of the layer's laws (x, z ~ N(0, 1) bf16, g =
+    -softplus(N(0, 1)), beta = sigmoid(N(0, 1)), conv weights ~ N(0, 0.5^2),
+    states ~ N(0, 0.1^2))."""
+    H_k, H_v, d = 16, 48, 128
+    C_ch = 2 * H_k * d + H_v * d
+    st_bytes = H_v * d * d * 4
+    hist_bytes = 3 * C_ch * 2
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8)
+    nrm = lambda *shape: torch.randn(*shape, device="cuda", generator=gen)
+    out = {}
+
+    # MTP verify step
+    B, T = 64, 3
+    dm = gdn.Dims(B=B, H_k=H_k, H_v=H_v, d_k=d, d_v=d, in_dtype=gdn.BF16, out_dtype=gdn.F32)
+    per_group = B * (1 + T)
+    R = max(2, math.ceil(ROTATE_BYTES / (B * st_bytes)))
+    n_slots = R * per_group
+    rec_pool = 0.1 * nrm(n_slots, H_v, d, d)
+    conv_pool = nrm(n_slots, 3, C_ch).bfloat16()
+    x = nrm(B, T, C_ch).bfloat16()
+    z = nrm(B, T, H_v, d).bfloat16()
+    g = -torch.nn.functional.softplus(nrm(B, T, H_v))
+    beta = torch.sigmoid(nrm(B, T, H_v))
+    w = (0.5 * nrm(C_ch, 4)).bfloat16()
+    y = torch.empty(B, T, H_v, d, device="cuda")
+    ws = torch.empty(T * gdn.decode_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
+    ins = [torch.arange(r * per_group, r * per_group + B, dtype=torch.int32, device="cuda")
+           for r in range(R)]
+    outs = [torch.arange(r * per_group + B, (r + 1) * per_group, dtype=torch.int32,
+                         device="cuda").reshape(B, T) for r in range(R)]
+
+    def mstep(r):
+        gdn.decode_multi(dm, x, z, g, beta, w, conv_pool, rec_pool, ins[r], outs[r], y=y, ws=ws)
+
+    for r in range(R):
+        mstep(r)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(R):
+            mstep(r)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.decode_rounds):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (args.decode_rounds * R)
+    tok_bytes = C_ch * 2 + H_v * d * 2 + 2 * H_v * 4 + H_v * d * 4
+    mb = B * ((1 + T) * (st_bytes + hist_bytes) + T * tok_bytes)
+    out["mtp_verify"] = {
+        "workload": f"gdn_decode_multi B={B} T={T}, the state after each token to its own slot, "
+                    f"16/48 heads d=128, bf16 in, fp32 y; {R} slot groups rotated, one graph",
+        "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(mb / (ms * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(mb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "alg_bytes_per_step": int(mb)}}
+    log(f"[bench] mtp verify B={B} T={T}: {ms * 1e3:.1f} us/step = "
+        f"{mb / (ms * 1e-3) / 1e9:.0f} GB/s of algorithmic bytes")
+    del rec_pool, conv_pool, graph
+
+    # packed variable-length prefill
+    lens = [4096, 2048, 1536, 1024, 777, 512, 300, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    Tt = int(cu[-1])
+    dv = gdn.Dims(B=len(lens), H_k=H_k, H_v=H_v, d_k=d, d_v=d, in_dtype=gdn.BF16, out_dtype=gdn.F32)
+    xv = nrm(Tt, C_ch).bfloat16()
+    zv = nrm(Tt, H_v, d).bfloat16()
+    gv = -torch.nn.functional.softplus(nrm(Tt, H_v))
+    bv = torch.sigmoid(nrm(Tt, H_v))
+    rec = torch.zeros(len(lens), H_v, d, d, device="cuda")
+    hist = torch.zeros(len(lens), 3, C_ch, device="cuda").bfloat16()
+    yv = torch.empty(Tt, H_v, d, device="cuda")
+    wsv = torch.empty(gdn.prefill_varlen_workspace_bytes(dv, cu, 64), dtype=torch.uint8, device="cuda")
+    slots = list(range(len(lens)))
+
+    def vstep():
+        rec.zero_()
+        hist.zero_()
+        gdn.prefill_varlen(dv, cu, xv, zv, gv, bv, w, hist, rec, slots, chunk=64, y=yv, ws=wsv)
+
+    for _ in range(args.warmup):
+        vstep()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        vstep()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    vb = prefill_bytes_per_token(C_ch, H_v, d, 2, 4) * Tt + len(lens) * 2 * st_bytes
+    out["varlen_prefill"] = {
+        "workload": f"gdn_prefill_varlen of {len(lens)} sequences {lens} ({Tt} tokens), chunk 64, "
+                    f"zero initial states (reset inside the timed step), fp32 y",
+        "us_per_call": round(ms * 1e3, 1), "tokens_per_s": round(Tt / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(vb / (ms * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(vb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "alg_bytes_per_call": int(vb)}}
+    log(f"[bench] varlen prefill {len(lens)} sequences, {Tt} tokens: {ms * 1e3:.1f} us = "
+        f"{Tt / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+    del xv, zv, yv, wsv
+
+    # grouped RMS norm + gate over the ungated readout
+    Tn = 4096
+    dn = gdn.Dims(B=1, H_k=H_k, H_v=H_v, d_k=d, d_v=d, in_dtype=gdn.BF16, out_dtype=gdn.BF16)
+    o = nrm(1, Tn, H_v, d)
+    zn = nrm(1, Tn, H_v, d).bfloat16()
+    nw = 0.1 * nrm(d)
+    yn = torch.empty(1, Tn, H_v, d, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        gdn.gated_rmsnorm(dn, o, zn, nw, y=yn)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        gdn.gated_rmsnorm(dn, o, zn, nw, y=yn)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nb = Tn * H_v * d * (4 + 2 + 2) + d * 4
+    out["gated_rmsnorm"] = {
+        "workload": f"gdn_gated_rmsnorm over {Tn} tokens x 48 heads x 128 (fp32 o, bf16 z and y)",
+        "us_per_call": round(ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(nb / (ms * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "alg_bytes_per_call": int(nb)}}
+    log(f"[bench] gated rmsnorm {Tn} tokens: {ms * 1e3:.2f} us = {nb / (ms * 1e-3) / 1e9:.0f} GB/s")
+    return out
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -331,7 +482,7 @@ def main():
                     help="graph replays per decode timing (each replays R rotated steps)")
     ap.add_argument("--legs", default="all",
                     help="comma list of: long64, long128, t4096, decode_b1, decode_b64, in_proj, "
-                         "hybrid, cpu (default all); the headline leg always runs")
+                         "hybrid, serving, cpu (default all); the headline leg always runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run --steps plain device copies of MIB MiB (for scaling the HBM "
@@ -410,7 +561,8 @@ def main():
         return
 
     legs = set(args.legs.split(",")) if args.legs != "all" else {
-        "long64", "long128", "t4096", "decode_b1", "decode_b64", "in_proj", "hybrid", "cpu"}
+        "long64", "long128", "t4096", "decode_b1", "decode_b64", "in_proj", "hybrid", "serving",
+        "cpu"}
     if args.no_cpu_baseline:
         legs.discard("cpu")
     head_leg = "long64" if args.chunk == 64 else "long128"
@@ -681,6 +833,9 @@ def main():
             f"the same shape {Fp / ms_t / 1e9:.0f} TFLOP/s")
         del hP, wP, outs
 
+    # ------------------------------------------------------------ serving shapes, epilogue
+    serving = serving_legs(args, gdn, torch, np) if "serving" in legs else None
+
     # ------------------------------------------------------------ hybrid 3:1 block
     hybrid = None
     if "hybrid" in legs:
@@ -744,6 +899,7 @@ def main():
         "prefill": out_legs,
         "decode": decode,
         "in_proj": proj,
+        "serving": serving,
         "hybrid_block": hybrid,
         "cpu_baseline": cpu,
     }
