@@ -11,7 +11,9 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/gdn.h"
 #include "gdn_internal.h"
@@ -522,6 +524,52 @@ int gdn_decode_multi(const gdn_dims *dims, int32_t T, const void *x, const void 
 // full before anything is enqueued; then each non-empty sequence runs the
 // chunked prefill on its own rows and its own slot, in stream order, all
 // sharing one workspace.
+// Packed variable-length prefill runs its sequences on up to kVarlenLanes
+// streams at once: the caller's stream and up to three auxiliary ones of the
+// library, forked from and joined back to the caller's stream by events.  A
+// short sequence's three passes leave most compute units idle; side by side,
+// the sequences' state passes share the GPU.  Each lane has its own workspace
+// part, so the workspace is lanes x the largest single-sequence workspace.
+constexpr int kVarlenLanes = 4;
+constexpr int kMaxDevices = 64;
+
+struct VarlenStreams {
+  hipStream_t aux[kVarlenLanes - 1] = {};
+  hipEvent_t fork = nullptr, join[kVarlenLanes - 1] = {};
+};
+std::mutex g_varlen_mu;
+VarlenStreams g_varlen[kMaxDevices];
+
+// The auxiliary streams and events of the current device, created on first
+// use (non-blocking, default priority) and kept until the process ends.
+// Called with g_varlen_mu held.
+static hipError_t varlen_streams(VarlenStreams **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  VarlenStreams &v = g_varlen[dev];
+  if (!v.fork) {
+    VarlenStreams n;
+    for (int k = 0; e == hipSuccess && k < kVarlenLanes - 1; ++k) {
+      e = hipStreamCreateWithFlags(&n.aux[k], hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join[k], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    v = n;
+  }
+  *out = &v;
+  return hipSuccess;
+}
+
+// Lanes of a sequence table: one per non-empty sequence, at most kVarlenLanes.
+static int varlen_lanes(const Geom &g, const int64_t *cu) {
+  int n = 0;
+  for (int i = 0; i < g.B; ++i) n += cu[i + 1] > cu[i];
+  return std::max(1, std::min(n, kVarlenLanes));
+}
+
 static int varlen_check(const Geom &g, const int64_t *cu, int32_t chunk, size_t *ws_need,
                         int64_t *T_total) {
   if (!cu) return GDN_ERR_INVALID_ARG;
@@ -539,7 +587,8 @@ static int varlen_check(const Geom &g, const int64_t *cu, int32_t chunk, size_t 
   }
   if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128) return GDN_ERR_UNSUPPORTED;
   if (cu[g.B] > (int64_t(1) << 40)) return GDN_ERR_INVALID_ARG;
-  *ws_need = std::max<size_t>(need, 256);
+  need = (need + 255) / 256 * 256;  // each lane's part 256-byte aligned
+  *ws_need = std::max<size_t>(need, 256) * varlen_lanes(g, cu);
   *T_total = cu[g.B];
   return GDN_OK;
 }
@@ -596,20 +645,51 @@ int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, int32_t 
   LaunchTimer tm(nullptr);
   Geom g1 = g;
   g1.B = 1;
-  for (int n = 0; n < g.B; ++n) {
+  const int lanes = varlen_lanes(g, cu_seqlens);
+  const size_t lane_ws = need / lanes;
+  std::unique_lock<std::mutex> lock(g_varlen_mu, std::defer_lock);
+  VarlenStreams *vs = nullptr;
+  hipStream_t ls[kVarlenLanes] = {s};
+  hipError_t e = hipSuccess;
+  if (lanes > 1) {
+    lock.lock();
+    e = varlen_streams(&vs);
+    if (e == hipSuccess) e = hipEventRecord(vs->fork, s);
+    for (int k = 1; e == hipSuccess && k < lanes; ++k) {
+      ls[k] = vs->aux[k - 1];
+      e = hipStreamWaitEvent(ls[k], vs->fork, 0);
+    }
+  }
+  // Longest sequences first, each to the lane with the fewest tokens so far.
+  std::vector<int> order;
+  for (int n = 0; n < g.B; ++n)
+    if (cu_seqlens[n + 1] > cu_seqlens[n]) order.push_back(n);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    return cu_seqlens[a + 1] - cu_seqlens[a] > cu_seqlens[b + 1] - cu_seqlens[b];
+  });
+  int64_t load[kVarlenLanes] = {};
+  for (size_t i = 0; e == hipSuccess && i < order.size(); ++i) {
+    const int n = order[i];
     const int64_t t0 = cu_seqlens[n], len = cu_seqlens[n + 1] - t0;
-    if (len == 0) continue;
+    const int k = static_cast<int>(std::min_element(load, load + lanes) - load);
+    load[k] += len;
     PrefillWs L;
     prefill_ws_layout(g1, len, chunk, &L);
     const size_t tok = static_cast<size_t>(t0);
-    const hipError_t e = enqueue_prefill(
+    e = enqueue_prefill(
         g1, L, static_cast<const char *>(x) + tok * g.C_ch * es,
         static_cast<const char *>(z) + tok * g.H_v * g.D * es, gl + tok * g.H_v,
         beta + tok * g.H_v, conv_w, static_cast<char *>(conv_pool) + slots[n] * conv_slot,
         rec_pool + static_cast<size_t>(slots[n]) * (rec_slot / 4),
-        static_cast<char *>(y) + tok * g.H_v * g.D * eo, static_cast<char *>(ws), s, &tm);
-    if (e != hipSuccess) return set_hip_error(e, "gdn_prefill_varlen");
+        static_cast<char *>(y) + tok * g.H_v * g.D * eo, static_cast<char *>(ws) + k * lane_ws,
+        ls[k], &tm);
   }
+  // The caller's stream continues once every lane is done.
+  for (int k = 1; e == hipSuccess && k < lanes; ++k) {
+    e = hipEventRecord(vs->join[k - 1], ls[k]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, vs->join[k - 1], 0);
+  }
+  if (e != hipSuccess) return set_hip_error(e, "gdn_prefill_varlen");
   return GDN_OK;
 }
 

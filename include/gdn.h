@@ -39,7 +39,9 @@
  *    conv_state 16-byte aligned (every token offset of a 16-byte aligned x
  *    stays 16-byte aligned).  The
  *    caller owns every buffer; the library allocates nothing,
- *    keeps no state between calls and is safe to call from several threads.
+ *    keeps no state between calls and is safe to call from several threads
+ *    (apart from gdn_prefill_varlen's auxiliary streams and the fixed
+ *    scratch of gdn_decode_step_noalloc, each described there).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Compute calls
  *    only enqueue work and never synchronise; save/restore return after the
  *    copy has completed.
@@ -216,7 +218,13 @@ GDN_API int gdn_decode_multi(const gdn_dims *dims, int32_t T, const void *x, con
  * Each sequence gets exactly what gdn_prefill_chunked gives it alone, and its
  * slot holds its states afterwards; other slots are not touched.  `ws`: at
  * least gdn_prefill_varlen_workspace_bytes(dims, cu_seqlens, chunk) bytes
- * (the largest single-sequence prefill workspace; contents ignored). */
+ * (min(4, non-empty sequences) times the largest single-sequence prefill
+ * workspace; contents ignored).  Up to four sequences run at once: on
+ * `stream` and on up to three auxiliary streams that the library creates on
+ * the current device at the first such call and keeps until the process
+ * ends (default priority), forked from and joined back to `stream` by
+ * events, so the call stays ordered on `stream` like any other.  Concurrent
+ * calls from several threads serialize on those streams. */
 GDN_API size_t gdn_prefill_varlen_workspace_bytes(const gdn_dims *dims,
                                                   const int64_t *cu_seqlens, int32_t chunk);
 GDN_API int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, int32_t chunk,

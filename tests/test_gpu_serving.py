@@ -161,3 +161,45 @@ def test_prefill_varlen(chunk):
                                       y[a:b].astype(np.float32).view(np.uint32))
         np.testing.assert_array_equal(S1.cpu().numpy()[0].view(np.uint32),
                                       S[slots[n]].view(np.uint32))
+
+
+def test_prefill_varlen_graph_replay():
+    # The call forks its sequences onto up to four streams and joins them back
+    # by events; captured into a graph and replayed three times (pools reset
+    # in between, with eager work on the stream), every replay equals the
+    # eager call bit for bit.
+    import gated_deltanet_layer_gdn_amd as gdn
+    import torch
+
+    lens = [300, 5, 129, 64, 1, 250]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T_total = int(cu[-1])
+    geom = Geometry(B=1, T=T_total, H_k=4, H_v=12, d_k=128, d_v=128, zero_state=False)
+    I = make_inputs(geom, seed=510)
+    n_slots = 8
+    hp, Sp = pools(geom, n_slots, seed=511)
+    slots = [3, 0, 6, 1, 7, 4]
+    x, z, g, beta = (to_dev(I[k][0]) for k in ("x", "z", "g", "beta"))
+    w = to_dev(I["w"])
+    d = dims_of(Geometry(B=len(lens), T=1, H_k=4, H_v=12, d_k=128, d_v=128))
+    hp0, Sp0 = to_dev(hp), to_dev(Sp)
+    hp_d, Sp_d = hp0.clone(), Sp0.clone()
+    y = torch.empty(T_total, 12, 128, device="cuda")
+    ws = torch.empty(gdn.prefill_varlen_workspace_bytes(d, cu, 64), dtype=torch.uint8, device="cuda")
+    gdn.prefill_varlen(d, cu, x, z, g, beta, w, hp_d, Sp_d, slots, chunk=64, y=y, ws=ws)
+    torch.cuda.synchronize()
+    y_ref, S_ref, h_ref = y.clone(), Sp_d.clone(), hp_d.clone()
+    hp_d.copy_(hp0)
+    Sp_d.copy_(Sp0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdn.prefill_varlen(d, cu, x, z, g, beta, w, hp_d, Sp_d, slots, chunk=64, y=y, ws=ws)
+    for rep in range(3):
+        hp_d.copy_(hp0)
+        Sp_d.copy_(Sp0)
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[parity] varlen graph replay {rep}", flush=True)
+        assert torch.equal(y, y_ref) and torch.equal(Sp_d, S_ref) and torch.equal(hp_d, h_ref)
