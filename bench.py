@@ -53,6 +53,9 @@ LEG_SOURCES = {
     "t4096": ("conv.hip", "prep.hip", "prefill.hip", "gdn_device.h", "gdn_internal.h"),
     "decode_b1": ("conv.hip", "decode.hip", "gdn_device.h", "gdn_internal.h"),
     "decode_b64": ("conv.hip", "decode.hip", "gdn_device.h", "gdn_internal.h"),
+    "mtp_verify": ("conv.hip", "decode.hip", "gdn_device.h", "gdn_internal.h"),
+    "varlen_prefill": ("conv.hip", "prep.hip", "prefill.hip", "gdn_device.h", "gdn_internal.h"),
+    "gated_rmsnorm": ("epilogue.hip", "gdn_device.h", "gdn_internal.h"),
 }
 MEASURED_TRAFFIC = {
     # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
@@ -67,6 +70,13 @@ MEASURED_TRAFFIC = {
                "read": 3560000, "write": 3270000},
     "decode_b64": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
                "read": 218460000, "write": 209450000},
+    # profiles/gdn_serving_mtp_verify_b64_varlen8_rmsnorm4096.txt (per step or call)
+    "mtp_verify": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
+                   "read": 244640000, "write": 628400000},
+    "varlen_prefill": {"sha256": "0803121fc887610f726409d69a7aaf71e6ced6f81758d36aac022b325d079329",
+                       "read": 831800000, "write": 541360000},
+    "gated_rmsnorm": {"sha256": "f29ff1a71bd29fa6164cc5c33f3bb29bbf4f7d723c2483e74cffc7451e1ac231",
+                      "read": 151020000, "write": 50330000},
 }
 
 
@@ -209,6 +219,7 @@ def serving_legs(args, gdn, torch, np):
         "roofline": {"bound": "hbm", "achieved": round(mb / (ms * 1e-3) / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(mb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("mtp_verify"),
                      "alg_bytes_per_step": int(mb)}}
     log(f"[bench] mtp verify B={B} T={T}: {ms * 1e3:.1f} us/step = "
         f"{mb / (ms * 1e-3) / 1e9:.0f} GB/s of algorithmic bytes")
@@ -251,6 +262,7 @@ def serving_legs(args, gdn, torch, np):
         "roofline": {"bound": "hbm", "achieved": round(vb / (ms * 1e-3) / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(vb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("varlen_prefill"),
                      "alg_bytes_per_call": int(vb)}}
     log(f"[bench] varlen prefill {len(lens)} sequences, {Tt} tokens: {ms * 1e3:.1f} us = "
         f"{Tt / (ms * 1e-3) / 1e6:.2f} M tokens/s")
@@ -279,6 +291,7 @@ def serving_legs(args, gdn, torch, np):
         "roofline": {"bound": "hbm", "achieved": round(nb / (ms * 1e-3) / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("gated_rmsnorm"),
                      "alg_bytes_per_call": int(nb)}}
     log(f"[bench] gated rmsnorm {Tn} tokens: {ms * 1e3:.2f} us = {nb / (ms * 1e-3) / 1e9:.0f} GB/s")
     return out
