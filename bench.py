@@ -60,22 +60,22 @@ LEG_SOURCES = {
 MEASURED_TRAFFIC = {
     # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
     # profiles/gdn_hbm_bytes_prefill_t65536_t4096_decode.txt (sums over the leg's kernels)
-    "long64": {"sha256": "0803121fc887610f726409d69a7aaf71e6ced6f81758d36aac022b325d079329",
-               "read": 5104550000, "write": 3292410000},
-    "long128": {"sha256": "0803121fc887610f726409d69a7aaf71e6ced6f81758d36aac022b325d079329",
-               "read": 9667140000, "write": 7288920000},
-    "t4096": {"sha256": "0803121fc887610f726409d69a7aaf71e6ced6f81758d36aac022b325d079329",
-               "read": 327990000, "write": 204560000},
-    "decode_b1": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
+    "long64": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
+               "read": 4324330000, "write": 3254960000},
+    "long128": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
+               "read": 9668010000, "write": 7288920000},
+    "t4096": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
+               "read": 327610000, "write": 204560000},
+    "decode_b1": {"sha256": "30734a9e99dd4d1115ec966191fb84387dff436587d478853298a73620b9e562",
                "read": 3560000, "write": 3270000},
-    "decode_b64": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
+    "decode_b64": {"sha256": "30734a9e99dd4d1115ec966191fb84387dff436587d478853298a73620b9e562",
                "read": 218460000, "write": 209450000},
     # profiles/gdn_serving_mtp_verify_b64_varlen8_rmsnorm4096.txt (per step or call)
-    "mtp_verify": {"sha256": "7b27a238f8e0d7d180d257f6ce1d2ce14a1141308096d9da787bde09d6cf11e0",
+    "mtp_verify": {"sha256": "30734a9e99dd4d1115ec966191fb84387dff436587d478853298a73620b9e562",
                    "read": 244640000, "write": 628400000},
-    "varlen_prefill": {"sha256": "0803121fc887610f726409d69a7aaf71e6ced6f81758d36aac022b325d079329",
-                       "read": 831800000, "write": 541360000},
-    "gated_rmsnorm": {"sha256": "f29ff1a71bd29fa6164cc5c33f3bb29bbf4f7d723c2483e74cffc7451e1ac231",
+    "varlen_prefill": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
+                       "read": 829890000, "write": 541390000},
+    "gated_rmsnorm": {"sha256": "d613a32e0f197e44432022c2e3af24a91cde6a060c99fc441cf0d88c22384c75",
                       "read": 151020000, "write": 50330000},
 }
 
@@ -658,7 +658,7 @@ def main():
             "roofline": {
                 "bound": "hbm" if Bytes * PEAK_BF16_TFLOPS * 1e12 > F * PEAK_HBM_GBS * 1e9
                 else "mfma",
-                "kernel": "gdn_prefill_chunked: conv_qk_kernel + prep_kernel + state_kernel_ws"
+                "kernel": "gdn_prefill_chunked: prep_kernel (with the q/k conv at this size) + state_kernel_ws"
                           if C == 64 else
                           "gdn_prefill_chunked: conv_kernel + prep_kernel + state_kernel",
                 "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

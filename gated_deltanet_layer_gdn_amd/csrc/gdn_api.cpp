@@ -341,9 +341,10 @@ static hipError_t enqueue_prefill(const Geom &g, const PrefillWs &L, const void 
                                   void *conv_state, float *rec_state, void *y, char *w,
                                   hipStream_t s, LaunchTimer *tm) {
   hipError_t e = tm->mark(s);
-  if (e == hipSuccess) e = launch_conv_prefill(g, L, x, conv_w, conv_state, w, s);
+  if (e == hipSuccess && !prep_fuses_conv(g, L))
+    e = launch_conv_prefill(g, L, x, conv_w, conv_state, w, s);
   if (e == hipSuccess) e = tm->mark(s);
-  if (e == hipSuccess) e = launch_prefill_prep(g, L, gl, beta, w, x, conv_state, s);
+  if (e == hipSuccess) e = launch_prefill_prep(g, L, gl, beta, w, x, conv_w, conv_state, s);
   if (e == hipSuccess) e = tm->mark(s);
   if (e == hipSuccess) e = launch_prefill_state(g, L, z, rec_state, y, w, x, conv_w, conv_state, s);
   if (e == hipSuccess) e = tm->mark(s);

@@ -157,6 +157,67 @@ __device__ __forceinline__ float conv4(float w0, float w1, float w2, float w3, f
   return acc;
 }
 
+// ---------------------------------------------------------------- head sums of squares
+
+// DPP lane exchange within a row of 16 lanes (gfx9 control codes):
+// row_mirror (0x140) pairs lanes l and 15 - l, row_half_mirror (0x141) pairs
+// l and 7 - l in each group of 8, quad_perm (2,3,0,1) (0x4E) pairs l and l ^ 2,
+// quad_perm (1,0,3,2) (0xB1) pairs l and l ^ 1.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// One exchange of the transpose-reduce: N per-token values become N / 2.  The
+// lane whose BIT is set keeps the upper half of the tokens, its partner (which
+// has BIT clear and the same bits above) the lower half; each adds what the
+// other sends for the half it keeps.
+template <int N, int CTRL, int BIT>
+__device__ __forceinline__ void tr_step(float *v, int lane) {
+  const bool up = (lane & BIT) != 0;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = up ? v[i + N / 2] : v[i];
+    const float send = up ? v[i] : v[i + N / 2];
+    v[i] = keep + dpp_f<CTRL>(send);
+  }
+}
+
+// Per-token factor sc / sqrt(sum of squares + eps) of one 128-channel head
+// held by two waves (w = 0, 1: the wave's place in the head; red and bc hold
+// the head's two rows), for 16 tokens: 8 + 4 + 2 + 1 exchanges leave lane l with
+// token l / 4, and two more DPP additions (partners l ^ 2, then l ^ 1) finish
+// the lane sums.  Every token's sum runs through the same pairing tree, so a
+// token's factor does not depend on its place in the tile.
+__device__ __forceinline__ void head_scale_128x16(float (&ss)[16], float eps, float sc,
+                                                  float (*red)[16], float (*bc)[16], int w) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss[i]),
+                                                    __float_as_uint(ss[i + 8]), false, false);
+    ss[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss[i]),
+                                                    __float_as_uint(ss[i + 4]), false, false);
+    ss[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  tr_step<4, 0x140, 8>(ss, lane);
+  tr_step<2, 0x141, 4>(ss, lane);
+  float s = ss[0] + dpp_f<0x4E>(ss[0]);
+  s += dpp_f<0xB1>(s);
+  const int t = lane >> 2;
+  if ((lane & 3) == 0) red[w][t] = s;
+  __syncthreads();
+  const float f = __builtin_amdgcn_rsqf(red[0][t] + red[1][t] + eps) * sc;
+  if ((lane & 3) == 0) bc[w][t] = f;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ss[i] = bc[w][i];
+}
+
 // ---------------------------------------------------------------- wave ops
 
 __device__ __forceinline__ float wave_sum(float v) {

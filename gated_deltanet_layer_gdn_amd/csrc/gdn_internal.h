@@ -132,10 +132,29 @@ hipError_t launch_in_proj(const Geom &g, int64_t M, int hidden, const void *h, c
 // values (z may be null: no gate; w may be null: unit scale).
 hipError_t launch_gated_rmsnorm(const Geom &g, int64_t rows, const float *o, const void *z,
                                 const float *w, float eps, void *y, hipStream_t s);
-// Also rolls the conv history (x, hist) after the sequence.
+// Prep grids of more than this many blocks (chunks x key heads x sequences)
+// stage K in LDS; with two or more value heads per key head they also take
+// the value heads one per wave.
+constexpr int64_t kPrepStageBlocks = 8 * 256;
+// Whether the prep pass computes the q and k channels' conv, SiLU and L2 norm
+// itself (and writes them to the workspace for the state pass) instead of
+// reading them from a conv pass, which is then not launched: the split-role
+// prefill on grids of more than kPrepFuseBlocks blocks (where prep stages K
+// and takes the value heads one per wave).  There the fused pass moves less
+// (x read once instead of the q/k rows written by one pass and read by the
+// next) and hides its conv among the other blocks; on smaller grids each
+// block's conv latency shows and the separate conv pass is faster (measured
+// crossover between 3,072 and 6,144 blocks).
+constexpr int64_t kPrepFuseBlocks = 16 * 256;
+inline bool prep_fuses_conv(const Geom &g, const PrefillWs &L) {
+  return prefill_split_roles(g, L) && g.G >= 2 &&
+         static_cast<int64_t>(L.NC) * g.H_k * g.B > kPrepFuseBlocks;
+}
+// Also rolls the conv history (x, hist) after the sequence; conv_w is read
+// when prep_fuses_conv.
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
-                               const float *beta, char *ws, const void *x, void *hist,
-                               hipStream_t s);
+                               const float *beta, char *ws, const void *x, const void *conv_w,
+                               void *hist, hipStream_t s);
 // x, conv_w and hist are used by the split-role pass (v and its history).
 hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z, float *S,
                                 void *y, const char *ws, const void *x, const void *conv_w,

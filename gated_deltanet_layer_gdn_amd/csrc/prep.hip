@@ -12,7 +12,9 @@
 //   P  = tril(D) * (Q K^T),
 // stored as MFMA A operands (Tm plain bf16, P split) for the state pass.
 // The blocks of the first chunk also roll the conv history of the q and k
-// channels (or of all channels, when the state pass does not roll v).
+// channels (or of all channels, when the state pass does not roll v).  On
+// the largest grids (prep_fuses_conv) each block first computes its chunk of
+// q-hat and k-hat from x itself, in place of the conv pass.
 // The chunked form is the sequential recurrence of the gated delta rule
 // (Yang, Kautz, Hatamizadeh, "Gated Delta Networks", ICLR 2025) regrouped per
 // chunk, exact up to rounding.
@@ -276,17 +278,161 @@ __device__ __forceinline__ void prep_head_wave(const Geom &g, const PrefillWs &L
   }
 }
 
-template <int D, int C, bool STAGE, bool PERWAVE>
-__global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, PrefillWs L,
+// The conv, SiLU and L2 norm of one key head's q and k channels for one
+// chunk, computed the way the q/k conv pass computes them (the same loads,
+// products, reduction tree and rounding, so the same bits).  The results go
+// to the workspace's token-major q/k rows (bf16 high halves, e4m3 low halves)
+// for the state pass, and straight to the block's operands of the Gram
+// products: K's rows into the LDS staging rows (krows: hi, then lo widened
+// to bf16, 16-byte pieces XOR-swizzled by token), wave w's Q operands of
+// token tile w into registers, so nothing is read back from memory.
+// Threads 0..127 take the q head's channels, 128..255 the k head's; the
+// chunk's rows of x (and the three before it) are loaded at once, then
+// reduced and stored one 16-token tile at a time.  sa, sb: scratch of
+// kPrepConvScratchA and kPrepConvScratchB bytes (16-byte aligned), free
+// again on return.
+constexpr int kPrepConvTT = 16;
+constexpr size_t kPrepConvScratchA = 512 + 8 * kPrepConvTT * 32 * 2;  // sums, hi stage
+constexpr size_t kPrepConvScratchB = 8 * kPrepConvTT * 32;            // lo stage
+template <int DT, int C>
+__device__ __forceinline__ void prep_conv_qk(const Geom &g, const PrefillWs &L,
+                                             const void *__restrict__ x,
+                                             const void *__restrict__ w,
+                                             const void *__restrict__ hist, char *__restrict__ ws,
+                                             int b, int kh, int64_t tau0, unsigned char *sa,
+                                             unsigned char *sb, uint16_t (*krows)[128],
+                                             u16x8 (&qh_op)[4], u16x8 (&ql_op)[4]) {
+  constexpr int D = 128, TT = kPrepConvTT;
+  static_assert(C == 4 * TT, "wave w keeps the Q operands of tile w");
+  const int hp = threadIdx.x >> 7;  // 0: q head kh, 1: k head kh (uniform per wave)
+  const int j = threadIdx.x & 127;
+  const int nq = g.H_k * D;
+  const int ch = hp * nq + kh * D + j;
+  const float sc = hp == 0 ? g.q_scale : 1.0f;
+  const float lo_scale = hp == 0 ? L.q_lo_scale : L.k_lo_scale;
+  float (*red)[16] = reinterpret_cast<float (*)[16]>(sa);  // [head][wave in head][token]
+  float (*bc)[16] = reinterpret_cast<float (*)[16]>(sa + 256);
+  uint16_t (*sth)[TT][32] = reinterpret_cast<uint16_t (*)[TT][32]>(sa + 512);  // [head][slice]
+  uint8_t (*stl)[TT][32] = reinterpret_cast<uint8_t (*)[TT][32]>(sb);
+  constexpr int ES = DT == 0 ? 4 : 2;
+  const size_t rowb = static_cast<size_t>(g.C_ch) * ES;
+  const uint32_t lane_off = static_cast<uint32_t>(ch) * ES;
+  auto ld = [&](const char *row) -> float {
+    if constexpr (DT == 0)
+      return *reinterpret_cast<const float *>(row + lane_off);
+    else
+      return bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(row + lane_off));
+  };
+  const float w0 = load_elem<DT>(w, static_cast<size_t>(ch) * 4 + 0);
+  const float w1 = load_elem<DT>(w, static_cast<size_t>(ch) * 4 + 1);
+  const float w2 = load_elem<DT>(w, static_cast<size_t>(ch) * 4 + 2);
+  const float w3 = load_elem<DT>(w, static_cast<size_t>(ch) * 4 + 3);
+  const char *xb = static_cast<const char *>(x) + static_cast<size_t>(b) * L.T * rowb;
+  const char *hb = static_cast<const char *>(hist) + static_cast<size_t>(b) * 3 * rowb;
+  // The chunk's rows and the three before it, all loads in flight at once.
+  float xa[C + 3];
+  if (tau0 >= 3 && tau0 + C <= L.T) {
+    const char *r0 = xb + static_cast<size_t>(tau0 - 3) * rowb;
+#pragma unroll
+    for (int i = 0; i < C + 3; ++i) xa[i] = ld(r0 + i * rowb);
+  } else {
+#pragma unroll
+    for (int i = 0; i < C + 3; ++i) {
+      const int64_t tau = tau0 - 3 + i;  // uniform per block
+      float v = 0.f;
+      if (tau < 0)
+        v = ld(hb + static_cast<size_t>(3 + tau) * rowb);
+      else if (tau < L.T)
+        v = ld(xb + static_cast<size_t>(tau) * rowb);
+      xa[i] = v;
+    }
+  }
+  // Slice 0 of the head: [b][kh][slice][T_pad][32] token-major rows.
+  const size_t slice0 = (static_cast<size_t>(b) * g.H_k + kh) * (L.Dp / 32) * L.T_pad;
+  const int pos = kslot(j & 31);
+#pragma unroll
+  for (int it = 0; it < C / TT; ++it) {
+    const int64_t t0 = tau0 + it * TT;
+    float val[TT], ss[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      val[t] = siluf_(conv4(w0, w1, w2, w3, xa[TT * it + t], xa[TT * it + t + 1], xa[TT * it + t + 2],
+                            xa[TT * it + t + 3]));
+      ss[t] = val[t] * val[t];
+    }
+    head_scale_128x16(ss, g.eps, sc, red + 2 * hp, bc + 2 * hp, (threadIdx.x >> 6) & 1);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) val[t] *= ss[t];
+    if (t0 + TT > L.T) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        if (t0 + t >= L.T) val[t] = 0.f;  // padding tokens of the prefill layout
+    }
+#pragma unroll
+    for (int t = 0; t < TT; t += 2) {
+      uint32_t h2;
+      uint16_t l2;
+      split2_lo8(val[t], val[t + 1], lo_scale, h2, l2);
+      sth[4 * hp + (j >> 5)][t][pos] = static_cast<uint16_t>(h2);
+      sth[4 * hp + (j >> 5)][t + 1][pos] = static_cast<uint16_t>(h2 >> 16);
+      stl[4 * hp + (j >> 5)][t][pos] = static_cast<uint8_t>(l2);
+      stl[4 * hp + (j >> 5)][t + 1][pos] = static_cast<uint8_t>(l2 >> 8);
+    }
+    __syncthreads();
+    {
+      // K rows 16 it .. 16 it + 15 of the Gram staging: thread (token tok,
+      // piece p = 4 ks + gq) moves slots 8 gq .. 8 gq + 7 of slice ks.
+      const int tok = threadIdx.x >> 4, p = threadIdx.x & 15, ks = p >> 2, gq = p & 3;
+      const int off = 8 * (p ^ tok);
+      *reinterpret_cast<u16x8 *>(&krows[16 * it + tok][off]) =
+          *reinterpret_cast<const u16x8 *>(&sth[4 + ks][tok][8 * gq]);
+      *reinterpret_cast<u16x8 *>(&krows[C + 16 * it + tok][off]) =
+          lo8_to_bf16x8(*reinterpret_cast<const uint2 *>(&stl[4 + ks][tok][8 * gq]), L.k_lo_scale);
+    }
+    if ((threadIdx.x >> 6) == it) {
+      // Wave `it`: the tile's Q operands (token c, slots 8 gq .. 8 gq + 7 of
+      // each slice, the low halves widened).
+      const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        qh_op[ks] = *reinterpret_cast<const u16x8 *>(&sth[ks][c][8 * gq]);
+        ql_op[ks] = lo8_to_bf16x8(*reinterpret_cast<const uint2 *>(&stl[ks][c][8 * gq]), L.q_lo_scale);
+      }
+    }
+    // Per head and tile: four 1 KB runs of hi and four 512-byte runs of lo
+    // (one per 32-channel slice), written as 16-byte pieces.
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int piece = threadIdx.x;  // of head u's 4 KB of hi
+      const int sl = piece >> 6, tok = (piece >> 2) & 15, part = piece & 3;
+      uint16_t *dst = reinterpret_cast<uint16_t *>(ws + (u == 0 ? L.q_hi : L.k_hi)) +
+                      ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 8 * part);
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&sth[4 * u + sl][tok][8 * part]);
+    }
+    {
+      const int u = threadIdx.x >> 7, piece = threadIdx.x & 127;  // of head u's 2 KB of lo
+      const int sl = piece >> 5, tok = (piece >> 1) & 15, part = piece & 1;
+      uint8_t *dst = reinterpret_cast<uint8_t *>(ws + (u == 0 ? L.q_lo : L.k_lo)) +
+                     ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 16 * part);
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stl[4 * u + sl][tok][16 * part]);
+    }
+    __syncthreads();  // the stages and sums are rewritten by the next tile
+  }
+}
+
+template <int D, int C, bool STAGE, bool PERWAVE, bool CONV = false>
+__global__ __launch_bounds__(256, (C <= 64 ? (CONV ? 3 : 4) : 1)) void prep_kernel(Geom g, PrefillWs L,
                                                    const float *__restrict__ gl,
                                                    const float *__restrict__ beta,
                                                    char *__restrict__ ws,
                                                    const void *__restrict__ x,
+                                                   const void *__restrict__ conv_w,
                                                    void *__restrict__ hist) {
   using Sh = PrepShape<D, C>;
   constexpr int NT = Sh::NT, NTRI = Sh::NTRI, Dp = Sh::Dp, Cp = Sh::Cp;
-  __shared__ float KK[NTRI][256];  // Gram tiles, row-major 16 x 16
-  __shared__ float QK[NTRI][256];
+  // Gram tiles, row-major 16 x 16 (with CONV, first the conv's scratch)
+  __shared__ __attribute__((aligned(16))) float KK[NTRI][256];
+  __shared__ __attribute__((aligned(16))) float QK[NTRI][256];
   // A, then (I + A)^{-1} in place; before that (STAGE, chunks of at most 64
   // tokens), the chunk's K tiles as MFMA operands (hi and lo, bf16).
   constexpr bool kStageK = STAGE && C <= 64;
@@ -303,10 +449,40 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
   const int64_t tau0 = static_cast<int64_t>(chunk) * C;
   const int n_valid = static_cast<int>((L.T - tau0) < C ? (L.T - tau0) : C);
 
-  // 0. The conv history roll rides on the first chunk's blocks (one slice of
-  //    the channels per key head): the conv pass, its only reader, has
-  //    finished before this kernel starts.
-  if (chunk == 0) {
+  // 0. With CONV, this block first computes its chunk of q-hat and k-hat
+  //    from x (the conv pass does not run); the first chunk's blocks then
+  //    roll the history of exactly the channels they read (no other block
+  //    reads them, and their own reads are done).
+  // With CONV: wave w's Q operands of token tile w, from the conv.
+  [[maybe_unused]] u16x8 cq_h[4], cq_l[4];
+  if constexpr (CONV) {
+    static_assert(D == 128 && C == 64 && STAGE && PERWAVE, "fused conv: split-role prefill, staged grids");
+    static_assert(sizeof(KK) >= kPrepConvScratchA && sizeof(QK) >= kPrepConvScratchB &&
+                      sizeof(ti_raw) >= size_t(2) * C * 128 * 2,
+                  "conv scratch in the Gram tiles, K rows in the staging space");
+    unsigned char *sa = reinterpret_cast<unsigned char *>(&KK[0][0]);
+    unsigned char *sb = reinterpret_cast<unsigned char *>(&QK[0][0]);
+    uint16_t (*krows)[128] = reinterpret_cast<uint16_t (*)[128]>(ti_raw);
+    if (g.in_dt == 0)
+      prep_conv_qk<0, C>(g, L, x, conv_w, hist, ws, b, kh, tau0, sa, sb, krows, cq_h, cq_l);
+    else
+      prep_conv_qk<1, C>(g, L, x, conv_w, hist, ws, b, kh, tau0, sa, sb, krows, cq_h, cq_l);
+    if (chunk == 0) {
+      const int nq = g.H_k * D;
+#pragma unroll 1
+      for (int part = 0; part < 2; ++part) {
+        const int c0 = part * nq + kh * D;
+        if (g.in_dt == 0)
+          roll_history(g.C_ch, L.T, b, c0, c0 + D, static_cast<const uint32_t *>(x), static_cast<uint32_t *>(hist));
+        else
+          roll_history(g.C_ch, L.T, b, c0, c0 + D, static_cast<const uint16_t *>(x), static_cast<uint16_t *>(hist));
+      }
+    }
+  }
+  // Otherwise the conv history roll rides on the first chunk's blocks (one
+  // slice of the channels per key head): the conv pass, its only reader, has
+  // finished before this kernel starts.
+  if (!CONV && chunk == 0) {
     // With the split-role state pass, that pass rolls the v channels itself.
     const int nroll = prefill_split_roles(g, L) ? 2 * g.H_k * g.D : g.C_ch;
     const int per = (nroll + g.H_k - 1) / g.H_k;
@@ -363,13 +539,25 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
       const int sw = c & (NP - 1);
       u16x8 akh[KS], akl[KS], aqh[KS], aql[KS];
       if (wave < NT) {
-        load_tile(khi, klo, L.k_lo_scale, wave, akh, akl);
-        load_tile(qhi, qlo, L.q_lo_scale, wave, aqh, aql);
+        if constexpr (CONV) {
+          // K's rows are already staged and Q's operands in registers.
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = 8 * ((4 * ks + gq) ^ sw);
-          *reinterpret_cast<u16x8 *>(&Kh[16 * wave + c][off]) = akh[ks];
-          *reinterpret_cast<u16x8 *>(&Kl[16 * wave + c][off]) = akl[ks];
+          for (int ks = 0; ks < KS; ++ks) {
+            const int off = 8 * ((4 * ks + gq) ^ sw);
+            akh[ks] = *reinterpret_cast<const u16x8 *>(&Kh[16 * wave + c][off]);
+            akl[ks] = *reinterpret_cast<const u16x8 *>(&Kl[16 * wave + c][off]);
+            aqh[ks] = cq_h[ks];
+            aql[ks] = cq_l[ks];
+          }
+        } else {
+          load_tile(khi, klo, L.k_lo_scale, wave, akh, akl);
+          load_tile(qhi, qlo, L.q_lo_scale, wave, aqh, aql);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const int off = 8 * ((4 * ks + gq) ^ sw);
+            *reinterpret_cast<u16x8 *>(&Kh[16 * wave + c][off]) = akh[ks];
+            *reinterpret_cast<u16x8 *>(&Kl[16 * wave + c][off]) = akl[ks];
+          }
         }
       }
       __syncthreads();
@@ -657,42 +845,52 @@ __global__ __launch_bounds__(256, (C <= 64 ? 4 : 1)) void prep_kernel(Geom g, Pr
 
 // ---------------------------------------------------------------- launcher
 
-// K staged in LDS once the grid spans more than 8 blocks per compute unit:
-// a 4096-token prefill (1,024 blocks) then keeps every block resident at
-// once (37 against 47 us staged), and 65,536 tokens (16,384 blocks, bound
-// by HBM traffic) read 1.31 instead of 1.84 GB (535 against 582 us).
-constexpr int64_t kPrepStageBlocks = 8 * 256;
+// K staged in LDS once the grid spans more than kPrepStageBlocks (8 blocks
+// per compute unit): a 4096-token prefill (1,024 blocks) then keeps every
+// block resident at once (37 against 47 us staged), and 65,536 tokens
+// (16,384 blocks, bound by HBM traffic) read 1.31 instead of 1.84 GB (535
+// against 582 us).
 
 template <int D, int C>
 static void launch_prep_t(const Geom &g, const PrefillWs &L, const float *gl, const float *beta,
-                          char *ws, const void *x, void *hist, hipStream_t s) {
+                          char *ws, const void *x, const void *conv_w, void *hist, hipStream_t s) {
   dim3 grid(L.NC, g.H_k, g.B);
   const bool stage = C <= 64 && static_cast<int64_t>(L.NC) * g.H_k * g.B > kPrepStageBlocks;
+  if constexpr (D == 128 && C == 64) {
+    if (prep_fuses_conv(g, L)) {
+      hipLaunchKernelGGL((prep_kernel<D, C, true, true, true>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x,
+                         conv_w, hist);
+      return;
+    }
+  }
   if constexpr (C <= 64) {
     if (stage && g.G >= 2) {
       // Value heads one per wave: 511-517 against 543-571 us at T = 65,536
       // (bitwise equal).  Smaller grids keep the four-wave form, whose
       // smaller LDS footprint keeps four blocks per compute unit (35 against
       // 41 us at T = 4096).
-      hipLaunchKernelGGL((prep_kernel<D, C, true, true>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
+      hipLaunchKernelGGL((prep_kernel<D, C, true, true>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, conv_w,
+                         hist);
       return;
     }
   }
   if (stage)
-    hipLaunchKernelGGL((prep_kernel<D, C, true, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
+    hipLaunchKernelGGL((prep_kernel<D, C, true, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, conv_w,
+                       hist);
   else
-    hipLaunchKernelGGL((prep_kernel<D, C, false, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, hist);
+    hipLaunchKernelGGL((prep_kernel<D, C, false, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, conv_w,
+                       hist);
 }
 
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
-                               const float *beta, char *ws, const void *x, void *hist,
-                               hipStream_t s) {
-#define GDN_PREP(Dv)                                                       \
-  switch (L.C) {                                                           \
-    case 16: launch_prep_t<Dv, 16>(g, L, gl, beta, ws, x, hist, s); break;  \
-    case 32: launch_prep_t<Dv, 32>(g, L, gl, beta, ws, x, hist, s); break;  \
-    case 64: launch_prep_t<Dv, 64>(g, L, gl, beta, ws, x, hist, s); break;  \
-    default: launch_prep_t<Dv, 128>(g, L, gl, beta, ws, x, hist, s); break; \
+                               const float *beta, char *ws, const void *x, const void *conv_w,
+                               void *hist, hipStream_t s) {
+#define GDN_PREP(Dv)                                                               \
+  switch (L.C) {                                                                   \
+    case 16: launch_prep_t<Dv, 16>(g, L, gl, beta, ws, x, conv_w, hist, s); break;  \
+    case 32: launch_prep_t<Dv, 32>(g, L, gl, beta, ws, x, conv_w, hist, s); break;  \
+    case 64: launch_prep_t<Dv, 64>(g, L, gl, beta, ws, x, conv_w, hist, s); break;  \
+    default: launch_prep_t<Dv, 128>(g, L, gl, beta, ws, x, conv_w, hist, s); break; \
   }
   if (g.D == 128) {
     GDN_PREP(128)

@@ -65,7 +65,9 @@ hipError_t launch_in_proj(const Geom &, int64_t, int, const void *, const void *
   reached("in_proj");
 }
 hipError_t launch_prefill_prep(const Geom &, const PrefillWs &, const float *, const float *,
-                               char *, const void *, void *, hipStream_t) { reached("prep"); }
+                               char *, const void *, const void *, void *, hipStream_t) {
+  reached("prep");
+}
 hipError_t launch_prefill_state(const Geom &, const PrefillWs &, const void *, float *, void *,
                                 const char *, const void *, const void *, void *, hipStream_t) {
   reached("state");

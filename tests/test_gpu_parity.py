@@ -86,6 +86,19 @@ def test_prefill_prep_staged(B, T, dtype, H_k, H_v):
                 oracle_run(geom, I))
 
 
+@pytest.mark.parametrize("B,T,dtype,H_k,H_v", [(2, 17000, "f32", 16, 48), (1, 70000, "bf16", 4, 8)])
+def test_prefill_prep_fused_conv(B, T, dtype, H_k, H_v):
+    # Grids of more than 4096 prep blocks compute q-hat and k-hat inside the
+    # prep pass (no conv pass): fp32 and bf16 inputs, two sequences with a
+    # ragged tail and the history read by the first chunk, three and two
+    # value heads per key head; the conv history after the call bit-exact.
+    geom = Geometry(B=B, T=T, H_k=H_k, H_v=H_v, d_k=128, d_v=128, zero_state=False, dtype=dtype)
+    assert -(-T // 64) * H_k * B > 4096
+    I = make_inputs(geom, seed=170 + B)
+    check_layer(f"prep fused conv B={B} T={T} {dtype} heads {H_k}/{H_v}", gpu_prefill(geom, I, 64),
+                oracle_run(geom, I))
+
+
 @pytest.mark.parametrize("chunk", [64, 128])
 def test_prefill_fp32_inputs(chunk):
     # x, z, the conv weights and history in fp32 at d = 128 (every other
