@@ -465,7 +465,13 @@ void launch_tiles(const ProjArgs &a, hipStream_t s) {
 // stages 828 / 970; 256 x 128 or 128 x 256, 8 waves of 64 x 64, two stages
 // 801-817 / 877-882.
 constexpr int kProjBM = 256, kProjBN = 256, kProjWGM = 2, kProjWGN = 4, kProjStages = 2;
-constexpr int kProjRemBM = 64;  // M tile of the blocks that cover the last, partial N tile
+// The columns after the last full 256-column tile (b and a: 2 H_v = 96 at the
+// Qwen geometry) in 32 x 96 tiles of 4 waves (16 x 48 each): 128 blocks at M =
+// 4096 with no padding columns.  Measured side by side (whole projection,
+// bitwise equal): 1,117-1,131 TFLOP/s at M = 4096 and 1,152-1,167 at 16,384,
+// against 1,073-1,084 / 1,142-1,153 with 64 x 256 tiles (62% of their columns
+// padding) and 1,116-1,124 / 1,135-1,148 with 16 x 128.
+constexpr int kProjRemBM = 32, kProjRemBN = 96, kProjRemWGM = 2, kProjRemWGN = 2;
 constexpr int kDmaWGM = 2, kDmaWGN = 4;  // waves of the direct-to-LDS kernel (M x N)
 
 }  // namespace
@@ -489,7 +495,7 @@ hipError_t launch_in_proj(const Geom &g, int64_t M, int hidden, const void *h, c
   a.H_v = g.H_v;
   a.N = g.C_ch + a.Z + 2 * g.H_v;
   // The full 256-column tiles, then the remaining columns (96 at the Qwen
-  // geometry) in 64-row tiles: as 256 x 256 tiles they would be a last round
+  // geometry) in small tiles: as 256 x 256 tiles they would be a last round
   // of blocks at the cost of a full one for a third of the work (at M = 4096,
   // 16 such blocks after 1024 full ones on 256 compute units).
   int n_full = a.N / kProjBN * kProjBN;
@@ -508,7 +514,7 @@ hipError_t launch_in_proj(const Geom &g, int64_t M, int hidden, const void *h, c
   if (n_full < a.N) {
     a.n_begin = n_full;
     a.n_count = a.N - n_full;
-    launch_tiles<kProjRemBM, kProjBN, kProjWGM, kProjWGN, kProjStages>(a, s);
+    launch_tiles<kProjRemBM, kProjRemBN, kProjRemWGM, kProjRemWGN, kProjStages>(a, s);
   }
   return hipGetLastError();
 }
