@@ -14,9 +14,10 @@
 //
 // Layout: LPR lanes share one row, each holding NPL consecutive-by-4 floats
 // (d_k = 128: 8 lanes x 16 floats, every load instruction covers 128
-// contiguous bytes per row); the two dot products are reduced across those
-// lanes with xor shuffles.  A block of 4 waves takes 256 / LPR consecutive
-// state rows (32 at d = 128), loading all of them before computing: with
+// contiguous bytes per row; at B <= 4, 32 lanes x 4 floats, for four times
+// the blocks); the two dot products are reduced across those lanes with xor
+// shuffles.  A block of 4 waves takes 256 / LPR consecutive state rows (32
+// at d = 128 and B > 4), loading all of them before computing: with
 // nontemporal stores, these small blocks (12,288 at B = 64) stream faster
 // than one block per (sequence, head) walking four such groups (67.7-68.4
 // vs 75.4-75.6 us at B = 64, measured side by side).
@@ -196,7 +197,13 @@ template <int TT>
 static void launch_decode_tt(const Geom &g, const float *qkv, const void *z, const float *gl,
                              const float *beta, float *S, void *y, const SlotArgs &sa,
                              hipStream_t s) {
-  if (g.D == 128)  // 8 lanes x 16 floats per row, 32 rows per block
+  // d = 128: 8 lanes x 16 floats per row, 32 rows per block; at B <= 4, 32
+  // lanes x 4 floats, 8 rows per block (768 blocks at B = 1 instead of 192:
+  // 5.36-5.38 against 5.62-5.64 us per graph-replayed step, measured side by
+  // side; 16 lanes x 8 floats 5.40-5.45).
+  if (g.D == 128 && g.B <= 4)
+    launch_decode_t<128, 4, TT>(g, qkv, z, gl, beta, S, y, sa, s);
+  else if (g.D == 128)
     launch_decode_t<128, 16, TT>(g, qkv, z, gl, beta, S, y, sa, s);
   else
     launch_decode_t<16, 4, TT>(g, qkv, z, gl, beta, S, y, sa, s);
