@@ -61,20 +61,20 @@ MEASURED_TRAFFIC = {
     # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
     # profiles/gdn_hbm_bytes_prefill_t65536_t4096_decode.txt (sums over the leg's kernels)
     "long64": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
-               "read": 4324330000, "write": 3254960000},
+               "read": 4324320000, "write": 3255350000},
     "long128": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
-               "read": 9668010000, "write": 7288920000},
+               "read": 9668070000, "write": 7288920000},
     "t4096": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
-               "read": 327610000, "write": 204560000},
-    "decode_b1": {"sha256": "30734a9e99dd4d1115ec966191fb84387dff436587d478853298a73620b9e562",
-               "read": 3560000, "write": 3270000},
-    "decode_b64": {"sha256": "30734a9e99dd4d1115ec966191fb84387dff436587d478853298a73620b9e562",
-               "read": 218460000, "write": 209450000},
+               "read": 326750000, "write": 204550000},
+    "decode_b1": {"sha256": "b5d6e42a5e23eb8e72b183e1408af00c976969d25b1d275a17aac5183e3db4ae",
+               "read": 3720000, "write": 3270000},
+    "decode_b64": {"sha256": "b5d6e42a5e23eb8e72b183e1408af00c976969d25b1d275a17aac5183e3db4ae",
+               "read": 218470000, "write": 209450000},
     # profiles/gdn_serving_mtp_verify_b64_varlen8_rmsnorm4096.txt (per step or call)
-    "mtp_verify": {"sha256": "30734a9e99dd4d1115ec966191fb84387dff436587d478853298a73620b9e562",
-                   "read": 244640000, "write": 628400000},
+    "mtp_verify": {"sha256": "b5d6e42a5e23eb8e72b183e1408af00c976969d25b1d275a17aac5183e3db4ae",
+                   "read": 244650000, "write": 628400000},
     "varlen_prefill": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
-                       "read": 829890000, "write": 541390000},
+                       "read": 830360000, "write": 541340000},
     "gated_rmsnorm": {"sha256": "d613a32e0f197e44432022c2e3af24a91cde6a060c99fc441cf0d88c22384c75",
                       "read": 151020000, "write": 50330000},
 }
