@@ -338,6 +338,9 @@ GDN_API int gdn_decode_step_noalloc(const gdn_dims *dims, const void *x, const v
  * launches:
  *   prefill: [0] conv + L2 norm, [1] chunk-local prep (Gram, (I+A)^{-1}, P)
  *            and the conv history roll, [2] state pass + gate     (3 floats)
+ *            (d = 128, chunk 64, more than 4096 chunk x key-head blocks:
+ *            the q/k conv and norm run inside the prep launch, and [0]
+ *            spans no kernel)
  *   decode:  [0] conv step + L2 norm, [1] state stream + gate      (2 floats)
  * These variants create HIP events and wait for the last one before they
  * return. */
