@@ -154,7 +154,7 @@ def serving_legs(args, gdn, torch, np):
       and y;
     * a packed variable-length prefill (gdn_prefill_varlen) of 8 sequences of
       mixed lengths (4096 .. 129 tokens, 10,422 in all) from zero states,
-      chunk 64 (up to four sequences side by side): the prefill's algorithmic
+      chunk 64 (up to three sequences side by side): the prefill's algorithmic
       bytes per token plus each sequence's state in and out;
     * the zero-centred grouped RMS norm and gate (gdn_gated_rmsnorm) over the
       ungated readout of 4096 tokens: fp32 o and bf16 z read, bf16 y written.

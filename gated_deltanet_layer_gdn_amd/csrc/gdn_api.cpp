@@ -526,12 +526,18 @@ int gdn_decode_multi(const gdn_dims *dims, int32_t T, const void *x, const void 
 // chunked prefill on its own rows and its own slot, in stream order, all
 // sharing one workspace.
 // Packed variable-length prefill runs its sequences on up to kVarlenLanes
-// streams at once: the caller's stream and up to three auxiliary ones of the
+// streams at once: the caller's stream and up to two auxiliary ones of the
 // library, forked from and joined back to the caller's stream by events.  A
 // short sequence's three passes leave most compute units idle; side by side,
 // the sequences' state passes share the GPU.  Each lane has its own workspace
 // part, so the workspace is lanes x the largest single-sequence workspace.
-constexpr int kVarlenLanes = 4;
+// Three lanes, not four: a process gets four hardware queues by default,
+// and next to the caller's stream there is usually another stream of the
+// framework (a graph-capture stream, for one), so a third auxiliary stream
+// shared a queue with another lane and waited behind it (8 mixed sequences
+// in a process that had captured graphs: 573-575 us with three lanes against
+// 618-621 with four; about equal in a fresh process).
+constexpr int kVarlenLanes = 3;
 constexpr int kMaxDevices = 64;
 
 struct VarlenStreams {

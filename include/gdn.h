@@ -218,9 +218,9 @@ GDN_API int gdn_decode_multi(const gdn_dims *dims, int32_t T, const void *x, con
  * Each sequence gets exactly what gdn_prefill_chunked gives it alone, and its
  * slot holds its states afterwards; other slots are not touched.  `ws`: at
  * least gdn_prefill_varlen_workspace_bytes(dims, cu_seqlens, chunk) bytes
- * (min(4, non-empty sequences) times the largest single-sequence prefill
- * workspace; contents ignored).  Up to four sequences run at once: on
- * `stream` and on up to three auxiliary streams that the library creates on
+ * (min(3, non-empty sequences) times the largest single-sequence prefill
+ * workspace; contents ignored).  Up to three sequences run at once: on
+ * `stream` and on up to two auxiliary streams that the library creates on
  * the current device at the first such call and keeps until the process
  * ends (default priority), forked from and joined back to `stream` by
  * events, so the call stays ordered on `stream` like any other.  Concurrent

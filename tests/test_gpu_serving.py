@@ -164,7 +164,7 @@ def test_prefill_varlen(chunk):
 
 
 def test_prefill_varlen_graph_replay():
-    # The call forks its sequences onto up to four streams and joins them back
+    # The call forks its sequences onto up to three streams and joins them back
     # by events; captured into a graph and replayed three times (pools reset
     # in between, with eager work on the stream), every replay equals the
     # eager call bit for bit.
