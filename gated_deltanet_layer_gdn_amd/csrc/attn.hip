@@ -12,7 +12,9 @@
 // query's) v.
 //
 // Launches per call:
-//   kv_cache_kernel    the new keys, rotated, and values into the cache, and
+//   kv_cache_kernel    (calls of more than one token; a one-token call does
+//                      this inside attn_kernel) the new keys, rotated, and
+//                      values into the cache, and
 //                      the cos and sin of the RoPE angles of the new
 //                      positions into the workspace (T x r/2 pairs; the angle
 //                      formed in double and reduced mod 2 pi before the fp32
@@ -50,6 +52,40 @@ constexpr double kTwoPi = 6.283185307179586476925286766559;
 // sincos (positions of 10^5 and more keep their accuracy), and the blocks of
 // sequence 0, KV head 0 store its cos and sin as cs[t][p]; the other threads
 // copy two dimensions past r.  Every thread copies two dimensions of v.
+// cos and sin of the RoPE angle of pair p at position pos: pos * base^(-2p/r)
+// formed in double and reduced mod 2 pi, then the fp32 sincos.  One function
+// for every kernel that needs them, so the angles agree bit for bit.
+__device__ __forceinline__ float2 rope_cs(float base, int rot, int p, int64_t pos) {
+  const double inv = pow(static_cast<double>(base), -2.0 * p / rot);
+  double ang = static_cast<double>(pos) * inv;
+  ang -= kTwoPi * floor(ang / kTwoPi);
+  float sn, c;
+  sincosf(static_cast<float>(ang), &sn, &c);
+  return make_float2(c, sn);
+}
+
+// One key's rotation and its cache row (bf16 in, bf16 out): thread p < r/2
+// turns the pair (p, p + r/2) by cs = (cos, sin); the other threads (p < D/2)
+// copy two dimensions past r; every thread p < D/2 copies dimensions 2p and
+// 2p + 1 of v.  Explicit fused operations, so that every caller gets the
+// same bits.
+template <int D>
+__device__ __forceinline__ void rope_cache_row(int p, int rot, float2 cs, const uint16_t *src,
+                                               const uint16_t *vs, uint16_t *kdst, uint16_t *vdst) {
+  const int half = rot / 2;
+  if (p < half) {
+    const float x0 = bf16_bits_to_f32(src[p]), x1 = bf16_bits_to_f32(src[p + half]);
+    kdst[p] = f32_to_bf16_bits(__builtin_fmaf(x0, cs.x, -(x1 * cs.y)));
+    kdst[p + half] = f32_to_bf16_bits(__builtin_fmaf(x1, cs.x, x0 * cs.y));
+  } else {
+    const int j = rot + 2 * (p - half);
+    kdst[j] = src[j];
+    kdst[j + 1] = src[j + 1];
+  }
+  vdst[2 * p] = vs[2 * p];
+  vdst[2 * p + 1] = vs[2 * p + 1];
+}
+
 template <int D>
 __global__ __launch_bounds__(D / 2) void kv_cache_kernel(AttnGeom a, int64_t T, int64_t pos0,
                                                          int64_t T_max, const uint16_t *k,
@@ -62,27 +98,15 @@ __global__ __launch_bounds__(D / 2) void kv_cache_kernel(AttnGeom a, int64_t T, 
   const int64_t t = idx % T;
   const int b = static_cast<int>(idx / T);
   const uint16_t *src = k + ((b * T + t) * a.H_kv + head) * D;
-  const int64_t crow = ((b * T_max + pos0 + t) * a.H_kv + head) * D;
-  uint16_t *dst = kc + crow;
-  const int half = a.rot / 2;
-  if (p < half) {
-    const double inv = pow(static_cast<double>(a.base), -2.0 * p / a.rot);
-    double ang = static_cast<double>(pos0 + t) * inv;
-    ang -= kTwoPi * floor(ang / kTwoPi);
-    float sn, c;
-    sincosf(static_cast<float>(ang), &sn, &c);
-    if (b == 0 && head == 0) cs[t * half + p] = make_float2(c, sn);
-    const float x0 = bf16_bits_to_f32(src[p]), x1 = bf16_bits_to_f32(src[p + half]);
-    dst[p] = f32_to_bf16_bits(x0 * c - x1 * sn);
-    dst[p + half] = f32_to_bf16_bits(x1 * c + x0 * sn);
-  } else {
-    const int j = a.rot + 2 * (p - half);
-    dst[j] = src[j];
-    dst[j + 1] = src[j + 1];
-  }
   const uint16_t *vs = v + ((b * T + t) * a.H_kv + head) * D;
-  vc[crow + 2 * p] = vs[2 * p];
-  vc[crow + 2 * p + 1] = vs[2 * p + 1];
+  const int64_t crow = ((b * T_max + pos0 + t) * a.H_kv + head) * D;
+  const int half = a.rot / 2;
+  float2 c = make_float2(1.f, 0.f);
+  if (p < half) {
+    c = rope_cs(a.base, a.rot, p, pos0 + t);
+    if (b == 0 && head == 0) cs[t * half + p] = c;
+  }
+  rope_cache_row<D>(p, a.rot, c, src, vs, kc + crow, vc + crow);
 }
 
 // Geometry of the attention pass, fixed on the host per call.
@@ -95,6 +119,10 @@ struct AttnArgs {
   int n_split, tps;  // KV splits and KV tiles per split (1, all: no split)
   const uint16_t *q, *kc, *vc;  // q as given (RoPE applied here, on load)
   const float2 *cs;             // RoPE cos / sin of the new positions [T][r/2]
+  // T = 1 with the cache write fused in: the new key and value [B][1][H_kv][D]
+  // and the cache again, writable.
+  const uint16_t *k_new, *v_new;
+  uint16_t *kc_w, *vc_w;
   void *o;
   float *part_o, *part_ml;  // partial results when n_split > 1
 };
@@ -126,12 +154,17 @@ struct AttnCfg {
 // (global latency hidden behind the current tile's products) and stored to
 // LDS, V transposed on the way.  With n_split > 1 a block covers only the KV
 // tiles [s tps, (s + 1) tps) and writes its unnormalised output with its row
-// maximum and sum; attn_combine_kernel merges the splits.
-template <int D, int NW, int OC, bool SPLIT>
+// maximum and sum; attn_combine_kernel merges the splits.  FUSE (one new
+// token, T = 1): the block forms the RoPE table of position pos0 itself, and
+// the block of the last KV split of each (sequence, KV head) writes the new
+// key, rotated, and value into cache row pos0 before it reads the cache,
+// in place of kv_cache_kernel (one launch less per decode step).
+template <int D, int NW, int OC, bool SPLIT, bool FUSE>
 __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs p) {
   using C = AttnCfg<D, NW>;
   constexpr int NS = C::NS, NJ = C::NJ, R = C::R, NT = C::NT;
   __shared__ typename C::Smem sm;
+  __shared__ __attribute__((aligned(16))) float2 cs_sm[FUSE ? D / 2 : 2];
   const AttnGeom &a = p.a;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -153,6 +186,18 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs p) {
   const int64_t tq = fc / p.G;
   const int hq = kvh * p.G + static_cast<int>(fc % p.G);
   const int64_t qpos = p.pos0 + tq;
+  if constexpr (FUSE) {
+    const int half = a.rot / 2;
+    if (tid < half) cs_sm[tid] = rope_cs(a.base, a.rot, tid, p.pos0);
+    __syncthreads();
+    if (s_idx == p.n_split - 1 && tid < D / 2) {
+      const int64_t nrow = (static_cast<int64_t>(b) * a.H_kv + kvh) * D;
+      const int64_t crow = ((static_cast<int64_t>(b) * p.T_max + p.pos0) * a.H_kv + kvh) * D;
+      rope_cache_row<D>(tid, a.rot, tid < half ? cs_sm[tid] : make_float2(1.f, 0.f), p.k_new + nrow,
+                        p.v_new + nrow, p.kc_w + crow, p.vc_w + crow);
+    }
+    __syncthreads();  // the new cache row written before any wave reads the cache
+  }
   u16x8 qb[NS];
   {
     // The lane's eight dimensions 32 s + 8 g .. + 7 of each K step, turned by
@@ -173,7 +218,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs p) {
         u16x8 r;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float4 c2 = cp[e2];  // (cos, sin) of pairs i0 + 2 e2, i0 + 2 e2 + 1
+          // (cos, sin) of pairs i0 + 2 e2, i0 + 2 e2 + 1
+          const float4 c2 = FUSE ? reinterpret_cast<const float4 *>(cs_sm)[i0 / 2 + e2] : cp[e2];
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             const int e = 2 * e2 + h2;
@@ -464,17 +510,17 @@ AttnPlan attn_plan(const AttnGeom &a, int64_t T, int64_t pos0) {
   return pl;
 }
 
-template <int D, int OC>
+template <int D, int OC, bool FUSE>
 void launch_attn_core(const AttnArgs &p, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(p.n_fb) * p.a.B * p.a.H_kv *
                                                 p.n_split);
   if (p.n_split == 1) {
-    hipLaunchKernelGGL((attn_kernel<D, kAttnWaves, OC, false>), dim3(blocks),
+    hipLaunchKernelGGL((attn_kernel<D, kAttnWaves, OC, false, FUSE>), dim3(blocks),
                        dim3(64 * kAttnWaves), 0, s, p);
     return;
   }
-  hipLaunchKernelGGL((attn_kernel<D, kAttnWaves, OC, true>), dim3(blocks), dim3(64 * kAttnWaves),
-                     0, s, p);
+  hipLaunchKernelGGL((attn_kernel<D, kAttnWaves, OC, true, FUSE>), dim3(blocks),
+                     dim3(64 * kAttnWaves), 0, s, p);
   const int64_t rows = static_cast<int64_t>(p.a.B) * p.T * p.a.H_q;
   hipLaunchKernelGGL((attn_combine_kernel<D, OC>), dim3(static_cast<unsigned>(rows)), dim3(D), 0,
                      s, p);
@@ -515,20 +561,42 @@ hipError_t launch_attn_prefill(const AttnGeom &a, int64_t T, int64_t pos0, const
   auto *vc16 = static_cast<uint16_t *>(vc);
   float2 *cs = reinterpret_cast<float2 *>(wsb);
   const dim3 g1(static_cast<unsigned>(static_cast<int64_t>(a.B) * T * a.H_kv));
+  // One new token (a decode step): the attention pass writes the cache row
+  // itself.  Since T = 1 gives one row block per (sequence, KV head), exactly
+  // one block (that of the last KV split) writes each row.
+  const bool fuse = T == 1 && pl.n_fb == 1;
+  p.k_new = k16;
+  p.v_new = v16;
+  p.kc_w = kc16;
+  p.vc_w = vc16;
   if (a.D == 256) {
+    if (fuse) {
+      if (a.out_dt == 0)
+        launch_attn_core<256, 0, true>(p, s);
+      else
+        launch_attn_core<256, 1, true>(p, s);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((kv_cache_kernel<256>), g1, dim3(128), 0, s, a, T, pos0, T_max, k16, v16, cs,
                        kc16, vc16);
     if (a.out_dt == 0)
-      launch_attn_core<256, 0>(p, s);
+      launch_attn_core<256, 0, false>(p, s);
     else
-      launch_attn_core<256, 1>(p, s);
+      launch_attn_core<256, 1, false>(p, s);
   } else {
+    if (fuse) {
+      if (a.out_dt == 0)
+        launch_attn_core<128, 0, true>(p, s);
+      else
+        launch_attn_core<128, 1, true>(p, s);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((kv_cache_kernel<128>), g1, dim3(64), 0, s, a, T, pos0, T_max, k16, v16, cs,
                        kc16, vc16);
     if (a.out_dt == 0)
-      launch_attn_core<128, 0>(p, s);
+      launch_attn_core<128, 0, false>(p, s);
     else
-      launch_attn_core<128, 1>(p, s);
+      launch_attn_core<128, 1, false>(p, s);
   }
   return hipGetLastError();
 }

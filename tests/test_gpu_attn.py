@@ -207,3 +207,31 @@ def test_attn_decode_path(B, pos0, T, H_q, H_kv, d, rot, out_bf16):
     check_out(f"attn decode B={B} pos0={pos0} T={T} H={H_q}/{H_kv} d={d} r={rot}", o, ref,
               TOL_BF16 if out_bf16 else TOL_F32)
     check_cache("cache", kc, vc, kr, vr, pos0, T, I["k"], a)
+
+
+@pytest.mark.parametrize("B,pos0,H_q,H_kv,d,rot", [
+    (2, 4113, 24, 2, 256, 64),
+    (1, 300, 12, 1, 128, 32),
+    (1, 70, 4, 1, 256, 0),
+])
+def test_attn_single_token_cache_rows_match(B, pos0, H_q, H_kv, d, rot):
+    # A one-token call writes its cache row inside the attention pass; a
+    # two-token call writes its rows with the separate cache kernel.  Two
+    # one-token calls at positions pos0 - 1 and pos0 must leave the cache
+    # bit-identical to one two-token call over the same keys and values.
+    import gated_deltanet_layer_gdn_amd as gdn
+    import torch
+
+    a = attn_dims(B, H_q, H_kv, d, rot, 1e7 if d == 256 else 1e4)
+    I = make_attn_inputs(B, 2, pos0 - 1, pos0 + 3, H_q, H_kv, d, seed=1200 + pos0)
+    q, k, v = to_dev(I["q"]), to_dev(I["k"]), to_dev(I["v"])
+    kc2, vc2 = to_dev(I["k_cache"]), to_dev(I["v_cache"])
+    gdn.attn_prefill(a, q, k, v, kc2, vc2, pos0=pos0 - 1)
+    kc1, vc1 = to_dev(I["k_cache"]), to_dev(I["v_cache"])
+    for t in range(2):
+        gdn.attn_prefill(a, q[:, t:t + 1].contiguous(), k[:, t:t + 1].contiguous(),
+                         v[:, t:t + 1].contiguous(), kc1, vc1, pos0=pos0 - 1 + t)
+    torch.cuda.synchronize()
+    print(f"[attn] single-token cache rows B={B} pos0={pos0} d={d} rot={rot}", flush=True)
+    np.testing.assert_array_equal(from_dev(kc1), from_dev(kc2))
+    np.testing.assert_array_equal(from_dev(vc1), from_dev(vc2))
