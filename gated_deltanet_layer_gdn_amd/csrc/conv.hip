@@ -265,9 +265,10 @@ __global__ __launch_bounds__(kConvThreads, (MODE == kOutPrefillQK && D == 128 ? 
           uint4 *dh = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_hi) + blk * D * 32);
           uint4 *dl = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_lo) + blk * D * 32);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) dh[threadIdx.x + kConvThreads * u] = stage[threadIdx.x + kConvThreads * u];
+          for (int u = 0; u < 4; ++u) st_stream(dh + threadIdx.x + kConvThreads * u, stage[threadIdx.x + kConvThreads * u]);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) dl[threadIdx.x + kConvThreads * u] = stage[512 + threadIdx.x + kConvThreads * u];
+          for (int u = 0; u < 4; ++u)
+            st_stream(dl + threadIdx.x + kConvThreads * u, stage[512 + threadIdx.x + kConvThreads * u]);
         } else {
           u16x8 *dh = reinterpret_cast<u16x8 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_hi) + (blk * D + j) * 32);
           u16x8 *dl = reinterpret_cast<u16x8 *>(reinterpret_cast<uint16_t *>(a.ws + L.kT_lo) + (blk * D + j) * 32);
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kConvThreads, (MODE == kOutPrefillQK && D == 128 ? 
         const size_t blk = (static_cast<size_t>(b) * g.H_v + h) * (L.T_pad / 16) + t0 / 16;
         uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<float *>(a.ws + L.vT) + blk * D * 16);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) dst[threadIdx.x + kConvThreads * u] = stage[threadIdx.x + kConvThreads * u];
+        for (int u = 0; u < 8; ++u) st_stream(dst + threadIdx.x + kConvThreads * u, stage[threadIdx.x + kConvThreads * u]);
       } else {
 #pragma unroll
         for (int half = 0; half < TT / 16; ++half) {
@@ -421,13 +422,15 @@ __global__ __launch_bounds__(kConvThreads) void conv_qk_kernel(Geom g, ConvArgs 
       const int piece = threadIdx.x + kConvThreads * u;  // 16-byte piece of the 4 KB of hi
       const int sl = piece >> 6, tok = (piece >> 2) & 15, part = piece & 3;
       uint16_t *dst = phi + ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 8 * part);
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stage_hi[sl][tok][8 * part]);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(&stage_hi[sl][tok][8 * part]),
+                                  reinterpret_cast<u32x4 *>(dst));
     }
     {
       const int piece = threadIdx.x;  // 16-byte piece of the 2 KB of lo
       const int sl = piece >> 5, tok = (piece >> 1) & 15, part = piece & 1;
       uint8_t *dst = plo + ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 16 * part);
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stage_lo[sl][tok][16 * part]);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(&stage_lo[sl][tok][16 * part]),
+                                  reinterpret_cast<u32x4 *>(dst));
     }
     if (it + 1 < NTL) {
       // red, bc and the stages are reused by the next tile.

@@ -24,6 +24,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A 16-byte store with the nontemporal hint: for workspace rows that the
+// next pass streams back once, so they do not stay in the L2 in place of the
+// operands that blocks share.
+__device__ __forceinline__ void st_stream(uint4 *p, const uint4 &v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+}
 
 constexpr int kWave = 64;
 

@@ -127,7 +127,8 @@ __device__ __forceinline__ void prep_head_wave(const Geom &g, const PrefillWs &L
   if constexpr (D == 128 && C == 64) {
     float4 *gt = reinterpret_cast<float4 *>(ws + L.gates) +
                  ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C;
-    gt[lane] = make_float4(__expf(g0), __expf(g_last - g0), b0, __expf(g_last));
+    const f32x4 gv = {__expf(g0), __expf(g_last - g0), b0, __expf(g_last)};
+    __builtin_nontemporal_store(gv, reinterpret_cast<f32x4 *>(gt + lane));
   } else {
     float *gt = reinterpret_cast<float *>(ws + L.gates) +
                 ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * 3 * C;
@@ -253,16 +254,16 @@ __device__ __forceinline__ void prep_head_wave(const Geom &g, const PrefillWs &L
       tv8[i] = f32_to_bf16_bits(tv);
     }
     const size_t o = static_cast<size_t>(t) * Cp + 32 * kk + 8 * q;
-    *reinterpret_cast<u16x8 *>(Tm + o) = tv8;
+    __builtin_nontemporal_store(tv8, reinterpret_cast<u16x8 *>(Tm + o));
     if constexpr (kLo8) {
       uint32_t hh[4];
       uint16_t ll[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) split2_lo8(pv[2 * i], pv[2 * i + 1], L.q_lo_scale, hh[i], ll[i]);
       const u32x4 hv = {hh[0], hh[1], hh[2], hh[3]};
-      *reinterpret_cast<u16x8 *>(Ph + o) = __builtin_bit_cast(u16x8, hv);
-      *reinterpret_cast<uint2 *>(Pl8 + o) =
-          make_uint2(ll[0] | (static_cast<uint32_t>(ll[1]) << 16), ll[2] | (static_cast<uint32_t>(ll[3]) << 16));
+      __builtin_nontemporal_store(__builtin_bit_cast(u16x8, hv), reinterpret_cast<u16x8 *>(Ph + o));
+      const u32x2 lv = {ll[0] | (static_cast<uint32_t>(ll[1]) << 16), ll[2] | (static_cast<uint32_t>(ll[3]) << 16)};
+      __builtin_nontemporal_store(lv, reinterpret_cast<u32x2 *>(Pl8 + o));
     } else {
       u16x8 ph8, pl8;
 #pragma unroll
@@ -272,8 +273,8 @@ __device__ __forceinline__ void prep_head_wave(const Geom &g, const PrefillWs &L
         ph8[i] = hi;
         pl8[i] = lo;
       }
-      *reinterpret_cast<u16x8 *>(Ph + o) = ph8;
-      *reinterpret_cast<u16x8 *>(Pl + o) = pl8;
+      __builtin_nontemporal_store(ph8, reinterpret_cast<u16x8 *>(Ph + o));
+      __builtin_nontemporal_store(pl8, reinterpret_cast<u16x8 *>(Pl + o));
     }
   }
 }
@@ -407,14 +408,16 @@ __device__ __forceinline__ void prep_conv_qk(const Geom &g, const PrefillWs &L,
       const int sl = piece >> 6, tok = (piece >> 2) & 15, part = piece & 3;
       uint16_t *dst = reinterpret_cast<uint16_t *>(ws + (u == 0 ? L.q_hi : L.k_hi)) +
                       ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 8 * part);
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&sth[4 * u + sl][tok][8 * part]);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(&sth[4 * u + sl][tok][8 * part]),
+                                  reinterpret_cast<u32x4 *>(dst));
     }
     {
       const int u = threadIdx.x >> 7, piece = threadIdx.x & 127;  // of head u's 2 KB of lo
       const int sl = piece >> 5, tok = (piece >> 1) & 15, part = piece & 1;
       uint8_t *dst = reinterpret_cast<uint8_t *>(ws + (u == 0 ? L.q_lo : L.k_lo)) +
                      ((slice0 + sl * L.T_pad + t0 + tok) * 32 + 16 * part);
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&stl[4 * u + sl][tok][16 * part]);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(&stl[4 * u + sl][tok][16 * part]),
+                                  reinterpret_cast<u32x4 *>(dst));
     }
     __syncthreads();  // the stages and sums are rewritten by the next tile
   }
