@@ -45,8 +45,8 @@ struct StateShape {
   static constexpr int NWV = D >= 128 ? 4 : 1;   // waves; each owns a slice of d_k
   static constexpr int NDT = D >= 32 ? 2 : 1;    // 16-wide d_k tiles per wave
   // 16-row state tiles per block: two share every K / Q / K^T operand load
-  // (the partial sums of a 128-token chunk would not fit the LDS twice).
-  static constexpr int NB = (D >= 128 && C <= 64) ? 2 : 1;
+  // (for 128-token chunks only with U and DU in the partial sums' space).
+  static constexpr int NB = D >= 128 ? 2 : 1;
   static constexpr int ROWS = 16 * NB;           // state rows per block
   static constexpr int Dp = D < 32 ? 32 : D;
 };
@@ -129,13 +129,32 @@ struct StateKernel {
 
   // Shared memory of one block.  Every tile is stored in D-register order
   // (one entry per lane), so writes and reads are lane-contiguous.
-  struct Smem {
+  struct SmemPlain {
     f32x4 part[NWV][2][NT][NB][64];  // K S^T / Q S^T partial sums of each wave's d_k slice
     Split4 R[NT][NB][64];            // R tiles, split
     Split4 U[NT][NB][64];            // U tiles, split (operand of P U)
     Split4 DU[NT][NB][64];           // exp(G_last - G_t) U tiles, split (operand of the update)
     uint4 z[NWV][16 * ZL];           // per wave: one token tile of z, token-major
   };
+  // d = 128, chunk 128: U and DU share the partial sums' space (those are
+  // consumed in step 2, before step 3 writes U), which brings the 32-row
+  // block to 148 KB of LDS, so that 192 blocks (one per compute unit) cover
+  // one sequence of 48 heads in one round; a barrier at the top of each
+  // chunk keeps the next chunk's partial sums from overwriting U and DU
+  // while steps 4 and 5 of other waves still read them.
+  static constexpr bool kAliasUDU = D == 128 && C == 128;
+  struct SmemAlias {
+    union {
+      f32x4 part[NWV][2][NT][NB][64];
+      struct {
+        Split4 U[NT][NB][64];
+        Split4 DU[NT][NB][64];
+      };
+    };
+    Split4 R[NT][NB][64];
+    uint4 z[NWV][16 * ZL];
+  };
+  using Smem = typename std::conditional<kAliasUDU, SmemAlias, SmemPlain>::type;
 
   // Wave-uniform base pointers (advanced per chunk by uniform strides) and
   // per-lane byte offsets, so that every load is base + 32-bit offset.
@@ -312,6 +331,7 @@ struct StateKernel {
     const int next = chunk + 1 < x.NC ? chunk + 1 : chunk;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const Split4 none = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+    if constexpr (kAliasUDU) __syncthreads();
 
     // 1. Partial K S^T and Q S^T over this wave's d_k slice, all token tiles.
 #pragma unroll
