@@ -60,23 +60,23 @@ LEG_SOURCES = {
 MEASURED_TRAFFIC = {
     # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
     # profiles/gdn_hbm_bytes_prefill_t65536_t4096_decode.txt (sums over the leg's kernels)
-    "long64": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
-               "read": 4324320000, "write": 3255350000},
-    "long128": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
-               "read": 9668070000, "write": 7288920000},
-    "t4096": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
-               "read": 326750000, "write": 204550000},
-    "decode_b1": {"sha256": "b5d6e42a5e23eb8e72b183e1408af00c976969d25b1d275a17aac5183e3db4ae",
+    "long64": {"sha256": "4bfcf356ee7eccc7d3aa7c8e0013df3b8f4e43c222febad353f7b0ca4af35e2f",
+               "read": 4320940000, "write": 3263360000},
+    "long128": {"sha256": "4bfcf356ee7eccc7d3aa7c8e0013df3b8f4e43c222febad353f7b0ca4af35e2f",
+               "read": 8858190000, "write": 7288760000},
+    "t4096": {"sha256": "4bfcf356ee7eccc7d3aa7c8e0013df3b8f4e43c222febad353f7b0ca4af35e2f",
+               "read": 326050000, "write": 204560000},
+    "decode_b1": {"sha256": "10f7302104c152795a05052267f8453efae34de81fef248c4bf93570b46d1b4a",
                "read": 3720000, "write": 3270000},
-    "decode_b64": {"sha256": "b5d6e42a5e23eb8e72b183e1408af00c976969d25b1d275a17aac5183e3db4ae",
-               "read": 218470000, "write": 209450000},
+    "decode_b64": {"sha256": "10f7302104c152795a05052267f8453efae34de81fef248c4bf93570b46d1b4a",
+               "read": 218480000, "write": 209450000},
     # profiles/gdn_serving_mtp_verify_b64_varlen8_rmsnorm4096.txt (per step or call)
-    "mtp_verify": {"sha256": "b5d6e42a5e23eb8e72b183e1408af00c976969d25b1d275a17aac5183e3db4ae",
+    "mtp_verify": {"sha256": "10f7302104c152795a05052267f8453efae34de81fef248c4bf93570b46d1b4a",
                    "read": 244650000, "write": 628400000},
-    "varlen_prefill": {"sha256": "e37c59d374d4b32f96d2c284fa11de75b0004f0587519671fdaac18f8905282b",
-                       "read": 830360000, "write": 541340000},
-    "gated_rmsnorm": {"sha256": "d613a32e0f197e44432022c2e3af24a91cde6a060c99fc441cf0d88c22384c75",
-                      "read": 151020000, "write": 50330000},
+    "varlen_prefill": {"sha256": "4bfcf356ee7eccc7d3aa7c8e0013df3b8f4e43c222febad353f7b0ca4af35e2f",
+                       "read": 829700000, "write": 541340000},
+    "gated_rmsnorm": {"sha256": "44871c6aaf78c15797c97bf790b85f96323063e3df84447add1d08ffe31039e2",
+                      "read": 151030000, "write": 50330000},
 }
 
 
