@@ -423,8 +423,111 @@ __device__ __forceinline__ void prep_conv_qk(const Geom &g, const PrefillWs &L,
   }
 }
 
+// Gate table of one value head and chunk for the state pass (four-wave prep
+// form; the per-wave form writes its own).
+template <int D, int C>
+__device__ __forceinline__ void store_gate_table(const Geom &g, const PrefillWs &L, char *ws, int b,
+                                                 int h, int chunk, const float *Gs, const float *Bs) {
+  if constexpr (D == 128 && C == 64) {
+    // Interleaved per token for the split-role state pass: one 16-byte
+    // load gives a token's gamma, decay to the chunk end, beta and the
+    // chunk's gamma_last.
+    float4 *gt = reinterpret_cast<float4 *>(ws + L.gates) +
+                 ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C;
+    const float glast = __expf(Gs[C - 1]);
+    for (int t = threadIdx.x; t < C; t += blockDim.x)
+      gt[t] = make_float4(__expf(Gs[t]), __expf(Gs[C - 1] - Gs[t]), Bs[t], glast);
+  } else {
+    float *gt = reinterpret_cast<float *>(ws + L.gates) +
+                ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * 3 * C;
+    for (int t = threadIdx.x; t < C; t += blockDim.x) {
+      gt[t] = __expf(Gs[t]);
+      gt[C + t] = __expf(Gs[C - 1] - Gs[t]);
+      gt[2 * C + t] = Bs[t];
+    }
+  }
+}
+
+// Tm (bf16, from TI) and / or P (hi/lo, tril(D) * QK) of one value head and
+// chunk as A operands of the state pass: row t, column s at its permuted K
+// slot; zero above the diagonal and in the padding columns.  One item is the
+// 16-byte piece of slots 8q..8q+7 of a 32-column step, which holds columns
+// 4q..4q+3 and 16+4q..16+4q+3 of that step.  Streamed to the workspace with
+// the nontemporal hint (read once, by the state pass).
+template <int D, int C, bool TM, bool PP>
+__device__ __forceinline__ void store_pieces(const Geom &g, const PrefillWs &L, char *ws, int b,
+                                             int h, int chunk, const float *Gs,
+                                             float (*TI)[256], float (*QK)[256]) {
+  constexpr int Cp = C < 32 ? 32 : C;
+  const size_t mat = ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C * Cp;
+  uint16_t *Tm = reinterpret_cast<uint16_t *>(ws + L.Tm) + mat;
+  uint16_t *Ph = reinterpret_cast<uint16_t *>(ws + L.P_hi) + mat;
+  uint16_t *Pl = reinterpret_cast<uint16_t *>(ws + L.P_lo) + mat;
+  // For the split-role state pass (d = 128, C = 64) the low half of P is
+  // e4m3 bytes (|P| <= |q_scale|, so q's scale), at the same element index.
+  constexpr bool kLo8 = D == 128 && C == 64;
+  uint8_t *Pl8 = reinterpret_cast<uint8_t *>(ws + L.P_lo) + mat;
+  // The split-role pass reads K step 1 only for rows 32..63 (a row's
+  // product stops at its own 32-column step), so there the pieces of K
+  // step 1 for rows 0..31, all zero, are not stored: 384 items, K step 0 of
+  // every row first.
+  constexpr int ITEMS = kLo8 ? 384 : C * (Cp / 32) * 4;
+  for (int it = threadIdx.x; it < ITEMS; it += 256) {
+    int t, kk, q;
+    if constexpr (kLo8) {
+      kk = it >> 8;
+      t = 32 * kk + ((it & 255) >> 2);
+      q = it & 3;
+    } else {
+      t = it / (Cp / 8);
+      const int rem = it % (Cp / 8);
+      kk = rem >> 2;
+      q = rem & 3;
+    }
+    u16x8 tv8;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sc = 32 * kk + (i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4));
+      float tv = 0.f;
+      pv[i] = 0.f;
+      if (sc < C && sc <= t) {
+        const int tr = tri_index(t >> 4, sc >> 4), off = (t & 15) * 16 + (sc & 15);
+        if constexpr (TM) tv = TI[tr][off];
+        if constexpr (PP) pv[i] = __expf(Gs[t] - Gs[sc]) * QK[tr][off];
+      }
+      tv8[i] = f32_to_bf16_bits(tv);
+    }
+    const size_t o = static_cast<size_t>(t) * Cp + 32 * kk + 8 * q;
+    if constexpr (TM) __builtin_nontemporal_store(tv8, reinterpret_cast<u16x8 *>(Tm + o));
+    if constexpr (PP) {
+      if constexpr (kLo8) {
+        uint32_t hh[4];
+        uint16_t ll[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split2_lo8(pv[2 * i], pv[2 * i + 1], L.q_lo_scale, hh[i], ll[i]);
+        const u32x4 hv = {hh[0], hh[1], hh[2], hh[3]};
+        __builtin_nontemporal_store(__builtin_bit_cast(u16x8, hv), reinterpret_cast<u16x8 *>(Ph + o));
+        const u32x2 lv = {ll[0] | (static_cast<uint32_t>(ll[1]) << 16), ll[2] | (static_cast<uint32_t>(ll[3]) << 16)};
+        __builtin_nontemporal_store(lv, reinterpret_cast<u32x2 *>(Pl8 + o));
+      } else {
+        u16x8 ph8, pl8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint16_t hi, lo;
+          split_bf16(pv[i], hi, lo);
+          ph8[i] = hi;
+          pl8[i] = lo;
+        }
+        __builtin_nontemporal_store(ph8, reinterpret_cast<u16x8 *>(Ph + o));
+        __builtin_nontemporal_store(pl8, reinterpret_cast<u16x8 *>(Pl + o));
+      }
+    }
+  }
+}
+
 template <int D, int C, bool STAGE, bool PERWAVE, bool CONV = false>
-__global__ __launch_bounds__(256, (C <= 64 ? (CONV ? 3 : 4) : 1)) void prep_kernel(Geom g, PrefillWs L,
+__global__ __launch_bounds__(256, (C <= 64 ? (CONV ? 3 : 4) : 2)) void prep_kernel(Geom g, PrefillWs L,
                                                    const float *__restrict__ gl,
                                                    const float *__restrict__ beta,
                                                    char *__restrict__ ws,
@@ -432,17 +535,22 @@ __global__ __launch_bounds__(256, (C <= 64 ? (CONV ? 3 : 4) : 1)) void prep_kern
                                                    const void *__restrict__ conv_w,
                                                    void *__restrict__ hist) {
   using Sh = PrepShape<D, C>;
-  constexpr int NT = Sh::NT, NTRI = Sh::NTRI, Dp = Sh::Dp, Cp = Sh::Cp;
+  constexpr int NT = Sh::NT, NTRI = Sh::NTRI, Dp = Sh::Dp;
   // Gram tiles, row-major 16 x 16 (with CONV, first the conv's scratch)
   __shared__ __attribute__((aligned(16))) float KK[NTRI][256];
   __shared__ __attribute__((aligned(16))) float QK[NTRI][256];
   // A, then (I + A)^{-1} in place; before that (STAGE, chunks of at most 64
   // tokens), the chunk's K tiles as MFMA operands (hi and lo, bf16).
   constexpr bool kStageK = STAGE && C <= 64;
-  constexpr size_t kTiBytes = sizeof(float) * NTRI * 256 * (PERWAVE ? kHeadSlots : 1);
+  // Chunks of 128 (four-wave form): P of every value head is formed and
+  // stored right after the Gram products, so that each head's inverse then
+  // works in QK's space; the block takes 74 instead of 111 KB of LDS and two
+  // blocks share a compute unit.
+  constexpr bool kPFirst = !STAGE && !PERWAVE && C > 64;
+  constexpr size_t kTiBytes = kPFirst ? 16 : sizeof(float) * NTRI * 256 * (PERWAVE ? kHeadSlots : 1);
   constexpr size_t kStageBytes = kStageK ? size_t(2) * NT * 16 * Dp * 2 : 0;
   __shared__ __attribute__((aligned(16))) unsigned char ti_raw[kTiBytes > kStageBytes ? kTiBytes : kStageBytes];
-  float (*TI)[256] = reinterpret_cast<float (*)[256]>(ti_raw);
+  float (*TI)[256] = kPFirst ? QK : reinterpret_cast<float (*)[256]>(ti_raw);
   // the four-wave form's gate prefix and beta (the per-wave form keeps them in registers)
   __shared__ float Gs[PERWAVE ? 1 : C], Bs[PERWAVE ? 1 : C];
 
@@ -639,9 +747,8 @@ __global__ __launch_bounds__(256, (C <= 64 ? (CONV ? 3 : 4) : 1)) void prep_kern
                              tau0, n_valid);
     return;
   } else {
-  for (int jv = 0; jv < g.G; ++jv) {
-    const int h = kh * g.G + jv;
-    __syncthreads();  // Gram tiles written; previous head's readers done
+  // Gate prefix G_t and beta_t of value head h into Gs, Bs (wave 0).
+  auto head_prefix = [&](int h) {
     if (wave == 0) {
       float g0, g1;
       const size_t base = (static_cast<size_t>(b) * L.T + tau0) * g.H_v + h;
@@ -656,29 +763,25 @@ __global__ __launch_bounds__(256, (C <= 64 ? (CONV ? 3 : 4) : 1)) void prep_kern
             (64 + lane < n_valid) ? beta[base + static_cast<size_t>(64 + lane) * g.H_v] : 0.f;
       }
     }
+  };
+  if constexpr (kPFirst) {
+    for (int jv = 0; jv < g.G; ++jv) {
+      const int h = kh * g.G + jv;
+      __syncthreads();  // Gram tiles written; previous head's readers done
+      head_prefix(h);
+      __syncthreads();
+      store_gate_table<D, C>(g, L, ws, b, h, chunk, Gs, Bs);
+      store_pieces<D, C, false, true>(g, L, ws, b, h, chunk, Gs, TI, QK);
+    }
+  }
+  for (int jv = 0; jv < g.G; ++jv) {
+    const int h = kh * g.G + jv;
+    __syncthreads();  // Gram tiles (and with kPFirst, every head's P) done; previous head's readers done
+    head_prefix(h);
     __syncthreads();
 
     // Gate factors of this chunk for the state pass.
-    {
-      if constexpr (D == 128 && C == 64) {
-        // Interleaved per token for the split-role state pass: one 16-byte
-        // load gives a token's gamma, decay to the chunk end, beta and the
-        // chunk's gamma_last.
-        float4 *gt = reinterpret_cast<float4 *>(ws + L.gates) +
-                     ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C;
-        const float glast = __expf(Gs[C - 1]);
-        for (int t = threadIdx.x; t < C; t += blockDim.x)
-          gt[t] = make_float4(__expf(Gs[t]), __expf(Gs[C - 1] - Gs[t]), Bs[t], glast);
-      } else {
-        float *gt = reinterpret_cast<float *>(ws + L.gates) +
-                    ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * 3 * C;
-        for (int t = threadIdx.x; t < C; t += blockDim.x) {
-          gt[t] = __expf(Gs[t]);
-          gt[C + t] = __expf(Gs[C - 1] - Gs[t]);
-          gt[2 * C + t] = Bs[t];
-        }
-      }
-    }
+    if constexpr (!kPFirst) store_gate_table<D, C>(g, L, ws, b, h, chunk, Gs, Bs);
 
     // 2. Tm = (I + A)^{-1}, A[t][s] = beta_t exp(G_t - G_s) KK[t][s] (s < t),
     //    blocked by 16 x 16 tiles and computed in place in TI:
@@ -775,73 +878,9 @@ __global__ __launch_bounds__(256, (C <= 64 ? (CONV ? 3 : 4) : 1)) void prep_kern
     }
     __syncthreads();
 
-    // 3. Store Tm (bf16) and P (hi/lo) as A operands: row t, column s at its
-    //    permuted K slot; zero above the diagonal and in the padding columns.
-    //    One item is the 16-byte piece of slots 8q..8q+7 of a 32-column step,
-    //    which holds columns 4q..4q+3 and 16+4q..16+4q+3 of that step.
-    const size_t mat = ((static_cast<size_t>(b) * g.H_v + h) * L.NC + chunk) * C * Cp;
-    uint16_t *Tm = reinterpret_cast<uint16_t *>(ws + L.Tm) + mat;
-    uint16_t *Ph = reinterpret_cast<uint16_t *>(ws + L.P_hi) + mat;
-    uint16_t *Pl = reinterpret_cast<uint16_t *>(ws + L.P_lo) + mat;
-    // For the split-role state pass (d = 128, C = 64) the low half of P is
-    // e4m3 bytes (|P| <= |q_scale|, so q's scale), at the same element index.
-    constexpr bool kLo8 = D == 128 && C == 64;
-    uint8_t *Pl8 = reinterpret_cast<uint8_t *>(ws + L.P_lo) + mat;
-    // The split-role pass reads K step 1 only for rows 32..63 (a row's
-    // product stops at its own 32-column step), so there the pieces of K
-    // step 1 for rows 0..31, all zero, are not stored: 384 items, K step 0 of
-    // every row first.
-    constexpr int ITEMS = kLo8 ? 384 : C * (Cp / 32) * 4;
-    for (int it = threadIdx.x; it < ITEMS; it += 256) {
-      int t, kk, q;
-      if constexpr (kLo8) {
-        kk = it >> 8;
-        t = 32 * kk + ((it & 255) >> 2);
-        q = it & 3;
-      } else {
-        t = it / (Cp / 8);
-        const int rem = it % (Cp / 8);
-        kk = rem >> 2;
-        q = rem & 3;
-      }
-      u16x8 tv8;
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int sc = 32 * kk + (i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4));
-        float tv = 0.f;
-        pv[i] = 0.f;
-        if (sc < C && sc <= t) {
-          const int tr = tri_index(t >> 4, sc >> 4), off = (t & 15) * 16 + (sc & 15);
-          tv = TI[tr][off];
-          pv[i] = __expf(Gs[t] - Gs[sc]) * QK[tr][off];
-        }
-        tv8[i] = f32_to_bf16_bits(tv);
-      }
-      const size_t o = static_cast<size_t>(t) * Cp + 32 * kk + 8 * q;
-      *reinterpret_cast<u16x8 *>(Tm + o) = tv8;
-      if constexpr (kLo8) {
-        uint32_t h[4];
-        uint16_t l[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split2_lo8(pv[2 * i], pv[2 * i + 1], L.q_lo_scale, h[i], l[i]);
-        const u32x4 hv = {h[0], h[1], h[2], h[3]};
-        *reinterpret_cast<u16x8 *>(Ph + o) = __builtin_bit_cast(u16x8, hv);
-        *reinterpret_cast<uint2 *>(Pl8 + o) =
-            make_uint2(l[0] | (static_cast<uint32_t>(l[1]) << 16), l[2] | (static_cast<uint32_t>(l[3]) << 16));
-      } else {
-        u16x8 ph8, pl8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint16_t hi, lo;
-          split_bf16(pv[i], hi, lo);
-          ph8[i] = hi;
-          pl8[i] = lo;
-        }
-        *reinterpret_cast<u16x8 *>(Ph + o) = ph8;
-        *reinterpret_cast<u16x8 *>(Pl + o) = pl8;
-      }
-    }
+    // 3. Store Tm (bf16) and P (hi/lo) as A operands (with kPFirst, P was
+    //    stored before the inverses).
+    store_pieces<D, C, true, !kPFirst>(g, L, ws, b, h, chunk, Gs, TI, QK);
   }
   }
 }
