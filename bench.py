@@ -60,12 +60,12 @@ LEG_SOURCES = {
 MEASURED_TRAFFIC = {
     # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
     # profiles/gdn_hbm_bytes_prefill_t65536_t4096_decode.txt (sums over the leg's kernels)
-    "long64": {"sha256": "4bfcf356ee7eccc7d3aa7c8e0013df3b8f4e43c222febad353f7b0ca4af35e2f",
-               "read": 4320940000, "write": 3263360000},
-    "long128": {"sha256": "4bfcf356ee7eccc7d3aa7c8e0013df3b8f4e43c222febad353f7b0ca4af35e2f",
-               "read": 8858190000, "write": 7288760000},
-    "t4096": {"sha256": "4bfcf356ee7eccc7d3aa7c8e0013df3b8f4e43c222febad353f7b0ca4af35e2f",
-               "read": 326050000, "write": 204560000},
+    "long64": {"sha256": "436d4f2cf47d357c1d0f3f3f619809438738849db9adc05161c44cc414bf9c0c",
+               "read": 4320920000, "write": 3263390000},
+    "long128": {"sha256": "436d4f2cf47d357c1d0f3f3f619809438738849db9adc05161c44cc414bf9c0c",
+               "read": 10172090000, "write": 7288780000},
+    "t4096": {"sha256": "436d4f2cf47d357c1d0f3f3f619809438738849db9adc05161c44cc414bf9c0c",
+               "read": 325880000, "write": 214090000},
     "decode_b1": {"sha256": "10f7302104c152795a05052267f8453efae34de81fef248c4bf93570b46d1b4a",
                "read": 3720000, "write": 3270000},
     "decode_b64": {"sha256": "10f7302104c152795a05052267f8453efae34de81fef248c4bf93570b46d1b4a",
@@ -73,8 +73,8 @@ MEASURED_TRAFFIC = {
     # profiles/gdn_serving_mtp_verify_b64_varlen8_rmsnorm4096.txt (per step or call)
     "mtp_verify": {"sha256": "10f7302104c152795a05052267f8453efae34de81fef248c4bf93570b46d1b4a",
                    "read": 244650000, "write": 628400000},
-    "varlen_prefill": {"sha256": "4bfcf356ee7eccc7d3aa7c8e0013df3b8f4e43c222febad353f7b0ca4af35e2f",
-                       "read": 829700000, "write": 541340000},
+    "varlen_prefill": {"sha256": "436d4f2cf47d357c1d0f3f3f619809438738849db9adc05161c44cc414bf9c0c",
+                       "read": 829560000, "write": 568990000},
     "gated_rmsnorm": {"sha256": "44871c6aaf78c15797c97bf790b85f96323063e3df84447add1d08ffe31039e2",
                       "read": 151030000, "write": 50330000},
 }
