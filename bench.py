@@ -658,7 +658,9 @@ def main():
             "roofline": {
                 "bound": "hbm" if Bytes * PEAK_BF16_TFLOPS * 1e12 > F * PEAK_HBM_GBS * 1e9
                 else "mfma",
-                "kernel": "gdn_prefill_chunked: prep_kernel (with the q/k conv at this size) + state_kernel_ws"
+                "kernel": ("gdn_prefill_chunked: prep_kernel (with the q/k conv at this size) + state_kernel_ws"
+                           if -(-G.T // C) * G.H_k * G.B > 4096 else
+                           "gdn_prefill_chunked: conv_qk_kernel + prep_kernel + state_kernel_ws")
                           if C == 64 else
                           "gdn_prefill_chunked: conv_kernel + prep_kernel + state_kernel",
                 "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
