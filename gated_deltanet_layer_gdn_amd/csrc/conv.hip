@@ -538,37 +538,41 @@ __global__ __launch_bounds__(kConvThreads) void conv_step_kernel(Geom g, const v
 template <int D, int BB, int TT>
 static hipError_t launch_conv_step_t(const Geom &g, const void *x, const void *w, void *hist,
                                      float *out, const int32_t *in_slots,
-                                     const int32_t *out_slots, int n_slots, hipStream_t s) {
+                                     const int32_t *out_slots, int n_slots, hipStream_t s,
+                                     const KernelEvents *ev) {
   dim3 grid((g.C_ch + kConvThreads - 1) / kConvThreads, (g.B + BB - 1) / BB);
   if (g.in_dt == 0)
-    hipLaunchKernelGGL((conv_step_kernel<0, D, BB, TT>), grid, dim3(kConvThreads), 0, s, g, x, w, hist, out, in_slots, out_slots, n_slots);
+    launch_kernel(conv_step_kernel<0, D, BB, TT>, grid, dim3(kConvThreads), s, ev, g, x, w, hist, out,
+                  in_slots, out_slots, n_slots);
   else
-    hipLaunchKernelGGL((conv_step_kernel<1, D, BB, TT>), grid, dim3(kConvThreads), 0, s, g, x, w, hist, out, in_slots, out_slots, n_slots);
+    launch_kernel(conv_step_kernel<1, D, BB, TT>, grid, dim3(kConvThreads), s, ev, g, x, w, hist, out,
+                  in_slots, out_slots, n_slots);
   return hipGetLastError();
 }
 
 template <int TT>
 static hipError_t launch_conv_step_tt(const Geom &g, const void *x, const void *w, void *hist,
                                       float *out, const int32_t *in_slots,
-                                      const int32_t *out_slots, int n_slots, hipStream_t s) {
+                                      const int32_t *out_slots, int n_slots, hipStream_t s,
+                                      const KernelEvents *ev) {
   // d = 128: two sequences per block (B = 64: 2,560 blocks) measured faster
   // than eight (640 blocks: too few waves in flight for the short loads).
   if (g.D == 128)
-    return g.B >= 8 ? launch_conv_step_t<128, 2, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s)
-                    : launch_conv_step_t<128, 1, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
+    return g.B >= 8 ? launch_conv_step_t<128, 2, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s, ev)
+                    : launch_conv_step_t<128, 1, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s, ev);
   return g.B >= 8 && TT == 1
-             ? launch_conv_step_t<16, 8, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s)
-             : launch_conv_step_t<16, 1, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
+             ? launch_conv_step_t<16, 8, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s, ev)
+             : launch_conv_step_t<16, 1, TT>(g, x, w, hist, out, in_slots, out_slots, n_slots, s, ev);
 }
 
 hipError_t launch_conv_step(const Geom &g, int T, const void *x, const void *w, void *hist,
                             float *out, const int32_t *in_slots, const int32_t *out_slots,
-                            int n_slots, hipStream_t s) {
+                            int n_slots, hipStream_t s, const KernelEvents *ev) {
   switch (T) {
-    case 1: return launch_conv_step_tt<1>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
-    case 2: return launch_conv_step_tt<2>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
-    case 3: return launch_conv_step_tt<3>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
-    case 4: return launch_conv_step_tt<4>(g, x, w, hist, out, in_slots, out_slots, n_slots, s);
+    case 1: return launch_conv_step_tt<1>(g, x, w, hist, out, in_slots, out_slots, n_slots, s, ev);
+    case 2: return launch_conv_step_tt<2>(g, x, w, hist, out, in_slots, out_slots, n_slots, s, ev);
+    case 3: return launch_conv_step_tt<3>(g, x, w, hist, out, in_slots, out_slots, n_slots, s, ev);
+    case 4: return launch_conv_step_tt<4>(g, x, w, hist, out, in_slots, out_slots, n_slots, s, ev);
     default: return hipErrorInvalidValue;
   }
 }

@@ -184,11 +184,12 @@ __global__ __launch_bounds__(256) void decode_kernel(Geom g, const float *__rest
 template <int D, int NPL, int TT>
 static void launch_decode_t(const Geom &g, const float *qkv, const void *z, const float *gl,
                             const float *beta, float *S, void *y, const SlotArgs &sa,
-                            hipStream_t s) {
+                            hipStream_t s, const KernelEvents *ev) {
   const int64_t rows = static_cast<int64_t>(g.B) * g.H_v * D;
   const dim3 grid(static_cast<unsigned>((rows + DecodeShape<D, NPL>::RPB - 1) /
                                         DecodeShape<D, NPL>::RPB));
-#define GDN_DEC(ZT, OC) hipLaunchKernelGGL((decode_kernel<D, NPL, ZT, OC, TT>), grid, dim3(256), 0, s, g, qkv, z, gl, beta, S, y, sa, rows)
+#define GDN_DEC(ZT, OC) \
+  launch_kernel(decode_kernel<D, NPL, ZT, OC, TT>, grid, dim3(256), s, ev, g, qkv, z, gl, beta, S, y, sa, rows)
   GDN_OUT_DISPATCH(g.in_dt, out_code(g.out_dt, z), GDN_DEC);
 #undef GDN_DEC
 }
@@ -196,28 +197,29 @@ static void launch_decode_t(const Geom &g, const float *qkv, const void *z, cons
 template <int TT>
 static void launch_decode_tt(const Geom &g, const float *qkv, const void *z, const float *gl,
                              const float *beta, float *S, void *y, const SlotArgs &sa,
-                             hipStream_t s) {
+                             hipStream_t s, const KernelEvents *ev) {
   // d = 128: 8 lanes x 16 floats per row, 32 rows per block; at B <= 4, 32
   // lanes x 4 floats, 8 rows per block (768 blocks at B = 1 instead of 192:
   // 5.36-5.38 against 5.62-5.64 us per graph-replayed step, measured side by
   // side; 16 lanes x 8 floats 5.40-5.45).
   if (g.D == 128 && g.B <= 4)
-    launch_decode_t<128, 4, TT>(g, qkv, z, gl, beta, S, y, sa, s);
+    launch_decode_t<128, 4, TT>(g, qkv, z, gl, beta, S, y, sa, s, ev);
   else if (g.D == 128)
-    launch_decode_t<128, 16, TT>(g, qkv, z, gl, beta, S, y, sa, s);
+    launch_decode_t<128, 16, TT>(g, qkv, z, gl, beta, S, y, sa, s, ev);
   else
-    launch_decode_t<16, 4, TT>(g, qkv, z, gl, beta, S, y, sa, s);
+    launch_decode_t<16, 4, TT>(g, qkv, z, gl, beta, S, y, sa, s, ev);
 }
 
 hipError_t launch_decode(const Geom &g, int T, const float *qkv, const void *z, const float *gl,
                          const float *beta, float *S, void *y, int n_slots,
-                         const int32_t *in_slots, const int32_t *out_slots, hipStream_t s) {
+                         const int32_t *in_slots, const int32_t *out_slots, hipStream_t s,
+                         const KernelEvents *ev) {
   const SlotArgs sa{in_slots, out_slots, n_slots};
   switch (T) {
-    case 1: launch_decode_tt<1>(g, qkv, z, gl, beta, S, y, sa, s); break;
-    case 2: launch_decode_tt<2>(g, qkv, z, gl, beta, S, y, sa, s); break;
-    case 3: launch_decode_tt<3>(g, qkv, z, gl, beta, S, y, sa, s); break;
-    case 4: launch_decode_tt<4>(g, qkv, z, gl, beta, S, y, sa, s); break;
+    case 1: launch_decode_tt<1>(g, qkv, z, gl, beta, S, y, sa, s, ev); break;
+    case 2: launch_decode_tt<2>(g, qkv, z, gl, beta, S, y, sa, s, ev); break;
+    case 3: launch_decode_tt<3>(g, qkv, z, gl, beta, S, y, sa, s, ev); break;
+    case 4: launch_decode_tt<4>(g, qkv, z, gl, beta, S, y, sa, s, ev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -447,18 +447,27 @@ static int decode_run(const gdn_dims *dims, const DecodeArgs &a, const char *whe
   if (a.ws_bytes < need) return GDN_ERR_WORKSPACE;
   if (injected_launch_failure()) return GDN_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(a.stream);
-  LaunchTimer tm(a.kernel_ms);
   float *qkv = static_cast<float *>(a.ws);
-  hipError_t e = tm.mark(s);
+  // The timed variant: events at each kernel's own start and end (the two
+  // kernels take a few microseconds at small B, about as long as the launch
+  // latency that events recorded between launches would add).
+  hipEvent_t ev[4] = {};
+  hipError_t e = hipSuccess;
+  for (int i = 0; a.kernel_ms && e == hipSuccess && i < 4; ++i) e = hipEventCreate(&ev[i]);
+  const KernelEvents k_conv{ev[0], ev[1]}, k_state{ev[2], ev[3]};
   if (e == hipSuccess)
     e = launch_conv_step(g, a.T, a.x, a.conv_w, a.conv_pool, qkv, a.in_slots, a.out_slots,
-                         a.n_slots, s);
-  if (e == hipSuccess) e = tm.mark(s);
+                         a.n_slots, s, a.kernel_ms ? &k_conv : nullptr);
   if (e == hipSuccess)
     e = launch_decode(g, a.T, qkv, a.z, a.gl, a.beta, a.rec_pool, a.y, a.n_slots, a.in_slots,
-                      a.out_slots, s);
-  if (e == hipSuccess) e = tm.mark(s);
-  if (e == hipSuccess) e = tm.elapsed();
+                      a.out_slots, s, a.kernel_ms ? &k_state : nullptr);
+  if (a.kernel_ms) {
+    if (e == hipSuccess) e = hipEventSynchronize(ev[3]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&a.kernel_ms[0], ev[0], ev[1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&a.kernel_ms[1], ev[2], ev[3]);
+    for (hipEvent_t v : ev)
+      if (v) (void)hipEventDestroy(v);
+  }
   return e == hipSuccess ? GDN_OK : set_hip_error(e, where);
 }
 

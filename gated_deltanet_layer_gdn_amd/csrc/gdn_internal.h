@@ -1,6 +1,9 @@
 // gdn_internal.h -- host-side plumbing between the C ABI and the kernels.
 #pragma once
 
+#ifdef __HIPCC__
+#include <hip/hip_ext.h>
+#endif
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -105,12 +108,35 @@ hipError_t launch_conv_roll(const Geom &g, int64_t T, const void *x, void *hist,
 // out slots; the state stream then reads qkv.  in_slots / out_slots may be
 // null (sequence b in slot b, state after the last token back into it).
 constexpr int kMaxMultiTokens = 4;
+// Events recorded at one kernel's own start and end (the timed entry points
+// launch through hipExtLaunchKernelGGL with them; null: a plain launch).
+struct KernelEvents {
+  hipEvent_t start, stop;
+};
+#ifdef __HIPCC__
+// Launch of `kernel` on `s`; with `ev` (the timed entry points), through
+// hipExtLaunchKernelGGL, which records ev->start and ev->stop at the kernel's
+// own start and end, so the interval leaves out the launch latency that
+// events recorded on the stream between launches would include.  The
+// arguments are converted to the kernel's parameter types first (the
+// extended launch passes them by address as given).
+template <typename... P, typename... A>
+inline void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s,
+                          const KernelEvents *ev, A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  if (ev)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev->start, ev->stop, 0, static_cast<P>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, static_cast<P>(args)...);
+}
+#endif
 hipError_t launch_conv_step(const Geom &g, int T, const void *x, const void *w, void *hist,
                             float *out, const int32_t *in_slots, const int32_t *out_slots,
-                            int n_slots, hipStream_t s);
+                            int n_slots, hipStream_t s, const KernelEvents *ev = nullptr);
 hipError_t launch_decode(const Geom &g, int T, const float *qkv, const void *z, const float *gl,
                          const float *beta, float *S, void *y, int n_slots,
-                         const int32_t *in_slots, const int32_t *out_slots, hipStream_t s);
+                         const int32_t *in_slots, const int32_t *out_slots, hipStream_t s,
+                         const KernelEvents *ev = nullptr);
 // Full attention of the hybrid schedule (attn.hip): geometry of one call.
 struct AttnGeom {
   int B, H_q, H_kv, D, rot;  // D = head dimension (128 or 256), rot = rotary width

@@ -334,8 +334,10 @@ GDN_API int gdn_decode_step_noalloc(const gdn_dims *dims, const void *x, const v
  * prefill, the decode and the recurrent-state update to be measured in
  * isolation).  Same arguments and effects as the plain calls, plus
  * `kernel_ms`, which receives the duration of each kernel launch of the call,
- * taken from HIP events that the library records on `stream` between its
- * launches:
+ * taken from HIP events: for prefill, events that the library records on
+ * `stream` between its launches; for decode, events recorded at each
+ * kernel's own start and end (an extended launch), since its kernels are as
+ * short as the launch latency:
  *   prefill: [0] conv + L2 norm, [1] chunk-local prep (Gram, (I+A)^{-1}, P)
  *            and the conv history roll, [2] state pass + gate     (3 floats)
  *            (d = 128, chunk 64, more than 4096 chunk x key-head blocks:

@@ -48,12 +48,13 @@ hipError_t launch_conv_roll(const Geom &, int64_t, const void *, void *, hipStre
   reached("conv_roll");
 }
 hipError_t launch_conv_step(const Geom &, int, const void *, const void *, void *, float *,
-                            const int32_t *, const int32_t *, int, hipStream_t) {
+                            const int32_t *, const int32_t *, int, hipStream_t,
+                            const KernelEvents *) {
   reached("conv_step");
 }
 hipError_t launch_decode(const Geom &, int, const float *, const void *, const float *,
                          const float *, float *, void *, int, const int32_t *, const int32_t *,
-                         hipStream_t) { reached("decode"); }
+                         hipStream_t, const KernelEvents *) { reached("decode"); }
 hipError_t launch_gated_rmsnorm(const Geom &, int64_t, const float *, const void *, const float *,
                                 float, void *, hipStream_t) { reached("gated_rmsnorm"); }
 size_t attn_ws_bytes(const AttnGeom &, int64_t, int64_t) { return 256; }
