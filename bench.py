@@ -60,22 +60,22 @@ LEG_SOURCES = {
 MEASURED_TRAFFIC = {
     # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
     # profiles/gdn_hbm_bytes_prefill_t65536_t4096_decode.txt (sums over the leg's kernels)
-    "long64": {"sha256": "436d4f2cf47d357c1d0f3f3f619809438738849db9adc05161c44cc414bf9c0c",
-               "read": 4320920000, "write": 3263390000},
-    "long128": {"sha256": "436d4f2cf47d357c1d0f3f3f619809438738849db9adc05161c44cc414bf9c0c",
-               "read": 10172090000, "write": 7288780000},
-    "t4096": {"sha256": "436d4f2cf47d357c1d0f3f3f619809438738849db9adc05161c44cc414bf9c0c",
-               "read": 325880000, "write": 214090000},
-    "decode_b1": {"sha256": "10f7302104c152795a05052267f8453efae34de81fef248c4bf93570b46d1b4a",
+    "long64": {"sha256": "f975949530c177d4063c7f6b33a6b60b816266574816ea829c71bc35ab38a5c7",
+               "read": 4322280000, "write": 3262030000},
+    "long128": {"sha256": "f975949530c177d4063c7f6b33a6b60b816266574816ea829c71bc35ab38a5c7",
+               "read": 10197020000, "write": 7288760000},
+    "t4096": {"sha256": "f975949530c177d4063c7f6b33a6b60b816266574816ea829c71bc35ab38a5c7",
+               "read": 325920000, "write": 214150000},
+    "decode_b1": {"sha256": "3caa50a191216eda4d77fea224db781b03e81879544407e6db822baaae6600b4",
                "read": 3720000, "write": 3270000},
-    "decode_b64": {"sha256": "10f7302104c152795a05052267f8453efae34de81fef248c4bf93570b46d1b4a",
+    "decode_b64": {"sha256": "3caa50a191216eda4d77fea224db781b03e81879544407e6db822baaae6600b4",
                "read": 218480000, "write": 209450000},
     # profiles/gdn_serving_mtp_verify_b64_varlen8_rmsnorm4096.txt (per step or call)
-    "mtp_verify": {"sha256": "10f7302104c152795a05052267f8453efae34de81fef248c4bf93570b46d1b4a",
+    "mtp_verify": {"sha256": "3caa50a191216eda4d77fea224db781b03e81879544407e6db822baaae6600b4",
                    "read": 244650000, "write": 628400000},
-    "varlen_prefill": {"sha256": "436d4f2cf47d357c1d0f3f3f619809438738849db9adc05161c44cc414bf9c0c",
-                       "read": 829560000, "write": 568990000},
-    "gated_rmsnorm": {"sha256": "44871c6aaf78c15797c97bf790b85f96323063e3df84447add1d08ffe31039e2",
+    "varlen_prefill": {"sha256": "f975949530c177d4063c7f6b33a6b60b816266574816ea829c71bc35ab38a5c7",
+                       "read": 829600000, "write": 569130000},
+    "gated_rmsnorm": {"sha256": "31cc808e45ea4183a296be4e6604b4d36afb684e6f9d4bc037cc53199d97fac0",
                       "read": 151030000, "write": 50330000},
 }
 
