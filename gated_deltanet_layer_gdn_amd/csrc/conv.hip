@@ -578,7 +578,8 @@ hipError_t launch_conv_step(const Geom &g, int T, const void *x, const void *w, 
 }
 
 template <int MODE, int TT>
-static hipError_t launch_conv(const Geom &g, const ConvArgs &a, hipStream_t s) {
+static hipError_t launch_conv(const Geom &g, const ConvArgs &a, hipStream_t s,
+                              const KernelEvents *ev = nullptr) {
   const int64_t tiles = (a.T_iter + TT - 1) / TT;
   // Without v the grid covers the q and k channels only (whole heads at d = 128).
   const int chans = (MODE == kOutPrefillQK) ? 2 * g.H_k * g.D : g.C_ch;
@@ -586,14 +587,14 @@ static hipError_t launch_conv(const Geom &g, const ConvArgs &a, hipStream_t s) {
   dim3 block(kConvThreads);
   if (g.D == 128) {
     if (g.in_dt == 0)
-      hipLaunchKernelGGL((conv_kernel<0, 128, MODE, TT>), grid, block, 0, s, g, a);
+      launch_kernel(conv_kernel<0, 128, MODE, TT>, grid, block, s, ev, g, a);
     else
-      hipLaunchKernelGGL((conv_kernel<1, 128, MODE, TT>), grid, block, 0, s, g, a);
+      launch_kernel(conv_kernel<1, 128, MODE, TT>, grid, block, s, ev, g, a);
   } else {
     if (g.in_dt == 0)
-      hipLaunchKernelGGL((conv_kernel<0, 16, MODE, TT>), grid, block, 0, s, g, a);
+      launch_kernel(conv_kernel<0, 16, MODE, TT>, grid, block, s, ev, g, a);
     else
-      hipLaunchKernelGGL((conv_kernel<1, 16, MODE, TT>), grid, block, 0, s, g, a);
+      launch_kernel(conv_kernel<1, 16, MODE, TT>, grid, block, s, ev, g, a);
   }
   return hipGetLastError();
 }
@@ -628,7 +629,8 @@ hipError_t launch_conv_plain(const Geom &g, int64_t T, const void *x, const void
 }
 
 hipError_t launch_conv_prefill(const Geom &g, const PrefillWs &L, const void *x,
-                               const void *w, const void *hist, char *ws, hipStream_t s) {
+                               const void *w, const void *hist, char *ws, hipStream_t s,
+                               const KernelEvents *ev) {
   ConvArgs a{};
   a.x = x;
   a.w = w;
@@ -640,15 +642,15 @@ hipError_t launch_conv_prefill(const Geom &g, const PrefillWs &L, const void *x,
   a.fuse_roll = 0;
   a.write_kT = !prefill_split_roles(g, L);
   a.write_v = !prefill_split_roles(g, L);
-  if (a.write_v) return launch_conv<kOutPrefill, kConvTT>(g, a, s);
+  if (a.write_v) return launch_conv<kOutPrefill, kConvTT>(g, a, s, ev);
   // q and k only (the split-role state pass computes v): d = 128.
   constexpr int NTL = 1;
   const int64_t tiles = a.T_iter / kConvQKTT;  // T_pad is a multiple of the 64-token chunk
   dim3 grid(static_cast<unsigned>(2 * g.H_k * ((tiles + NTL - 1) / NTL)), 1, g.B);
   if (g.in_dt == 0)
-    hipLaunchKernelGGL((conv_qk_kernel<0, NTL>), grid, dim3(kConvThreads), 0, s, g, a);
+    launch_kernel(conv_qk_kernel<0, NTL>, grid, dim3(kConvThreads), s, ev, g, a);
   else
-    hipLaunchKernelGGL((conv_qk_kernel<1, NTL>), grid, dim3(kConvThreads), 0, s, g, a);
+    launch_kernel(conv_qk_kernel<1, NTL>, grid, dim3(kConvThreads), s, ev, g, a);
   return hipGetLastError();
 }
 

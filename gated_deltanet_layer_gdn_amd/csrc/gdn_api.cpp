@@ -149,24 +149,39 @@ size_t rec_state_bytes(const Geom &g) {
 
 // Optional HIP events around each launch of one call, for the timed entry
 // points.  Records on the caller's stream; elapsed() waits for the last one.
-struct LaunchTimer {
+// Start and stop events of each kernel of a timed call, recorded at the
+// kernels' own boundaries (see launch_kernel); durations in milliseconds.
+struct CallTimer {
+  static constexpr int kMax = 3;
   float *out;
-  int n = 0;
-  hipEvent_t ev[8] = {};
-  explicit LaunchTimer(float *o) : out(o) {}
-  ~LaunchTimer() {
-    for (int i = 0; i < n; ++i) (void)hipEventDestroy(ev[i]);
+  hipEvent_t ev[2 * kMax] = {};
+  KernelEvents k[kMax] = {};
+  bool ran[kMax] = {};
+  hipError_t err = hipSuccess;
+  explicit CallTimer(float *o, int n) : out(o) {
+    for (int i = 0; o && err == hipSuccess && i < 2 * n; ++i) err = hipEventCreate(&ev[i]);
+    for (int i = 0; i < kMax; ++i) k[i] = KernelEvents{ev[2 * i], ev[2 * i + 1]};
   }
-  hipError_t mark(hipStream_t s) {
-    if (!out) return hipSuccess;
-    hipError_t e = hipEventCreate(&ev[n]);
-    if (e != hipSuccess) return e;
-    return hipEventRecord(ev[n++], s);
+  ~CallTimer() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
   }
-  hipError_t elapsed() {
+  // Events for kernel i of the call (null when the call is not timed).
+  const KernelEvents *at(int i) {
+    if (!out) return nullptr;
+    ran[i] = true;
+    return &k[i];
+  }
+  // Waits for the call's last kernel; kernels that did not run report 0.
+  hipError_t elapsed(int n) {
     if (!out) return hipSuccess;
-    hipError_t e = hipEventSynchronize(ev[n - 1]);
-    for (int i = 0; e == hipSuccess && i + 1 < n; ++i) e = hipEventElapsedTime(&out[i], ev[i], ev[i + 1]);
+    hipError_t e = hipSuccess;
+    for (int i = 0; e == hipSuccess && i < n; ++i) {
+      out[i] = 0.f;
+      if (!ran[i]) continue;
+      e = hipEventSynchronize(k[i].stop);
+      if (e == hipSuccess) e = hipEventElapsedTime(&out[i], k[i].start, k[i].stop);
+    }
     return e;
   }
 };
@@ -339,15 +354,15 @@ int gdn_conv1d(const gdn_dims *dims, int64_t T, const void *x, const void *conv_
 static hipError_t enqueue_prefill(const Geom &g, const PrefillWs &L, const void *x, const void *z,
                                   const float *gl, const float *beta, const void *conv_w,
                                   void *conv_state, float *rec_state, void *y, char *w,
-                                  hipStream_t s, LaunchTimer *tm) {
-  hipError_t e = tm->mark(s);
+                                  hipStream_t s, CallTimer *tm) {
+  hipError_t e = tm ? tm->err : hipSuccess;
   if (e == hipSuccess && !prep_fuses_conv(g, L))
-    e = launch_conv_prefill(g, L, x, conv_w, conv_state, w, s);
-  if (e == hipSuccess) e = tm->mark(s);
-  if (e == hipSuccess) e = launch_prefill_prep(g, L, gl, beta, w, x, conv_w, conv_state, s);
-  if (e == hipSuccess) e = tm->mark(s);
-  if (e == hipSuccess) e = launch_prefill_state(g, L, z, rec_state, y, w, x, conv_w, conv_state, s);
-  if (e == hipSuccess) e = tm->mark(s);
+    e = launch_conv_prefill(g, L, x, conv_w, conv_state, w, s, tm ? tm->at(0) : nullptr);
+  if (e == hipSuccess)
+    e = launch_prefill_prep(g, L, gl, beta, w, x, conv_w, conv_state, s, tm ? tm->at(1) : nullptr);
+  if (e == hipSuccess)
+    e = launch_prefill_state(g, L, z, rec_state, y, w, x, conv_w, conv_state, s,
+                             tm ? tm->at(2) : nullptr);
   return e;
 }
 
@@ -377,10 +392,10 @@ static int prefill_impl(const gdn_dims *dims, int64_t T, int32_t chunk, const vo
   if (ws_bytes < L.total) return GDN_ERR_WORKSPACE;
   if (injected_launch_failure()) return GDN_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  LaunchTimer tm(kernel_ms);
+  CallTimer tm(kernel_ms, 3);
   hipError_t e = enqueue_prefill(g, L, x, z, gl, beta, conv_w, conv_state, rec_state, y,
                                  static_cast<char *>(ws), s, &tm);
-  if (e == hipSuccess) e = tm.elapsed();
+  if (e == hipSuccess) e = tm.elapsed(3);
   return e == hipSuccess ? GDN_OK : set_hip_error(e, "gdn_prefill_chunked");
 }
 
@@ -451,23 +466,15 @@ static int decode_run(const gdn_dims *dims, const DecodeArgs &a, const char *whe
   // The timed variant: events at each kernel's own start and end (the two
   // kernels take a few microseconds at small B, about as long as the launch
   // latency that events recorded between launches would add).
-  hipEvent_t ev[4] = {};
-  hipError_t e = hipSuccess;
-  for (int i = 0; a.kernel_ms && e == hipSuccess && i < 4; ++i) e = hipEventCreate(&ev[i]);
-  const KernelEvents k_conv{ev[0], ev[1]}, k_state{ev[2], ev[3]};
+  CallTimer tm(a.kernel_ms, 2);
+  hipError_t e = tm.err;
   if (e == hipSuccess)
     e = launch_conv_step(g, a.T, a.x, a.conv_w, a.conv_pool, qkv, a.in_slots, a.out_slots,
-                         a.n_slots, s, a.kernel_ms ? &k_conv : nullptr);
+                         a.n_slots, s, tm.at(0));
   if (e == hipSuccess)
     e = launch_decode(g, a.T, qkv, a.z, a.gl, a.beta, a.rec_pool, a.y, a.n_slots, a.in_slots,
-                      a.out_slots, s, a.kernel_ms ? &k_state : nullptr);
-  if (a.kernel_ms) {
-    if (e == hipSuccess) e = hipEventSynchronize(ev[3]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&a.kernel_ms[0], ev[0], ev[1]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&a.kernel_ms[1], ev[2], ev[3]);
-    for (hipEvent_t v : ev)
-      if (v) (void)hipEventDestroy(v);
-  }
+                      a.out_slots, s, tm.at(1));
+  if (e == hipSuccess) e = tm.elapsed(2);
   return e == hipSuccess ? GDN_OK : set_hip_error(e, where);
 }
 
@@ -659,7 +666,7 @@ int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, int32_t 
   if (T_total > 0 && ws_bytes < need) return GDN_ERR_WORKSPACE;
   if (injected_launch_failure()) return GDN_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  LaunchTimer tm(nullptr);
+  CallTimer *tm = nullptr;  // not timed
   Geom g1 = g;
   g1.B = 1;
   const int lanes = varlen_lanes(g, cu_seqlens);
@@ -703,7 +710,7 @@ int gdn_prefill_varlen(const gdn_dims *dims, const int64_t *cu_seqlens, int32_t 
         beta + tok * g.H_v, conv_w, static_cast<char *>(conv_pool) + slots[n] * conv_slot,
         rec_pool + static_cast<size_t>(slots[n]) * (rec_slot / 4),
         static_cast<char *>(y) + tok * g.H_v * g.D * eo, static_cast<char *>(ws) + k * lane_ws,
-        ls[k], &tm);
+        ls[k], tm);
   }
   // The caller's stream continues once every lane is done.
   for (int k = 1; e == hipSuccess && k < lanes; ++k) {

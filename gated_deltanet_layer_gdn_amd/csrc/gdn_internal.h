@@ -12,6 +12,12 @@
 
 namespace gdn {
 
+// Events recorded at one kernel's own start and end (the timed entry points
+// launch through hipExtLaunchKernelGGL with them; null: a plain launch).
+struct KernelEvents {
+  hipEvent_t start, stop;
+};
+
 // Output code of the kernels' DTY template parameter (see gdn_device.h):
 // y's element type, plus 4 when z is null (no gate, y = o).
 inline int out_code(int out_dt, const void *z) { return out_dt | (z ? 0 : 4); }
@@ -100,7 +106,8 @@ hipError_t noalloc_scratch(hipStream_t s, void **ptr);
 hipError_t launch_conv_plain(const Geom &g, int64_t T, const void *x, const void *w,
                              void *hist, float *out, hipStream_t s);
 hipError_t launch_conv_prefill(const Geom &g, const PrefillWs &L, const void *x,
-                               const void *w, const void *hist, char *ws, hipStream_t s);
+                               const void *w, const void *hist, char *ws, hipStream_t s,
+                               const KernelEvents *ev = nullptr);
 hipError_t launch_conv_roll(const Geom &g, int64_t T, const void *x, void *hist,
                             hipStream_t s);
 // Decode of T = 1..kMaxMultiTokens tokens per sequence in two launches: the
@@ -108,11 +115,6 @@ hipError_t launch_conv_roll(const Geom &g, int64_t T, const void *x, void *hist,
 // out slots; the state stream then reads qkv.  in_slots / out_slots may be
 // null (sequence b in slot b, state after the last token back into it).
 constexpr int kMaxMultiTokens = 4;
-// Events recorded at one kernel's own start and end (the timed entry points
-// launch through hipExtLaunchKernelGGL with them; null: a plain launch).
-struct KernelEvents {
-  hipEvent_t start, stop;
-};
 #ifdef __HIPCC__
 // Launch of `kernel` on `s`; with `ev` (the timed entry points), through
 // hipExtLaunchKernelGGL, which records ev->start and ev->stop at the kernel's
@@ -180,10 +182,10 @@ inline bool prep_fuses_conv(const Geom &g, const PrefillWs &L) {
 // when prep_fuses_conv.
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
                                const float *beta, char *ws, const void *x, const void *conv_w,
-                               void *hist, hipStream_t s);
+                               void *hist, hipStream_t s, const KernelEvents *ev = nullptr);
 // x, conv_w and hist are used by the split-role pass (v and its history).
 hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z, float *S,
                                 void *y, const char *ws, const void *x, const void *conv_w,
-                                void *hist, hipStream_t s);
+                                void *hist, hipStream_t s, const KernelEvents *ev = nullptr);
 
 }  // namespace gdn

@@ -1304,11 +1304,11 @@ __global__ __launch_bounds__(512) void state_kernel_ws(Geom g, PrefillWs L,
 template <int D, int C>
 static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, float *S, void *y,
                            const char *ws, const void *x, const void *cw, void *hist,
-                           hipStream_t s) {
+                           hipStream_t s, const KernelEvents *ev) {
   if constexpr (D == 128 && C == 64) {
     dim3 grid(g.B * g.H_v * (D / StateKernelWS<0, 0>::ROWS));
     dim3 block(StateKernelWS<0, 0>::kThreads);
-#define GDN_WS(ZT, OC) hipLaunchKernelGGL((state_kernel_ws<ZT, OC>), grid, block, 0, s, g, L, z, S, y, ws, x, cw, hist)
+#define GDN_WS(ZT, OC) launch_kernel(state_kernel_ws<ZT, OC>, grid, block, s, ev, g, L, z, S, y, ws, x, cw, hist)
     GDN_OUT_DISPATCH(g.in_dt, out_code(g.out_dt, z), GDN_WS);
 #undef GDN_WS
     return;
@@ -1318,20 +1318,20 @@ static void launch_state_t(const Geom &g, const PrefillWs &L, const void *z, flo
   (void)hist;
   dim3 grid(g.B * g.H_v * (D / StateShape<D, C>::ROWS));
   dim3 block(StateShape<D, C>::NWV * 64);
-#define GDN_ST(ZT, OC) hipLaunchKernelGGL((state_kernel<D, C, ZT, OC>), grid, block, 0, s, g, L, z, S, y, ws)
+#define GDN_ST(ZT, OC) launch_kernel(state_kernel<D, C, ZT, OC>, grid, block, s, ev, g, L, z, S, y, ws)
   GDN_OUT_DISPATCH(g.in_dt, out_code(g.out_dt, z), GDN_ST);
 #undef GDN_ST
 }
 
 hipError_t launch_prefill_state(const Geom &g, const PrefillWs &L, const void *z, float *S,
                                 void *y, const char *ws, const void *x, const void *conv_w,
-                                void *hist, hipStream_t s) {
+                                void *hist, hipStream_t s, const KernelEvents *ev) {
 #define GDN_STATE(Dv)                                                                   \
   switch (L.C) {                                                                        \
-    case 16: launch_state_t<Dv, 16>(g, L, z, S, y, ws, x, conv_w, hist, s); break;     \
-    case 32: launch_state_t<Dv, 32>(g, L, z, S, y, ws, x, conv_w, hist, s); break;     \
-    case 64: launch_state_t<Dv, 64>(g, L, z, S, y, ws, x, conv_w, hist, s); break;     \
-    default: launch_state_t<Dv, 128>(g, L, z, S, y, ws, x, conv_w, hist, s); break;    \
+    case 16: launch_state_t<Dv, 16>(g, L, z, S, y, ws, x, conv_w, hist, s, ev); break;     \
+    case 32: launch_state_t<Dv, 32>(g, L, z, S, y, ws, x, conv_w, hist, s, ev); break;     \
+    case 64: launch_state_t<Dv, 64>(g, L, z, S, y, ws, x, conv_w, hist, s, ev); break;     \
+    default: launch_state_t<Dv, 128>(g, L, z, S, y, ws, x, conv_w, hist, s, ev); break;    \
   }
   if (g.D == 128) {
     GDN_STATE(128)

@@ -895,13 +895,14 @@ __global__ __launch_bounds__(256, (C <= 64 ? (CONV ? 3 : 4) : 2)) void prep_kern
 
 template <int D, int C>
 static void launch_prep_t(const Geom &g, const PrefillWs &L, const float *gl, const float *beta,
-                          char *ws, const void *x, const void *conv_w, void *hist, hipStream_t s) {
+                          char *ws, const void *x, const void *conv_w, void *hist, hipStream_t s,
+                          const KernelEvents *ev) {
   dim3 grid(L.NC, g.H_k, g.B);
   const bool stage = C <= 64 && static_cast<int64_t>(L.NC) * g.H_k * g.B > kPrepStageBlocks;
   if constexpr (D == 128 && C == 64) {
     if (prep_fuses_conv(g, L)) {
-      hipLaunchKernelGGL((prep_kernel<D, C, true, true, true>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x,
-                         conv_w, hist);
+      launch_kernel(prep_kernel<D, C, true, true, true>, grid, dim3(256), s, ev, g, L, gl, beta, ws, x,
+                    conv_w, hist);
       return;
     }
   }
@@ -911,28 +912,26 @@ static void launch_prep_t(const Geom &g, const PrefillWs &L, const float *gl, co
       // (bitwise equal).  Smaller grids keep the four-wave form, whose
       // smaller LDS footprint keeps four blocks per compute unit (35 against
       // 41 us at T = 4096).
-      hipLaunchKernelGGL((prep_kernel<D, C, true, true>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, conv_w,
-                         hist);
+      launch_kernel(prep_kernel<D, C, true, true>, grid, dim3(256), s, ev, g, L, gl, beta, ws, x, conv_w,
+                    hist);
       return;
     }
   }
   if (stage)
-    hipLaunchKernelGGL((prep_kernel<D, C, true, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, conv_w,
-                       hist);
+    launch_kernel(prep_kernel<D, C, true, false>, grid, dim3(256), s, ev, g, L, gl, beta, ws, x, conv_w, hist);
   else
-    hipLaunchKernelGGL((prep_kernel<D, C, false, false>), grid, dim3(256), 0, s, g, L, gl, beta, ws, x, conv_w,
-                       hist);
+    launch_kernel(prep_kernel<D, C, false, false>, grid, dim3(256), s, ev, g, L, gl, beta, ws, x, conv_w, hist);
 }
 
 hipError_t launch_prefill_prep(const Geom &g, const PrefillWs &L, const float *gl,
                                const float *beta, char *ws, const void *x, const void *conv_w,
-                               void *hist, hipStream_t s) {
+                               void *hist, hipStream_t s, const KernelEvents *ev) {
 #define GDN_PREP(Dv)                                                               \
   switch (L.C) {                                                                   \
-    case 16: launch_prep_t<Dv, 16>(g, L, gl, beta, ws, x, conv_w, hist, s); break;  \
-    case 32: launch_prep_t<Dv, 32>(g, L, gl, beta, ws, x, conv_w, hist, s); break;  \
-    case 64: launch_prep_t<Dv, 64>(g, L, gl, beta, ws, x, conv_w, hist, s); break;  \
-    default: launch_prep_t<Dv, 128>(g, L, gl, beta, ws, x, conv_w, hist, s); break; \
+    case 16: launch_prep_t<Dv, 16>(g, L, gl, beta, ws, x, conv_w, hist, s, ev); break;  \
+    case 32: launch_prep_t<Dv, 32>(g, L, gl, beta, ws, x, conv_w, hist, s, ev); break;  \
+    case 64: launch_prep_t<Dv, 64>(g, L, gl, beta, ws, x, conv_w, hist, s, ev); break;  \
+    default: launch_prep_t<Dv, 128>(g, L, gl, beta, ws, x, conv_w, hist, s, ev); break; \
   }
   if (g.D == 128) {
     GDN_PREP(128)

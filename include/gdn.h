@@ -333,16 +333,14 @@ GDN_API int gdn_decode_step_noalloc(const gdn_dims *dims, const void *x, const v
  * backend on Metal", section Measurements and gates, asks for the conv, the
  * prefill, the decode and the recurrent-state update to be measured in
  * isolation).  Same arguments and effects as the plain calls, plus
- * `kernel_ms`, which receives the duration of each kernel launch of the call,
- * taken from HIP events: for prefill, events that the library records on
- * `stream` between its launches; for decode, events recorded at each
- * kernel's own start and end (an extended launch), since its kernels are as
- * short as the launch latency:
+ * `kernel_ms`, which receives the duration of each kernel of the call, taken
+ * from HIP events recorded at the kernel's own start and end (an extended
+ * launch, so the launch latency between kernels is not counted):
  *   prefill: [0] conv + L2 norm, [1] chunk-local prep (Gram, (I+A)^{-1}, P)
  *            and the conv history roll, [2] state pass + gate     (3 floats)
  *            (d = 128, chunk 64, more than 4096 chunk x key-head blocks:
  *            the q/k conv and norm run inside the prep launch, and [0]
- *            spans no kernel)
+ *            is 0)
  *   decode:  [0] conv step + L2 norm, [1] state stream + gate      (2 floats)
  * These variants create HIP events and wait for the last one before they
  * return. */

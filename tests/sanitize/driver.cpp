@@ -43,7 +43,9 @@ hipError_t noalloc_scratch(hipStream_t, void **) { reached("noalloc_scratch"); }
 hipError_t launch_conv_plain(const Geom &, int64_t, const void *, const void *, void *, float *,
                              hipStream_t) { reached("conv_plain"); }
 hipError_t launch_conv_prefill(const Geom &, const PrefillWs &, const void *, const void *,
-                               const void *, char *, hipStream_t) { reached("conv_prefill"); }
+                               const void *, char *, hipStream_t, const KernelEvents *) {
+  reached("conv_prefill");
+}
 hipError_t launch_conv_roll(const Geom &, int64_t, const void *, void *, hipStream_t) {
   reached("conv_roll");
 }
@@ -66,11 +68,13 @@ hipError_t launch_in_proj(const Geom &, int64_t, int, const void *, const void *
   reached("in_proj");
 }
 hipError_t launch_prefill_prep(const Geom &, const PrefillWs &, const float *, const float *,
-                               char *, const void *, const void *, void *, hipStream_t) {
+                               char *, const void *, const void *, void *, hipStream_t,
+                               const KernelEvents *) {
   reached("prep");
 }
 hipError_t launch_prefill_state(const Geom &, const PrefillWs &, const void *, float *, void *,
-                                const char *, const void *, const void *, void *, hipStream_t) {
+                                const char *, const void *, const void *, void *, hipStream_t,
+                                const KernelEvents *) {
   reached("state");
 }
 }  // namespace gdn

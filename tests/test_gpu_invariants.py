@@ -223,3 +223,35 @@ def test_long_context_all_heads_and_resume(long_ctx, chunk):
     np.testing.assert_array_equal(yb.cpu().numpy().view(np.uint32), y32[:, half:].view(np.uint32))
     np.testing.assert_array_equal(S2.cpu().numpy().view(np.uint32), S.view(np.uint32))
     np.testing.assert_array_equal(from_dev(h2), h)
+
+
+def test_timed_variants_match_plain_calls():
+    # The timed entry points (per-kernel durations from events at each
+    # kernel's own start and end) leave every result bit-identical to the
+    # plain calls; every kernel that ran reports a positive duration, and the
+    # conv entry is 0 where prep computes the q/k conv (no conv launch).
+    import gated_deltanet_layer_gdn_amd as gdn
+    import torch
+
+    geom = Geometry(B=1, T=300, H_k=4, H_v=12, d_k=128, d_v=128, zero_state=False)
+    I = make_inputs(geom, 77)
+    d = dims_of(geom)
+    outs = []
+    for timed in (False, True):
+        D = dev_inputs(I)
+        km = [] if timed else None
+        y = gdn.prefill_chunked(d, D["x"], D["z"], D["g"], D["beta"], D["w"], D["hist"], D["S"],
+                                chunk=64, kernel_ms=km)
+        x1 = D["x"][:, :1].reshape(geom.B, -1).contiguous()
+        z1 = D["z"][:, :1].reshape(geom.B, geom.H_v, geom.d_v).contiguous()
+        g1 = D["g"][:, :1].reshape(geom.B, geom.H_v).contiguous()
+        b1 = D["beta"][:, :1].reshape(geom.B, geom.H_v).contiguous()
+        kd = [] if timed else None
+        yd = gdn.decode_step(d, x1, z1, g1, b1, D["w"], D["hist"], D["S"], kernel_ms=kd)
+        torch.cuda.synchronize()
+        outs.append((y.cpu().numpy(), yd.cpu().numpy(), D["S"].cpu().numpy(), from_dev(D["hist"])))
+        if timed:
+            assert len(km) == 3 and all(v > 0 for v in km), km  # conv pass, prep, state pass
+            assert len(kd) == 2 and all(v > 0 for v in kd), kd  # conv step, state stream
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
