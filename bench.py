@@ -60,22 +60,22 @@ LEG_SOURCES = {
 MEASURED_TRAFFIC = {
     # leg -> {"sha256": sources' hash, "read": bytes, "write": bytes}; from
     # profiles/gdn_hbm_bytes_prefill_t65536_t4096_decode.txt (sums over the leg's kernels)
-    "long64": {"sha256": "f975949530c177d4063c7f6b33a6b60b816266574816ea829c71bc35ab38a5c7",
-               "read": 4322280000, "write": 3262030000},
-    "long128": {"sha256": "f975949530c177d4063c7f6b33a6b60b816266574816ea829c71bc35ab38a5c7",
-               "read": 10197020000, "write": 7288760000},
-    "t4096": {"sha256": "f975949530c177d4063c7f6b33a6b60b816266574816ea829c71bc35ab38a5c7",
-               "read": 325920000, "write": 214150000},
-    "decode_b1": {"sha256": "3caa50a191216eda4d77fea224db781b03e81879544407e6db822baaae6600b4",
+    "long64": {"sha256": "3718e9a19065089207ea07a56925cd56e2a26b4c536360b82949931fbfb04df4",
+               "read": 4321000000, "write": 3263090000},
+    "long128": {"sha256": "3718e9a19065089207ea07a56925cd56e2a26b4c536360b82949931fbfb04df4",
+               "read": 10215130000, "write": 7288780000},
+    "t4096": {"sha256": "3718e9a19065089207ea07a56925cd56e2a26b4c536360b82949931fbfb04df4",
+               "read": 325820000, "write": 214160000},
+    "decode_b1": {"sha256": "053b9905f7aaf031ee90567d640dc9da83d1e07f35922dee8d64bb7616beeca2",
                "read": 3720000, "write": 3270000},
-    "decode_b64": {"sha256": "3caa50a191216eda4d77fea224db781b03e81879544407e6db822baaae6600b4",
+    "decode_b64": {"sha256": "053b9905f7aaf031ee90567d640dc9da83d1e07f35922dee8d64bb7616beeca2",
                "read": 218480000, "write": 209450000},
     # profiles/gdn_serving_mtp_verify_b64_varlen8_rmsnorm4096.txt (per step or call)
-    "mtp_verify": {"sha256": "3caa50a191216eda4d77fea224db781b03e81879544407e6db822baaae6600b4",
-                   "read": 244650000, "write": 628400000},
-    "varlen_prefill": {"sha256": "f975949530c177d4063c7f6b33a6b60b816266574816ea829c71bc35ab38a5c7",
-                       "read": 829600000, "write": 569130000},
-    "gated_rmsnorm": {"sha256": "31cc808e45ea4183a296be4e6604b4d36afb684e6f9d4bc037cc53199d97fac0",
+    "mtp_verify": {"sha256": "053b9905f7aaf031ee90567d640dc9da83d1e07f35922dee8d64bb7616beeca2",
+                   "read": 244650000, "write": 628410000},
+    "varlen_prefill": {"sha256": "3718e9a19065089207ea07a56925cd56e2a26b4c536360b82949931fbfb04df4",
+                       "read": 829500000, "write": 568990000},
+    "gated_rmsnorm": {"sha256": "7c3dcbf2cd36e667884d09c932cc5ba6cf264706e9f159d0b3bbe60f5c094e02",
                       "read": 151030000, "write": 50330000},
 }
 
