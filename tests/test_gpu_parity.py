@@ -64,11 +64,14 @@ def test_prefill_ragged_small(T, chunk):
 def test_prefill_head_groupings(H_k, H_v, B):
     # d = 128, chunk 64 (the split-role passes) with 1, 2 and 5 value heads
     # per key head, including state-pass grids (4 blocks per value head) that
-    # are not a multiple of 8 blocks; the same tokens through decode steps.
+    # are not a multiple of 8 blocks; chunk 128 (prep forms every value head's
+    # P before the inverses; 32-row state blocks), two chunks with a ragged
+    # tail; the same tokens through decode steps.
     geom = Geometry(B=B, T=150, H_k=H_k, H_v=H_v, d_k=128, d_v=128, zero_state=False)
     I = make_inputs(geom, seed=500 + 10 * H_k + H_v)
     ref = oracle_run(geom, I)
     check_layer(f"heads {H_k}/{H_v} B={B} T=150 C=64", gpu_prefill(geom, I, 64), ref)
+    check_layer(f"heads {H_k}/{H_v} B={B} T=150 C=128", gpu_prefill(geom, I, 128), ref)
     check_layer(f"heads {H_k}/{H_v} B={B} 150 decode steps", gpu_decode_seq(geom, I), ref)
 
 
