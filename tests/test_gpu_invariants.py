@@ -255,3 +255,69 @@ def test_timed_variants_match_plain_calls():
             assert len(kd) == 2 and all(v > 0 for v in kd), kd  # conv step, state stream
     for a, b in zip(*outs):
         np.testing.assert_array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+
+
+@pytest.mark.timeout(900)
+def test_largest_token_count_one_call_equals_split():
+    # The largest T a call accepts (2^24 tokens), on one key head and one
+    # value head of 128 (chunk 64: the passes whose q/k slices are addressed
+    # with 32-bit offsets, which that limit keeps below 2^32): one call
+    # against the same tokens in two chunk-aligned calls, bit for bit, and its
+    # first 4096 outputs against the fp64 oracle.  Inputs are drawn on the
+    # device in slices (same distributions as the seeded workloads).
+    import gated_deltanet_layer_gdn_amd as gdn
+    import oracle
+    import torch
+
+    T = 1 << 24
+    geom = Geometry(B=1, T=T, H_k=1, H_v=1, d_k=128, d_v=128)
+    d = dims_of(geom)
+    C_ch = 3 * 128
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    x = torch.empty((1, T, C_ch), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((1, T, 1, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((1, T, 1), dtype=torch.float32, device="cuda")
+    beta = torch.empty((1, T, 1), dtype=torch.float32, device="cuda")
+    step = 1 << 20
+    for t0 in range(0, T, step):
+        x[:, t0:t0 + step] = torch.randn((1, step, C_ch), device="cuda", generator=gen).to(torch.bfloat16)
+        z[:, t0:t0 + step] = torch.randn((1, step, 1, 128), device="cuda", generator=gen).to(torch.bfloat16)
+        g[:, t0:t0 + step] = -torch.nn.functional.softplus(torch.randn((1, step, 1), device="cuda", generator=gen))
+        beta[:, t0:t0 + step] = torch.sigmoid(torch.randn((1, step, 1), device="cuda", generator=gen))
+    w = (0.5 * torch.randn((C_ch, 4), device="cuda", generator=gen)).to(torch.bfloat16)
+    print("[invariant] 2^24-token inputs drawn", flush=True)
+    ws = torch.empty(gdn.prefill_workspace_bytes(d, T, 64), dtype=torch.uint8, device="cuda")
+
+    def fresh():
+        return (torch.zeros((1, 3, C_ch), dtype=torch.bfloat16, device="cuda"),
+                torch.zeros((1, 1, 128, 128), dtype=torch.float32, device="cuda"))
+
+    h1, S1 = fresh()
+    y1 = gdn.prefill_chunked(d, x, z, g, beta, w, h1, S1, chunk=64, ws=ws)
+    torch.cuda.synchronize()
+    print("[invariant] one call done", flush=True)
+    h2, S2 = fresh()
+    half = T // 2
+    ya = gdn.prefill_chunked(d, x[:, :half], z[:, :half], g[:, :half], beta[:, :half], w, h2, S2,
+                             chunk=64, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int32), y1[:, :half].view(torch.int32))
+    del ya
+    yb = gdn.prefill_chunked(d, x[:, half:], z[:, half:], g[:, half:], beta[:, half:], w, h2, S2,
+                             chunk=64, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(yb.view(torch.int32), y1[:, half:].view(torch.int32))
+    assert torch.equal(S2.view(torch.int32), S1.view(torch.int32))
+    assert torch.equal(h2.view(torch.int16), h1.view(torch.int16))
+    del yb
+    assert bool(torch.isfinite(S1).all()) and bool(torch.isfinite(y1[:, -4096:]).all())
+    # the first 4096 tokens against the oracle (they depend on nothing later)
+    n = 4096
+    I = {"x": from_dev(x[:, :n].contiguous()), "z": from_dev(z[:, :n].contiguous()),
+         "g": g[:, :n].cpu().numpy(), "beta": beta[:, :n].cpu().numpy(), "w": from_dev(w),
+         "hist": np.zeros((1, 3, C_ch), np.uint16), "S": np.zeros((1, 1, 128, 128), np.float32)}
+    yr, _, _ = oracle.layer(I["x"], I["z"], I["g"], I["beta"], I["w"], I["hist"], I["S"],
+                            H_k=1, H_v=1, d_k=128, d_v=128, eps=d.l2_eps)
+    e = rel_l2(y1[:, :n].double().cpu().numpy(), yr)
+    print(f"[invariant] T=2^24: first {n} outputs rel_l2 {e:.3e}", flush=True)
+    assert e <= TOL
